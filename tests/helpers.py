@@ -1,0 +1,61 @@
+"""Test helpers: bit views of torch tensors and a one-call oracle run on a
+workload.  Shared by the CPU pin tests and the GPU parity tests."""
+import numpy as np
+import torch
+
+from oracle import rpa_oracle as O
+
+_VIEW = {"f32": (torch.int32, np.uint32), "bf16": (torch.int16, np.uint16),
+         "fp8": (torch.uint8, np.uint8)}
+
+
+def bits(t: torch.Tensor, dtype: str) -> np.ndarray:
+    tv, nv = _VIEW[dtype]
+    return t.detach().contiguous().view(tv).cpu().numpy().view(nv)
+
+
+def oracle_forward(w, cache_bits=None, seqs=None, update=True):
+    """Run the oracle on workload `w` (tensors may live on any device)."""
+    if cache_bits is None:
+        cache_bits = bits(w.kv_cache, w.cache_dtype)
+    sink = None if w.attention_sink is None else w.attention_sink.cpu().numpy()
+    return O.forward(
+        bits(w.queries, w.q_dtype),
+        bits(w.keys, w.kv_in_dtype) if update else None,
+        bits(w.values, w.kv_in_dtype) if update else None,
+        cache_bits, w.kv_lens, w.block_tables, w.query_start_loc, w.distribution,
+        page_size=w.page_size, pages_per_seq=w.pages_per_seq, q_dtype=w.q_dtype,
+        kv_in_dtype=w.kv_in_dtype, cache_dtype=w.cache_dtype, softmax_scale=w.softmax_scale,
+        sliding_window=w.sliding_window, logits_soft_cap=w.logits_soft_cap, q_scale=w.q_scale,
+        k_scale=w.k_scale, v_scale=w.v_scale, attention_sink=sink, seqs=seqs)
+
+
+def oracle_update(w, cache_bits=None):
+    if cache_bits is None:
+        cache_bits = bits(w.kv_cache, w.cache_dtype)
+    return O.update_kv_cache(
+        cache_bits, bits(w.keys, w.kv_in_dtype), bits(w.values, w.kv_in_dtype), w.kv_lens,
+        w.block_tables, w.query_start_loc, w.distribution, page_size=w.page_size,
+        pages_per_seq=w.pages_per_seq, kv_in_dtype=w.kv_in_dtype, cache_dtype=w.cache_dtype,
+        k_scale=w.k_scale, v_scale=w.v_scale)
+
+
+def poison_unused(w, include_written=True):
+    """Fill every cache slot that no query can see (after the update) with NaN
+    (in place), so that any read outside the visible ranges shows in the
+    output.  With `include_written`, slots the update overwrites are poisoned
+    too (only valid when the call under test performs the update)."""
+    used = O.visible_slots(w.kv_lens, w.block_tables, w.query_start_loc, w.distribution,
+                           page_size=w.page_size, pages_per_seq=w.pages_per_seq,
+                           num_pages=w.num_pages, sliding_window=w.sliding_window)
+    written = O.written_slots(w.kv_lens, w.block_tables, w.query_start_loc, w.distribution,
+                              page_size=w.page_size, pages_per_seq=w.pages_per_seq,
+                              num_pages=w.num_pages)
+    bad = torch.from_numpy((~used) | (written if include_written else False)).reshape(-1).to(w.kv_cache.device)
+    flat = w.kv_cache.view(w.num_pages * w.page_size, -1)
+    nan = {"f32": float("nan"), "bf16": float("nan")}
+    if w.cache_dtype == "fp8":
+        flat[bad] = 0x7F
+    else:
+        flat[bad] = nan[w.cache_dtype]
+    return w

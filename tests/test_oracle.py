@@ -1,0 +1,416 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+library routines (torch SDPA, torch's float8_e4m3fn cast), closed forms,
+a hand-derived golden fixture, brute force on tiny inputs, and invariants of
+the method (chunked prefill, decode = last prefill row, page permutation,
+sequence order, distribution).  CPU only."""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import rpa_oracle as O
+from ragged_paged_kv_scatter_amd import workloads as W
+from tests import bruteforce
+from tests.helpers import bits, oracle_forward, oracle_update
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def sdpa_causal(q, k, v, scale, mask=None):
+    """torch reference: q [L, Hq, D], k/v [S, Hkv, D] float64, GQA by
+    repeat_interleave, bottom-right aligned causal mask built for L == S."""
+    Hq, Hkv = q.shape[1], k.shape[1]
+    G = Hq // Hkv
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]
+    kt = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+    vt = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+    if mask is None:
+        o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True,
+                                                             scale=scale)
+    else:
+        o = torch.nn.functional.scaled_dot_product_attention(
+            qt, kt, vt, attn_mask=torch.from_numpy(mask), scale=scale)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+# ---------------------------------------------------------------------------
+# attention core
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("L,Hq,Hkv,D", [(1, 2, 1, 8), (7, 4, 2, 16), (33, 8, 2, 64)])
+def test_no_context_prefill_equals_sdpa(L, Hq, Hkv, D):
+    q, k, v = rand((L, Hq, D), 1), rand((L, Hkv, D), 2), rand((L, Hkv, D), 3)
+    scale = 1 / math.sqrt(D)
+    out = O.attend_sequence(q, k, v, 0, softmax_scale=scale)
+    ref = sdpa_causal(q, k, v, scale)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_window_equals_sdpa_with_band_mask():
+    L, Hq, Hkv, D, Wn = 40, 4, 2, 16, 7
+    q, k, v = rand((L, Hq, D), 4), rand((L, Hkv, D), 5), rand((L, Hkv, D), 6)
+    i = np.arange(L)[:, None]
+    j = np.arange(L)[None, :]
+    band = (j <= i) & (j > i - Wn)          # window_size = (W - 1, 0): W keys incl. self
+    out = O.attend_sequence(q, k, v, 0, softmax_scale=0.3, sliding_window=Wn)
+    ref = sdpa_causal(q, k, v, 0.3, mask=band)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_context_tail_alignment_equals_sdpa_slice():
+    """A chunk with context: its rows equal the last rows of a full causal
+    prefill (queries are the tail of the sequence)."""
+    S, L, Hq, Hkv, D = 29, 6, 4, 1, 8
+    q, k, v = rand((S, Hq, D), 7), rand((S, Hkv, D), 8), rand((S, Hkv, D), 9)
+    full = sdpa_causal(q, k, v, 0.5)
+    out = O.attend_sequence(q[S - L:], k, v, S - L, softmax_scale=0.5)
+    np.testing.assert_allclose(out, full[S - L:], rtol=1e-12, atol=1e-12)
+
+
+def test_single_key_returns_v_exactly():
+    q, k, v = rand((1, 4, 8), 10), rand((1, 2, 8), 11), rand((1, 2, 8), 12)
+    out = O.attend_sequence(q, k, v, 0, softmax_scale=1.7, logits_soft_cap=2.0)
+    np.testing.assert_array_equal(out[0, :2], v[0, [0, 0]])
+    np.testing.assert_array_equal(out[0, 2:], v[0, [1, 1]])
+
+
+def test_single_key_with_sink_closed_form():
+    q, k, v = rand((1, 2, 8), 13), rand((1, 1, 8), 14), rand((1, 1, 8), 15)
+    sink = np.array([0.4, -1.3])
+    out = O.attend_sequence(q, k, v, 0, softmax_scale=0.5, sink=sink)
+    for h in range(2):
+        s = 0.5 * float(q[0, h] @ k[0, 0])
+        expect = v[0, 0] / (1.0 + math.exp(sink[h] - s))
+        np.testing.assert_allclose(out[0, h], expect, rtol=1e-13)
+
+
+def test_window_one_returns_own_value():
+    L = 9
+    q, k, v = rand((L, 4, 8), 16), rand((L, 2, 8), 17), rand((L, 2, 8), 18)
+    out = O.attend_sequence(q, k, v, 0, softmax_scale=1.0, sliding_window=1)
+    np.testing.assert_array_equal(out[:, 0], v[:, 0])
+    np.testing.assert_array_equal(out[:, 3], v[:, 1])
+
+
+def test_uniform_keys_average_visible_values():
+    kv, L, ctx = 12, 4, 8
+    q = rand((L, 2, 8), 19)
+    k = np.repeat(rand((1, 1, 8), 20), kv, axis=0)
+    v = rand((kv, 1, 8), 21)
+    out = O.attend_sequence(q, k, v, ctx, softmax_scale=0.9, sliding_window=5)
+    for t in range(L):
+        p = ctx + t
+        lo = max(0, p - 5 + 1)
+        np.testing.assert_allclose(out[t, 0], v[lo:p + 1, 0].mean(axis=0), rtol=1e-12)
+
+
+def test_soft_cap_closed_form_two_keys():
+    q = np.array([[[1.0, 0.0]]])
+    k = np.array([[[3.0, 0.0]], [[-2.0, 0.0]]])
+    v = np.array([[[1.0, 0.0]], [[0.0, 1.0]]])
+    cap = 1.5
+    out = O.attend_sequence(q, k, v, 1, softmax_scale=1.0, logits_soft_cap=cap)
+    s1, s2 = cap * math.tanh(3.0 / cap), cap * math.tanh(-2.0 / cap)
+    w1 = 1.0 / (1.0 + math.exp(s2 - s1))
+    np.testing.assert_allclose(out[0, 0], [w1, 1 - w1], rtol=1e-14)
+
+
+def test_huge_cap_and_neg_sink_are_no_ops():
+    q, k, v = rand((5, 4, 8), 22), rand((9, 2, 8), 23), rand((9, 2, 8), 24)
+    base = O.attend_sequence(q, k, v, 4, softmax_scale=0.7)
+    capped = O.attend_sequence(q, k, v, 4, softmax_scale=0.7, logits_soft_cap=1e30)
+    sunk = O.attend_sequence(q, k, v, 4, softmax_scale=0.7, sink=np.full(4, -1e30))
+    np.testing.assert_allclose(capped, base, rtol=1e-12)
+    np.testing.assert_allclose(sunk, base, rtol=1e-12)
+
+
+def test_weights_sum_to_one():
+    q, k, v = rand((6, 4, 8), 25), rand((20, 2, 8), 26), rand((20, 2, 8), 27)
+    _, w = O.attend_sequence(q, k, v, 14, softmax_scale=0.4, sliding_window=9,
+                             logits_soft_cap=3.0, return_weights=True)
+    np.testing.assert_allclose(w.sum(axis=-1), 1.0, rtol=1e-13)
+    sink = np.array([0.1, 2.0, -0.5, 1.0])
+    _, ws = O.attend_sequence(q, k, v, 14, softmax_scale=0.4, sink=sink, return_weights=True)
+    # the missing mass is the sink's share exp(sigma)/(exp(sigma) + sum_j exp(s_j))
+    for h in range(4):
+        s = (q[:, h] @ k[:, h // 2].T) * 0.4
+        mask = O.visible(14 + np.arange(6), 20, 0)
+        den = np.where(mask, np.exp(s), 0).sum(1) + math.exp(sink[h])
+        np.testing.assert_allclose(1 - ws[:, h].sum(-1), math.exp(sink[h]) / den, rtol=1e-11)
+
+
+def test_linearity_in_values():
+    q, k, v = rand((5, 4, 8), 28), rand((9, 2, 8), 29), rand((9, 2, 8), 30)
+    a, b = 2.5, -0.75
+    o1 = O.attend_sequence(q, k, v, 4, softmax_scale=0.5)
+    o2 = O.attend_sequence(q, k, a * v + b, 4, softmax_scale=0.5)
+    np.testing.assert_allclose(o2, a * o1 + b, rtol=1e-12, atol=1e-12)
+
+
+def test_bruteforce_all_features():
+    rng = np.random.default_rng(31)
+    kv, L, Hq, Hkv, D = 11, 4, 4, 2, 6
+    q, k, v = rng.standard_normal((L, Hq, D)), rng.standard_normal((kv, Hkv, D)), \
+        rng.standard_normal((kv, Hkv, D))
+    sink = rng.standard_normal(Hq)
+    ctx = kv - L
+    out = O.attend_sequence(q, k, v, ctx, softmax_scale=0.6, sliding_window=5,
+                            logits_soft_cap=1.2, sink=sink)
+    for t in range(L):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            ref = bruteforce.attention_row(list(q[t, h]), [list(r) for r in k[:, g]],
+                                           [list(r) for r in v[:, g]], ctx + t, scale=0.6,
+                                           window=5, cap=1.2, sink=float(sink[h]))
+            np.testing.assert_allclose(out[t, h], ref, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# update (scatter) and gather
+# ---------------------------------------------------------------------------
+
+def _tiny_handmade():
+    w = W.tiny_fp32()
+    bt = np.zeros(6, dtype=np.int32)
+    bt[0], bt[2], bt[3], bt[4] = 5, 2, 7, 3
+    w.block_tables = bt
+    return w
+
+
+def test_scatter_matches_hand_derived_slots():
+    w = _tiny_handmade()
+    rows = np.loadtxt(os.path.join(GOLDEN, "tiny_scatter_slots.txt"), dtype=np.int64, ndmin=2)
+    before = bits(w.kv_cache, "f32")
+    after = oracle_update(w, before)
+    kb, vb = bits(w.keys, "f32"), bits(w.values, "f32")
+    touched = np.zeros(before.shape[:2], dtype=bool)
+    for tok, page, off in rows:
+        for h in range(2):
+            np.testing.assert_array_equal(after[page, off, 2 * h], kb[tok, h])
+            np.testing.assert_array_equal(after[page, off, 2 * h + 1], vb[tok, h])
+        touched[page, off] = True
+    np.testing.assert_array_equal(after[~touched], before[~touched])
+
+
+def test_scatter_zero_fills_pad_lanes_and_roundtrips():
+    w = W.make("mixed_bf16", small=True, head_dim=64, head_dim_padded=96)
+    before = bits(w.kv_cache, "bf16")
+    after = oracle_update(w, before)
+    written = O.written_slots(w.kv_lens, w.block_tables, w.query_start_loc, w.distribution,
+                              page_size=w.page_size, pages_per_seq=w.pages_per_seq,
+                              num_pages=w.num_pages)
+    assert np.all(after[written][..., 64:] == 0)
+    np.testing.assert_array_equal(after[~written], before[~written])
+    kb = bits(w.keys, "bf16")
+    for s in range(w.num_seqs):
+        q0, ql, ctx, kvl = O.seq_bounds(w.query_start_loc, w.kv_lens, s)
+        k, _ = O.gather_kv(after, s, kvl, w.block_tables, page_size=w.page_size,
+                           pages_per_seq=w.pages_per_seq, head_dim=64, cache_dtype="bf16")
+        np.testing.assert_array_equal(k[ctx:], O.bf16_bits_to_f64(kb[q0:q0 + ql]))
+
+
+def test_scatter_fp8_quantises_with_scale():
+    w = W.make("fp8_full", small=True)
+    after = oracle_update(w)
+    kb = bits(w.keys, "bf16")
+    x = torch.from_numpy(O.bf16_bits_to_f64(kb).astype(np.float32))
+    lib = torch.clamp(x / 0.05, -448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    for s in range(w.num_seqs):
+        q0, ql, ctx, kvl = O.seq_bounds(w.query_start_loc, w.kv_lens, s)
+        page, off = O.slot_of(w.block_tables, w.pages_per_seq, w.page_size, s,
+                              np.arange(ctx, kvl))
+        np.testing.assert_array_equal(after[page, off][:, 0::2, :], lib[q0:q0 + ql])
+
+
+# ---------------------------------------------------------------------------
+# whole-step invariants
+# ---------------------------------------------------------------------------
+
+def _place(w, perm_seed):
+    """Re-lay the same logical context of every sequence on a new random page
+    permutation (test-side placement, independent of the oracle's scatter)."""
+    rng = np.random.default_rng(perm_seed)
+    cache = bits(w.kv_cache, w.cache_dtype)
+    new = np.zeros_like(cache)
+    perm = rng.permutation(w.num_pages)
+    bt = np.zeros_like(w.block_tables)
+    cur = 0
+    for s in range(w.num_seqs):
+        kvl = int(w.kv_lens[s])
+        npg = -(-kvl // w.page_size)
+        for i in range(npg):
+            src = w.block_tables[s * w.pages_per_seq + i]
+            dst = perm[cur]
+            cur += 1
+            bt[s * w.pages_per_seq + i] = dst
+            new[dst] = cache[src]
+    return new, bt
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "mixed_bf16", "fp8_full"])
+def test_page_permutation_invariance(name):
+    w = W.make(name, small=True)
+    out1, _ = oracle_forward(w)
+    cache2, bt2 = _place(w, 99)
+    w.block_tables = bt2
+    out2, _ = oracle_forward(w, cache_bits=cache2)
+    np.testing.assert_array_equal(out1, out2)
+
+
+def test_distribution_only_sets_num_seqs():
+    w = W.make("mixed_bf16", small=True)
+    out1, c1 = oracle_forward(w)
+    w.distribution = np.array([0, 0, w.num_seqs], dtype=np.int32)
+    out2, c2 = oracle_forward(w)
+    np.testing.assert_array_equal(out1, out2)
+    np.testing.assert_array_equal(c1, c2)
+
+
+def test_sequence_order_permutes_outputs():
+    w = W.make("mixed_bf16", small=True)
+    out1, _ = oracle_forward(w)
+    n = w.num_seqs
+    order = np.random.default_rng(5).permutation(n)
+    ql = w.q_lens()
+    qsl = w.query_start_loc
+    pps = w.pages_per_seq
+    q = w.queries.clone()
+    k = w.keys.clone()
+    v = w.values.clone()
+    new_qsl = np.zeros_like(qsl)
+    new_kv = np.zeros_like(w.kv_lens)
+    new_bt = np.zeros_like(w.block_tables)
+    rows = []
+    cur = 0
+    for i, s in enumerate(order):
+        new_qsl[i] = cur
+        rows.append(np.arange(qsl[s], qsl[s] + ql[s]))
+        cur += ql[s]
+        new_kv[i] = w.kv_lens[s]
+        new_bt[i * pps:(i + 1) * pps] = w.block_tables[s * pps:(s + 1) * pps]
+    new_qsl[n:] = cur
+    rows = np.concatenate(rows)
+    w.queries, w.keys, w.values = q[rows], k[rows], v[rows]
+    w.query_start_loc, w.kv_lens, w.block_tables = new_qsl, new_kv, new_bt
+    w.distribution = np.array([0, 0, n], dtype=np.int32)
+    out2, _ = oracle_forward(w)
+    np.testing.assert_array_equal(out2, out1[rows])
+
+
+def test_chunked_prefill_and_decode_consistency():
+    """One sequence: prefill of a+b tokens == prefill a then prefill b with the
+    context grown by a; and its last row == a decode step at that position."""
+    w = W.build("one", q_lens=[13], kv_lens=[20], distribution=(0, 1, 0), num_q_heads=4,
+                num_kv_heads=2, head_dim=16, page_size=4, q_dtype="f32", kv_in_dtype="f32",
+                cache_dtype="f32", softmax_scale=0.25, seed=3, sliding_window=6,
+                logits_soft_cap=2.0, with_sink=True)
+    full, cache_full = oracle_forward(w)
+    # first chunk: 8 tokens, kv 15
+    a = 8
+    wa = W.build("one", q_lens=[a], kv_lens=[15], distribution=(0, 1, 0), num_q_heads=4,
+                 num_kv_heads=2, head_dim=16, page_size=4, q_dtype="f32", kv_in_dtype="f32",
+                 cache_dtype="f32", softmax_scale=0.25, seed=3, sliding_window=6,
+                 logits_soft_cap=2.0, with_sink=True)
+    for name in ("queries", "keys", "values"):
+        setattr(wa, name, getattr(w, name)[:a].clone())
+    wa.kv_cache, wa.block_tables, wa.attention_sink = w.kv_cache, w.block_tables, w.attention_sink
+    wa.num_pages, wa.pages_per_seq = w.num_pages, w.pages_per_seq
+    out_a, cache_a = oracle_forward(wa)
+    wb = W.build("one", q_lens=[5], kv_lens=[20], distribution=(0, 1, 0), num_q_heads=4,
+                 num_kv_heads=2, head_dim=16, page_size=4, q_dtype="f32", kv_in_dtype="f32",
+                 cache_dtype="f32", softmax_scale=0.25, seed=3, sliding_window=6,
+                 logits_soft_cap=2.0, with_sink=True)
+    for name in ("queries", "keys", "values"):
+        setattr(wb, name, getattr(w, name)[a:].clone())
+    wb.block_tables, wb.attention_sink = w.block_tables, w.attention_sink
+    wb.num_pages, wb.pages_per_seq = w.num_pages, w.pages_per_seq
+    out_b, cache_b = oracle_forward(wb, cache_bits=cache_a)
+    np.testing.assert_allclose(np.concatenate([out_a, out_b]), full, rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(cache_b, cache_full)
+    # decode step at the last position, over the fully updated cache
+    wd = W.build("one", q_lens=[1], kv_lens=[20], distribution=(1, 0, 0), num_q_heads=4,
+                 num_kv_heads=2, head_dim=16, page_size=4, q_dtype="f32", kv_in_dtype="f32",
+                 cache_dtype="f32", softmax_scale=0.25, seed=3, sliding_window=6,
+                 logits_soft_cap=2.0, with_sink=True)
+    wd.queries = w.queries[-1:].clone()
+    wd.block_tables, wd.attention_sink = w.block_tables, w.attention_sink
+    wd.num_pages, wd.pages_per_seq = w.num_pages, w.pages_per_seq
+    from tests.helpers import bits as _b
+    out_d, _ = O.forward(_b(wd.queries, "f32"), None, None, cache_full, wd.kv_lens,
+                         wd.block_tables, wd.query_start_loc, wd.distribution, page_size=4,
+                         pages_per_seq=w.pages_per_seq, q_dtype="f32", kv_in_dtype="f32",
+                         cache_dtype="f32", softmax_scale=0.25, sliding_window=6,
+                         logits_soft_cap=2.0, attention_sink=w.attention_sink.numpy())
+    np.testing.assert_allclose(out_d[0], full[-1], rtol=1e-12, atol=1e-13)
+
+
+def test_padding_rows_and_seqs_untouched():
+    w = W.make("mixed_bf16", small=True, extra_seqs=3, extra_tokens=5)
+    out, _ = oracle_forward(w)
+    n_valid = int(w.query_start_loc[w.num_seqs])
+    assert np.all(np.isnan(out[n_valid:]))
+    assert not np.any(np.isnan(out[:n_valid]))
+
+
+def test_tiny_config_bruteforce_end_to_end():
+    """The tiny fp32 workload through the whole oracle vs scalar loops over
+    hand-gathered keys (test-side addressing)."""
+    w = W.tiny_fp32()
+    out, cache = oracle_forward(w)
+    kb = bits(w.keys, "f32").view(np.float32)
+    vb = bits(w.values, "f32").view(np.float32)
+    qb = bits(w.queries, "f32").view(np.float32)
+    c0 = bits(w.kv_cache, "f32").view(np.float32)
+    for s in range(3):
+        q0 = int(w.query_start_loc[s])
+        ql = int(w.query_start_loc[s + 1]) - q0
+        kvl = int(w.kv_lens[s])
+        ctx = kvl - ql
+        keys = [[None] * 2 for _ in range(kvl)]
+        vals = [[None] * 2 for _ in range(kvl)]
+        for j in range(kvl):
+            if j >= ctx:
+                keys[j] = [list(map(float, kb[q0 + j - ctx, g])) for g in range(2)]
+                vals[j] = [list(map(float, vb[q0 + j - ctx, g])) for g in range(2)]
+            else:
+                p = w.block_tables[s * w.pages_per_seq + j // 16]
+                keys[j] = [list(map(float, c0[p, j % 16, 2 * g])) for g in range(2)]
+                vals[j] = [list(map(float, c0[p, j % 16, 2 * g + 1])) for g in range(2)]
+        for t in range(ql):
+            for h in range(4):
+                g = h // 2
+                ref = bruteforce.attention_row(list(map(float, qb[q0 + t, h])),
+                                               [r[g] for r in keys], [r[g] for r in vals],
+                                               ctx + t, scale=1 / 8)
+                np.testing.assert_allclose(out[q0 + t, h], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_fp8_prefill_equals_sdpa_on_library_dequant():
+    """A no-context prefill through an e4m3 cache: update (quantise + scatter),
+    gather and attention vs torch's own float8_e4m3fn cast of K/V / scale,
+    dequantised by multiplying back, then torch SDPA."""
+    L, Hq, Hkv, D, sc = 37, 4, 2, 16, 0.05
+    w = W.build("fp8", q_lens=[L], kv_lens=[L], distribution=(0, 1, 0), num_q_heads=Hq,
+                num_kv_heads=Hkv, head_dim=D, page_size=8, q_dtype="bf16", kv_in_dtype="bf16",
+                cache_dtype="fp8", softmax_scale=0.3, k_scale=sc, v_scale=sc * 2, seed=11)
+    out, _ = oracle_forward(w)
+
+    def deq(t, s):
+        c = torch.clamp(t.float() / s, -448, 448).to(torch.float8_e4m3fn)
+        return (c.to(torch.float64) * s).numpy()
+    q = w.queries.to(torch.float64).numpy()
+    ref = sdpa_causal(q, deq(w.keys, sc), deq(w.values, sc * 2), 0.3)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_q_scale_multiplies_logits():
+    q, k, v = rand((5, 4, 8), 40), rand((9, 2, 8), 41), rand((9, 2, 8), 42)
+    a = O.attend_sequence(q, k, v, 4, softmax_scale=0.2, q_scale=3.0)
+    ref = sdpa_causal(np.concatenate([np.zeros((4, 4, 8)), q]) * 0.6, k, v, 1.0)[4:]
+    np.testing.assert_allclose(a, ref, rtol=1e-12, atol=1e-12)
