@@ -225,6 +225,17 @@ def visible(q_pos: np.ndarray, kv_len: int, sliding_window: int) -> np.ndarray:
     return m
 
 
+def _weighted_sum(w, v, mask):
+    """sum over visible j of w[q, j] * v[j]: keys a row cannot see contribute
+    nothing whatever their stored bits (a masked slot may hold NaN)."""
+    finite = np.isfinite(v).all(axis=1)
+    out = w @ np.where(finite[:, None], v, 0.0)
+    for j in np.nonzero(~finite)[0]:
+        rows = mask[:, j]
+        out[rows] += w[rows, j, None] * v[j][None, :]
+    return out
+
+
 def attend_sequence(q, k, v, ctx, *, softmax_scale=1.0, sliding_window=0, logits_soft_cap=0.0,
                     q_scale=0.0, sink=None, return_weights=False):
     """Attention of one sequence's query rows over its own keys.
@@ -255,7 +266,7 @@ def attend_sequence(q, k, v, ctx, *, softmax_scale=1.0, sliding_window=0, logits
         z = w.sum(axis=1)
         if sink is not None:
             z = z + np.exp(sink[h] - m)
-        out[:, h, :] = (w @ v[:, g, :]) / z[:, None]
+        out[:, h, :] = _weighted_sum(w, v[:, g, :], mask) / z[:, None]
         if return_weights:
             weights[:, h, :] = w / z[:, None]
     return (out, weights) if return_weights else out

@@ -414,3 +414,21 @@ def test_q_scale_multiplies_logits():
     a = O.attend_sequence(q, k, v, 4, softmax_scale=0.2, q_scale=3.0)
     ref = sdpa_causal(np.concatenate([np.zeros((4, 4, 8)), q]) * 0.6, k, v, 1.0)[4:]
     np.testing.assert_allclose(a, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_masked_slots_may_hold_nan():
+    """Keys outside a row's window contribute nothing whatever their bits:
+    NaN in a slot no row sees leaves every output finite and unchanged, NaN in
+    a slot some rows see turns exactly those rows to NaN."""
+    q, k, v = rand((6, 2, 8), 50), rand((20, 1, 8), 51), rand((20, 1, 8), 52)
+    base = O.attend_sequence(q, k, v, 14, softmax_scale=0.4, sliding_window=4)
+    k2, v2 = k.copy(), v.copy()
+    k2[:8] = np.nan                       # before every row's window (rows see j >= 11)
+    v2[:8] = np.nan
+    np.testing.assert_array_equal(O.attend_sequence(q, k2, v2, 14, softmax_scale=0.4,
+                                                    sliding_window=4), base)
+    v3 = v.copy()
+    v3[12] = np.nan                       # visible from positions 12..15 = rows 0, 1
+    o3 = O.attend_sequence(q, k, v3, 14, softmax_scale=0.4, sliding_window=4)
+    assert np.isnan(o3[:2]).all() and np.isfinite(o3[2:]).all()
+    np.testing.assert_array_equal(o3[2:], base[2:])

@@ -36,8 +36,8 @@ MUTANTS = [
      "y = np.asarray(x_f32, dtype=np.float32) * s"),
     ("no_clamp", "y = np.clip(y, np.float32(-448.0), np.float32(448.0))", "y = y"),
     ("num_seqs_drops_mixed", "return int(d[0] + d[1] + d[2])", "return int(d[0] + d[1])"),
-    ("pv_wrong_operand", "out[:, h, :] = (w @ v[:, g, :]) / z[:, None]",
-     "out[:, h, :] = (w @ k[:, g, :]) / z[:, None]"),
+    ("pv_wrong_operand", "out[:, h, :] = _weighted_sum(w, v[:, g, :], mask) / z[:, None]",
+     "out[:, h, :] = _weighted_sum(w, k[:, g, :], mask) / z[:, None]"),
     ("exp_sign", "w = np.where(mask, np.exp(s - m[:, None]), 0.0)",
      "w = np.where(mask, np.exp(m[:, None] - s), 0.0)"),
     ("subnormal_scale", "return s * (m / 8.0) * 2.0 ** -6", "return s * (m / 8.0) * 2.0 ** -7"),
@@ -65,6 +65,7 @@ PINS = [
     T.test_tiny_config_bruteforce_end_to_end,
     T.test_fp8_prefill_equals_sdpa_on_library_dequant,
     T.test_q_scale_multiplies_logits,
+    T.test_masked_slots_may_hold_nan,
     test_fp8_codec.test_decode_all_codes_match_torch,
     test_fp8_codec.test_closed_forms,
     test_fp8_codec.test_encode_every_bf16_pattern_matches_torch,
