@@ -1,0 +1,186 @@
+/*
+ * rpa.h -- C ABI of the MI355X (gfx950) ragged paged attention library.
+ *
+ * Two operations, mirroring the ragged-paged-attention v3 interface (ejkernel
+ * docs, "ragged_page_attention_v3" signature and parameter list):
+ *
+ *   rpa_update_kv_cache  writes each step's new K/V tokens into their pages
+ *                        (tpu-inference v3 kernel diff, "_update_kv_cache").
+ *   rpa_forward          optionally performs that update, then attention of
+ *                        the concatenated ragged queries over the paged cache
+ *                        (same diff, "flash_attention_step1_qk_softmax" and
+ *                        "flash_attention_step2_pv"; the v3 call returns the
+ *                        output and the updated cache).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every array pointer is a DEVICE pointer owned by the caller.  The library
+ *   never allocates, frees or copies caller memory, and never synchronises
+ *   the stream.  All work is enqueued on `stream` (a hipStream_t, NULL = the
+ *   default stream).
+ * - All shape checks happen on the host before anything is enqueued: a call
+ *   that returns an error has no side effect.
+ * - Layouts (row-major, contiguous):
+ *     queries, out       [total_tokens, num_q_heads, head_dim]      in q_dtype
+ *     keys, values       [total_tokens, num_kv_heads, head_dim]     in kv_in_dtype
+ *     kv_cache           [num_pages, page_size, 2*num_kv_heads, head_dim_padded]
+ *                        in cache_dtype.  This is the same memory as the v3
+ *                        shape [num_pages, page_size, 2*num_kv_heads/kv_packing,
+ *                        kv_packing, head_dim_padded]: combined head 2h holds
+ *                        K of kv head h and 2h+1 holds its V ("k and v are
+ *                        packed together", v3 kernel diff).  Lanes
+ *                        [head_dim, head_dim_padded) are zero-filled on update.
+ *     kv_lens            int32[max_num_seqs]   kv length INCLUDING the new tokens
+ *     block_tables       int32[max_num_seqs * pages_per_seq]  page ids per sequence
+ *     query_start_loc    int32[max_num_seqs + 1]  cumulative query lengths
+ *     distribution       int32[3] = (decode, prefill, mixed) sequence counts;
+ *                        num_seqs = their sum.  Entries of the metadata past
+ *                        num_seqs are never read.
+ *     attention_sink     float32[num_q_heads] or NULL
+ * - Sequence s owns query rows [qsl[s], qsl[s+1]); its queries are the LAST
+ *   q_len = qsl[s+1]-qsl[s] positions of a kv_len-token sequence (vLLM
+ *   differential_flash_attn.py, context_len/query_len/seq_len diagram), so
+ *   query t sits at position kv_len - q_len + t and sees keys j <= that
+ *   position (and, with a window W > 0, the W most recent of them).
+ * - Device-side preconditions (documented, not checked):
+ *   0 <= q_len <= kv_len <= pages_per_seq*page_size; qsl non-decreasing from
+ *   0 with qsl[num_seqs] <= total_tokens; block-table entries that cover
+ *   [0, kv_len) are < num_pages; the slots written by one update are
+ *   distinct.  Block-table entries past ceil(kv_len/page_size) are not read.
+ */
+#ifndef RPA_H_
+#define RPA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  The pages raise NotImplementedError / ValueError / assert
+ * for unsupported features, bad head sizes and shape mismatches (tpu-inference
+ * layers/vllm/attention.py and vLLM differential_flash_attn.py); the C ABI
+ * returns codes instead. */
+enum {
+  RPA_OK = 0,
+  RPA_ERR_NULL_POINTER = 1,   /* a required pointer is NULL */
+  RPA_ERR_INVALID_SHAPE = 2,  /* non-positive or inconsistent sizes */
+  RPA_ERR_UNSUPPORTED = 3,    /* head_dim / page_size / dtype combination not built */
+  RPA_ERR_INVALID_OPTION = 4, /* negative window or cap, non-finite scale */
+  RPA_ERR_WORKSPACE = 5,      /* workspace missing or smaller than rpa_workspace_bytes */
+  RPA_ERR_HIP = 6             /* a HIP launch failed (see rpa_error_string) */
+};
+
+typedef enum {
+  RPA_F32 = 0,
+  RPA_BF16 = 1,
+  RPA_FP8_E4M3 = 2 /* OCP e4m3fn: bias 7, max 448, no infinity, NaN = 0x7F/0xFF */
+} rpa_dtype;
+
+/* Static sizes of a call.  Passed by pointer, read on the host only. */
+typedef struct rpa_desc {
+  int32_t total_tokens;     /* rows of queries / keys / values / out */
+  int32_t max_num_seqs;     /* length of kv_lens (query_start_loc has +1) */
+  int32_t pages_per_seq;    /* row length of block_tables */
+  int32_t num_pages;        /* pages in kv_cache */
+  int32_t page_size;        /* tokens per page: 16, 32, 64 or 128 */
+  int32_t num_q_heads;      /* multiple of num_kv_heads (GQA) */
+  int32_t num_kv_heads;
+  int32_t head_dim;         /* 64 or 128 */
+  int32_t head_dim_padded;  /* >= head_dim; head_dim_padded*elem_size % 16 == 0 */
+  int32_t q_dtype;          /* rpa_dtype of queries and out */
+  int32_t kv_in_dtype;      /* rpa_dtype of keys / values */
+  int32_t cache_dtype;      /* rpa_dtype of kv_cache */
+} rpa_desc;
+/* Supported (q, kv_in, cache) dtype triples: (F32, F32, F32),
+ * (BF16, BF16, BF16), (BF16, BF16, FP8_E4M3), (BF16, FP8_E4M3, FP8_E4M3). */
+
+/* Scalar options of rpa_forward (the v3 keyword arguments). */
+typedef struct rpa_options {
+  float softmax_scale;      /* multiplies q.k (v3 default 1.0; pass it explicitly) */
+  int32_t sliding_window;   /* 0 = off; W > 0: key j visible iff pos - j < W */
+  float logits_soft_cap;    /* 0 = off; c > 0: s -> c * tanh(s / c), after all scales */
+  float q_scale;            /* 0 = none (1.0); multiplies the logits */
+  float k_scale;            /* 0 = none (1.0); K as read = stored element * k_scale */
+  float v_scale;            /* 0 = none (1.0); V as read = stored element * v_scale */
+  int32_t chunk_prefill_size;      /* tuning hints; 0 = automatic; results do */
+  int32_t num_kv_pages_per_block;  /* not depend on them */
+  int32_t num_queries_per_block;
+  int64_t lds_limit_bytes;         /* the v3 vmem_limit_bytes; 0 = automatic */
+} rpa_options;
+
+/* Paged KV-cache update (the scatter).
+ *
+ * For every valid sequence s and every t < q_len: with pos = kv_len - q_len + t,
+ * page = block_tables[s*pages_per_seq + pos/page_size], off = pos % page_size,
+ * and for every kv head h:
+ *   kv_cache[page][off][2h  ][0:head_dim] = encode(keys  [qsl[s]+t][h][:], k_scale)
+ *   kv_cache[page][off][2h+1][0:head_dim] = encode(values[qsl[s]+t][h][:], v_scale)
+ *   lanes [head_dim, head_dim_padded) of both rows = 0.
+ * No other byte of kv_cache changes.  encode() is a bit copy when
+ * kv_in_dtype == cache_dtype; for an FP8_E4M3 cache fed with BF16 keys it is
+ * the quantisation step applied before the v3 kernel ("quantize_kv" in
+ * tpu-inference layers/vllm/attention.py): y = x / scale in float32 (IEEE
+ * round-to-nearest-even), clamped to [-448, 448], rounded to the nearest
+ * e4m3fn code with ties to even (NaN -> 0x7F with its sign).  A scale of 0
+ * means 1.0.  The result is bit-exact and independent of launch geometry.
+ * `distribution` supplies num_seqs.  Returns RPA_OK or an error code.
+ */
+int rpa_update_kv_cache(const rpa_desc* desc, const void* keys, const void* values,
+                        void* kv_cache, const int32_t* kv_lens, const int32_t* block_tables,
+                        const int32_t* query_start_loc, const int32_t* distribution,
+                        float k_scale, float v_scale, void* stream);
+
+/* Bytes of device workspace rpa_forward needs for these sizes and options
+ * (plan, work lists and split-KV partial results).  Writes *bytes; returns a
+ * status code (the same host checks rpa_forward makes). */
+int rpa_workspace_bytes(const rpa_desc* desc, const rpa_options* opts, size_t* bytes);
+
+/* Ragged paged attention (v3 semantics), optionally preceded by the update.
+ *
+ * If keys and values are both non-NULL, first performs exactly
+ * rpa_update_kv_cache(desc, keys, values, kv_cache, ..., opts->k_scale,
+ * opts->v_scale, stream); if both are NULL the cache is used as it is.
+ * Then for every valid sequence s, query row r = qsl[s] + t (t < q_len) and
+ * q head h (kv head g = h / (num_q_heads/num_kv_heads)):
+ *   s_j  = softmax_scale * q_scale * k_scale * (q[r][h] . Kstored[s][j][g])
+ *   s_j  = cap * tanh(s_j / cap)                       if cap > 0
+ *   out[r][h] = sum_{j visible} e^{s_j} v_scale*Vstored[s][j][g]
+ *               / (sum_{j visible} e^{s_j} + e^{sink[h]} if a sink is given)
+ * computed with an online softmax in float32 and rounded (nearest even) to
+ * q_dtype.  Rows >= qsl[num_seqs] of `out` are not written.  The result does
+ * not depend on `distribution` beyond num_seqs, nor on the tuning hints.
+ * `workspace` must hold rpa_workspace_bytes() bytes (device memory, caller
+ * owned, contents need not be initialised; it is overwritten).
+ * Concurrent calls must use distinct workspaces.
+ */
+int rpa_forward(const rpa_desc* desc, const rpa_options* opts, const void* queries,
+                const void* keys, const void* values, void* kv_cache, const int32_t* kv_lens,
+                const int32_t* block_tables, const int32_t* query_start_loc,
+                const int32_t* distribution, const float* attention_sink, void* out,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable text of a status code (for RPA_ERR_HIP, includes the last
+ * HIP error seen by the library). */
+const char* rpa_error_string(int status);
+
+/* Kernel timing for measurement.  While enabled, every kernel the library
+ * launches is bracketed by a pair of hipEvents recorded on the launch stream.
+ * rpa_profile_read() waits for the recorded events, writes up to `max`
+ * per-kernel aggregates and clears the record; it returns the number of
+ * kernels written, or a negative status.  Off by default. */
+typedef struct rpa_kernel_stat {
+  char name[32];      /* kernel name */
+  int32_t launches;   /* number of launches recorded */
+  double total_ms;    /* summed event-to-event duration */
+} rpa_kernel_stat;
+
+int rpa_profile_enable(int on);
+int rpa_profile_read(rpa_kernel_stat* stats, int max);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RPA_H_ */

@@ -1,0 +1,182 @@
+"""MI355X-native ragged paged attention with paged KV-cache scatter.
+
+Thin Python binding over librpa.so (include/rpa.h).  PyTorch supplies device
+memory and the current HIP stream; every step of the computation runs in the
+library's HIP kernels.  The two operations follow the ragged paged attention
+v3 interface (ejkernel ``ragged_page_attention_v3`` signature):
+
+* :func:`rpa_update_kv_cache` -- scatter new K/V tokens into their pages;
+* :func:`rpa_forward` -- optional update, then attention of the ragged query
+  batch over the paged cache; returns ``(out, kv_cache)``.
+"""
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import RpaDesc, RpaError, RpaKernelStat, RpaOptions
+
+__all__ = ["rpa_update_kv_cache", "rpa_forward", "rpa_workspace_bytes", "profile_enable",
+           "profile_read", "RpaError"]
+
+_DT = {torch.float32: _lib.RPA_F32, torch.bfloat16: _lib.RPA_BF16, torch.uint8: _lib.RPA_FP8_E4M3,
+       torch.float8_e4m3fn: _lib.RPA_FP8_E4M3}
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+    return dev
+
+
+def _meta(t: torch.Tensor, name: str):
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+    return t
+
+
+def _cache_dims(kv_cache: torch.Tensor):
+    if kv_cache.dim() == 5:       # [P, ps, 2Hkv/packing, packing, Dpad]
+        P, ps, a, b, dp = kv_cache.shape
+        return P, ps, a * b, dp
+    if kv_cache.dim() == 4:       # [P, ps, 2Hkv, Dpad]
+        return tuple(kv_cache.shape)
+    raise ValueError("kv_cache must be [num_pages, page_size, 2*num_kv_heads(/packing, packing), "
+                     "head_dim_padded]")
+
+
+def _desc(queries, kv_in_dtype, kv_cache, kv_lens, block_tables, num_kv_heads=None):
+    T, Hq, D = queries.shape
+    P, ps, two_h, dp = _cache_dims(kv_cache)
+    if two_h % 2:
+        raise ValueError("kv_cache head axis must hold 2 * num_kv_heads rows")
+    Hkv = two_h // 2 if num_kv_heads is None else num_kv_heads
+    max_num_seqs = kv_lens.shape[0]
+    if block_tables.numel() % max(max_num_seqs, 1):
+        raise ValueError("block_tables must hold max_num_seqs * pages_per_seq entries")
+    pps = block_tables.numel() // max(max_num_seqs, 1)
+    d = RpaDesc()
+    d.total_tokens, d.max_num_seqs, d.pages_per_seq, d.num_pages, d.page_size = \
+        T, max_num_seqs, pps, P, ps
+    d.num_q_heads, d.num_kv_heads, d.head_dim, d.head_dim_padded = Hq, Hkv, D, dp
+    d.q_dtype, d.kv_in_dtype, d.cache_dtype = _dtype(queries), kv_in_dtype, _dtype(kv_cache)
+    return d
+
+
+def _options(softmax_scale, sliding_window, logits_soft_cap, q_scale, k_scale, v_scale,
+             chunk_prefill_size, num_kv_pages_per_block, num_queries_per_block, vmem_limit_bytes):
+    o = RpaOptions()
+    o.softmax_scale = float(softmax_scale)
+    o.sliding_window = int(sliding_window or 0)
+    o.logits_soft_cap = float(logits_soft_cap or 0.0)
+    o.q_scale = float(q_scale or 0.0)
+    o.k_scale = float(k_scale or 0.0)
+    o.v_scale = float(v_scale or 0.0)
+    o.chunk_prefill_size = int(chunk_prefill_size or 0)
+    o.num_kv_pages_per_block = int(num_kv_pages_per_block or 0)
+    o.num_queries_per_block = int(num_queries_per_block or 0)
+    o.lds_limit_bytes = int(vmem_limit_bytes or 0)
+    return o
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def rpa_update_kv_cache(keys, values, kv_cache, kv_lens, block_tables, query_start_loc,
+                        distribution, *, k_scale=None, v_scale=None, queries_dtype=None):
+    """Write new tokens' K/V ([T, Hkv, D]) into their pages of `kv_cache` in place."""
+    dev = _check_dev(keys, values, kv_cache, kv_lens, block_tables, query_start_loc, distribution)
+    for t, n in ((kv_lens, "kv_lens"), (block_tables, "block_tables"),
+                 (query_start_loc, "query_start_loc"), (distribution, "distribution")):
+        _meta(t, n)
+    T, Hkv, D = keys.shape
+    qdt = queries_dtype if queries_dtype is not None else (
+        torch.float32 if keys.dtype == torch.float32 else torch.bfloat16)
+    fake_q = torch.empty((T, Hkv, D), dtype=qdt, device="meta")
+    d = _desc(fake_q, _dtype(keys), kv_cache, kv_lens, block_tables, num_kv_heads=Hkv)
+    lib = _lib.load()
+    _lib.check(lib.rpa_update_kv_cache(
+        ctypes.byref(d), _ptr(keys), _ptr(values), _ptr(kv_cache), _ptr(kv_lens),
+        _ptr(block_tables), _ptr(query_start_loc), _ptr(distribution),
+        float(k_scale or 0.0), float(v_scale or 0.0), _stream(dev)))
+    return kv_cache
+
+
+def rpa_workspace_bytes(desc: RpaDesc, opts: RpaOptions) -> int:
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.load().rpa_workspace_bytes(ctypes.byref(desc), ctypes.byref(opts),
+                                               ctypes.byref(n)))
+    return n.value
+
+
+def rpa_forward(queries, keys, values, kv_cache, kv_lens, block_tables, query_start_loc,
+                distribution, attention_sink=None, *, softmax_scale=1.0, sliding_window=None,
+                logits_soft_cap=None, q_scale=None, k_scale=None, v_scale=None,
+                chunk_prefill_size=None, num_kv_pages_per_block=None,
+                num_queries_per_block=None, vmem_limit_bytes=None, out=None, workspace=None):
+    """Ragged paged attention (v3 semantics).  `keys`/`values` may be None to
+    attend over the cache as it is.  Returns ``(out, kv_cache)``; the cache is
+    updated in place."""
+    if (keys is None) != (values is None):
+        raise ValueError("keys and values must both be given or both be None")
+    dev = _check_dev(queries, keys, values, kv_cache, kv_lens, block_tables, query_start_loc,
+                     distribution, attention_sink, out, workspace)
+    for t, n in ((kv_lens, "kv_lens"), (block_tables, "block_tables"),
+                 (query_start_loc, "query_start_loc"), (distribution, "distribution")):
+        _meta(t, n)
+    if attention_sink is not None and attention_sink.dtype != torch.float32:
+        raise TypeError("attention_sink must be float32")
+    kv_in = _dtype(keys) if keys is not None else _dtype(kv_cache)
+    d = _desc(queries, kv_in, kv_cache, kv_lens, block_tables)
+    if keys is not None and keys.shape[1] != d.num_kv_heads:
+        raise ValueError("keys head count does not match the cache")
+    o = _options(softmax_scale, sliding_window, logits_soft_cap, q_scale, k_scale, v_scale,
+                 chunk_prefill_size, num_kv_pages_per_block, num_queries_per_block,
+                 vmem_limit_bytes)
+    nbytes = rpa_workspace_bytes(d, o)
+    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty(queries.shape, dtype=queries.dtype, device=dev)
+    lib = _lib.load()
+    _lib.check(lib.rpa_forward(
+        ctypes.byref(d), ctypes.byref(o), _ptr(queries), _ptr(keys), _ptr(values),
+        _ptr(kv_cache), _ptr(kv_lens), _ptr(block_tables), _ptr(query_start_loc),
+        _ptr(distribution), _ptr(attention_sink), _ptr(out), _ptr(workspace),
+        ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(dev)))
+    return out, kv_cache
+
+
+def profile_enable(on: bool = True):
+    _lib.check(_lib.load().rpa_profile_enable(1 if on else 0))
+
+
+def profile_read() -> dict:
+    """{kernel name: (launches, total_ms)} since the last read."""
+    buf = (RpaKernelStat * 32)()
+    n = _lib.load().rpa_profile_read(buf, 32)
+    if n < 0:
+        _lib.check(-n)
+    return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(n)}

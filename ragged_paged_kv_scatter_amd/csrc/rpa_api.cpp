@@ -1,0 +1,360 @@
+// Host side of the C ABI: argument validation (all before any launch),
+// workspace layout, kernel sequencing on the caller's stream, error strings
+// and the optional per-kernel event timing.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "rpa.h"
+#include "rpa_internal.h"
+
+namespace rpa {
+namespace {
+
+thread_local std::string g_last_hip_error;
+
+int elem_size(int dt) { return dt == RPA_F32 ? 4 : dt == RPA_BF16 ? 2 : 1; }
+
+bool valid_dtype(int dt) { return dt == RPA_F32 || dt == RPA_BF16 || dt == RPA_FP8_E4M3; }
+
+bool supported_triple(int q, int in, int c) {
+  return (q == RPA_F32 && in == RPA_F32 && c == RPA_F32) ||
+         (q == RPA_BF16 && in == RPA_BF16 && c == RPA_BF16) ||
+         (q == RPA_BF16 && in == RPA_BF16 && c == RPA_FP8_E4M3) ||
+         (q == RPA_BF16 && in == RPA_FP8_E4M3 && c == RPA_FP8_E4M3);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool finite_nonneg(float x) { return std::isfinite(x) && x >= 0.f; }
+
+constexpr int kMaxSeqs = 16000;  // planner keeps a per-sequence table in LDS
+
+int check_desc(const rpa_desc* d) {
+  if (!d) return RPA_ERR_NULL_POINTER;
+  if (d->total_tokens < 0 || d->max_num_seqs < 0 || d->pages_per_seq <= 0 ||
+      d->num_pages <= 0 || d->page_size <= 0 || d->num_q_heads <= 0 ||
+      d->num_kv_heads <= 0 || d->head_dim <= 0 || d->head_dim_padded < d->head_dim)
+    return RPA_ERR_INVALID_SHAPE;
+  if (d->num_q_heads % d->num_kv_heads != 0) return RPA_ERR_INVALID_SHAPE;
+  if (!valid_dtype(d->q_dtype) || !valid_dtype(d->kv_in_dtype) || !valid_dtype(d->cache_dtype))
+    return RPA_ERR_UNSUPPORTED;
+  if (!supported_triple(d->q_dtype, d->kv_in_dtype, d->cache_dtype)) return RPA_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return RPA_ERR_UNSUPPORTED;
+  const int ps = d->page_size;
+  if (ps != 16 && ps != 32 && ps != 64 && ps != 128) return RPA_ERR_UNSUPPORTED;
+  const int g = d->num_q_heads / d->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16) return RPA_ERR_UNSUPPORTED;
+  if (((long long)d->head_dim_padded * elem_size(d->cache_dtype)) % 16 != 0)
+    return RPA_ERR_UNSUPPORTED;
+  if (d->max_num_seqs > kMaxSeqs) return RPA_ERR_UNSUPPORTED;
+  return RPA_OK;
+}
+
+int check_meta(const void* kv_lens, const void* bt, const void* qsl, const void* dist) {
+  if (!kv_lens || !bt || !qsl || !dist) return RPA_ERR_NULL_POINTER;
+  return RPA_OK;
+}
+
+int check_options(const rpa_options* o) {
+  if (!o) return RPA_ERR_NULL_POINTER;
+  if (!std::isfinite(o->softmax_scale)) return RPA_ERR_INVALID_OPTION;
+  if (o->sliding_window < 0) return RPA_ERR_INVALID_OPTION;
+  if (!finite_nonneg(o->logits_soft_cap)) return RPA_ERR_INVALID_OPTION;
+  if (!finite_nonneg(o->q_scale) || !finite_nonneg(o->k_scale) || !finite_nonneg(o->v_scale))
+    return RPA_ERR_INVALID_OPTION;
+  if (o->chunk_prefill_size < 0 || o->num_kv_pages_per_block < 0 ||
+      o->num_queries_per_block < 0 || o->lds_limit_bytes < 0)
+    return RPA_ERR_INVALID_OPTION;
+  return RPA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = hipGetErrorString(e);
+  return RPA_ERR_HIP;
+}
+
+// ---- profiling ------------------------------------------------------------
+struct ProfRec {
+  std::string name;
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_recs;
+std::vector<hipEvent_t> g_event_pool;
+ProfRec g_pending;
+bool g_have_pending = false;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+}  // namespace
+
+void prof_begin(const char* name, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on) return;
+  g_pending.name = name;
+  g_pending.start = take_event();
+  g_pending.stop = take_event();
+  g_have_pending = g_pending.start && g_pending.stop;
+  if (g_have_pending) (void)hipEventRecord(g_pending.start, s);
+}
+
+void prof_end(hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on || !g_have_pending) return;
+  (void)hipEventRecord(g_pending.stop, s);
+  g_prof_recs.push_back(g_pending);
+  g_have_pending = false;
+}
+
+bool prefill_supported(const rpa_desc& d);
+
+int prefill_min_q(const rpa_desc& d) {
+  return prefill_supported(d) ? 2 : INT_MAX;
+}
+
+Workspace workspace_layout(const rpa_desc& d) {
+  Workspace w = {};
+  const long long T = d.total_tokens;
+  const int pmq = prefill_min_q(d);
+  long long max_rows = T;
+  if (pmq != INT_MAX) max_rows = std::min<long long>(T, (long long)d.max_num_seqs * (pmq - 1));
+  w.max_rows = (int32_t)std::max<long long>(max_rows, 1);
+  w.max_items = kTargetItems + w.max_rows;
+  w.max_parts = std::min(2 * kTargetItems, w.max_items);
+  w.max_merge_rows = std::min(kTargetItems, w.max_rows);
+  w.max_pf_items = (pmq != INT_MAX)
+                       ? (int32_t)((T + kPrefillBQ - 1) / kPrefillBQ + d.max_num_seqs + 1)
+                       : 1;
+  size_t off = 0;
+  w.header = off;
+  off = align256(off + sizeof(PlanHeader));
+  w.seq_rows = off;
+  w.rows = off;
+  off = align256(off + (size_t)w.max_rows * sizeof(RowDesc));
+  w.items = off;
+  off = align256(off + (size_t)w.max_items * sizeof(ItemDesc));
+  w.merge_rows = off;
+  off = align256(off + (size_t)w.max_merge_rows * sizeof(int32_t));
+  w.pf_items = off;
+  off = align256(off + (size_t)w.max_pf_items * sizeof(PrefillItem));
+  w.part_ml = off;
+  off = align256(off + (size_t)w.max_parts * d.num_q_heads * 2 * sizeof(float));
+  w.part_acc = off;
+  off = align256(off + (size_t)w.max_parts * d.num_q_heads * d.head_dim * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+}  // namespace rpa
+
+using namespace rpa;
+
+extern "C" {
+
+int rpa_update_kv_cache(const rpa_desc* desc, const void* keys, const void* values,
+                        void* kv_cache, const int32_t* kv_lens, const int32_t* block_tables,
+                        const int32_t* query_start_loc, const int32_t* distribution,
+                        float k_scale, float v_scale, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (!keys || !values || !kv_cache) return RPA_ERR_NULL_POINTER;
+  if ((st = check_meta(kv_lens, block_tables, query_start_loc, distribution))) return st;
+  if (!finite_nonneg(k_scale) || !finite_nonneg(v_scale)) return RPA_ERR_INVALID_OPTION;
+  if (!aligned16(keys) || !aligned16(values) || !aligned16(kv_cache)) return RPA_ERR_INVALID_SHAPE;
+  if (desc->total_tokens == 0 || desc->max_num_seqs == 0) return RPA_OK;
+  ScatterParams p = {};
+  p.keys = keys;
+  p.values = values;
+  p.cache = kv_cache;
+  p.kv_lens = kv_lens;
+  p.block_tables = block_tables;
+  p.qsl = query_start_loc;
+  p.dist = distribution;
+  p.T = desc->total_tokens;
+  p.max_num_seqs = desc->max_num_seqs;
+  p.pps = desc->pages_per_seq;
+  p.page_size = desc->page_size;
+  p.Hkv = desc->num_kv_heads;
+  p.D = desc->head_dim;
+  p.Dpad = desc->head_dim_padded;
+  p.inv_k_scale_src = k_scale > 0.f ? k_scale : 1.f;
+  p.inv_v_scale_src = v_scale > 0.f ? v_scale : 1.f;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  prof_begin("scatter", s);
+  hipError_t e = launch_scatter(p, (rpa_dtype)desc->kv_in_dtype, (rpa_dtype)desc->cache_dtype, s);
+  prof_end(s);
+  return e == hipSuccess ? RPA_OK : hip_fail(e);
+}
+
+int rpa_workspace_bytes(const rpa_desc* desc, const rpa_options* opts, size_t* bytes) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if ((st = check_options(opts))) return st;
+  if (!bytes) return RPA_ERR_NULL_POINTER;
+  *bytes = workspace_layout(*desc).total;
+  return RPA_OK;
+}
+
+int rpa_forward(const rpa_desc* desc, const rpa_options* opts, const void* queries,
+                const void* keys, const void* values, void* kv_cache, const int32_t* kv_lens,
+                const int32_t* block_tables, const int32_t* query_start_loc,
+                const int32_t* distribution, const float* attention_sink, void* out,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if ((st = check_options(opts))) return st;
+  if (!queries || !kv_cache || !out) return RPA_ERR_NULL_POINTER;
+  if ((keys == nullptr) != (values == nullptr)) return RPA_ERR_NULL_POINTER;
+  if ((st = check_meta(kv_lens, block_tables, query_start_loc, distribution))) return st;
+  if (!aligned16(queries) || !aligned16(kv_cache) || !aligned16(out) ||
+      (keys && (!aligned16(keys) || !aligned16(values))))
+    return RPA_ERR_INVALID_SHAPE;
+  const Workspace lay = workspace_layout(*desc);
+  if (!workspace || workspace_bytes < lay.total || !aligned16(workspace)) return RPA_ERR_WORKSPACE;
+  if (desc->total_tokens == 0 || desc->max_num_seqs == 0) return RPA_OK;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (keys) {
+    st = rpa_update_kv_cache(desc, keys, values, kv_cache, kv_lens, block_tables,
+                             query_start_loc, distribution, opts->k_scale, opts->v_scale, stream);
+    if (st) return st;
+  }
+  char* ws = static_cast<char*>(workspace);
+  PlanParams pp = {};
+  pp.kv_lens = kv_lens;
+  pp.qsl = query_start_loc;
+  pp.dist = distribution;
+  pp.ws = ws;
+  pp.lay = lay;
+  pp.max_num_seqs = desc->max_num_seqs;
+  pp.T = desc->total_tokens;
+  pp.window = opts->sliding_window;
+  pp.prefill_min_q = prefill_min_q(*desc);
+  prof_begin("plan", s);
+  hipError_t e = launch_plan(pp, s);
+  prof_end(s);
+  if (e != hipSuccess) return hip_fail(e);
+
+  AttnParams ap = {};
+  ap.q = queries;
+  ap.cache = kv_cache;
+  ap.kv_lens = kv_lens;
+  ap.block_tables = block_tables;
+  ap.qsl = query_start_loc;
+  ap.sink = attention_sink;
+  ap.out = out;
+  ap.ws = ws;
+  ap.lay = lay;
+  ap.Hq = desc->num_q_heads;
+  ap.Hkv = desc->num_kv_heads;
+  ap.D = desc->head_dim;
+  ap.Dpad = desc->head_dim_padded;
+  ap.page_size = desc->page_size;
+  ap.pps = desc->pages_per_seq;
+  ap.window = opts->sliding_window;
+  const float qs = opts->q_scale > 0.f ? opts->q_scale : 1.f;
+  const float ks = opts->k_scale > 0.f ? opts->k_scale : 1.f;
+  ap.qk_scale = opts->softmax_scale * qs * ks;
+  ap.v_scale = opts->v_scale > 0.f ? opts->v_scale : 1.f;
+  ap.cap = opts->logits_soft_cap;
+  const rpa_dtype qd = (rpa_dtype)desc->q_dtype, cd = (rpa_dtype)desc->cache_dtype;
+
+  if (prefill_supported(*desc)) {
+    prof_begin("prefill", s);
+    e = launch_prefill(ap, qd, cd, s);
+    prof_end(s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  prof_begin("decode", s);
+  e = launch_rows(ap, qd, cd, s);
+  prof_end(s);
+  if (e != hipSuccess) return hip_fail(e);
+  prof_begin("merge", s);
+  e = launch_merge(ap, qd, s);
+  prof_end(s);
+  if (e != hipSuccess) return hip_fail(e);
+  return RPA_OK;
+}
+
+const char* rpa_error_string(int status) {
+  switch (status) {
+    case RPA_OK: return "ok";
+    case RPA_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case RPA_ERR_INVALID_SHAPE: return "invalid or inconsistent sizes, or a misaligned buffer";
+    case RPA_ERR_UNSUPPORTED:
+      return "unsupported configuration (head_dim 64/128, page_size 16/32/64/128, "
+             "q/kv heads ratio 1/2/4/8/16, supported dtype triples only)";
+    case RPA_ERR_INVALID_OPTION: return "invalid option (negative or non-finite value)";
+    case RPA_ERR_WORKSPACE: return "workspace missing or smaller than rpa_workspace_bytes()";
+    case RPA_ERR_HIP: {
+      static thread_local std::string msg;
+      msg = "HIP error: " + g_last_hip_error;
+      return msg.c_str();
+    }
+    default: return "unknown status";
+  }
+}
+
+int rpa_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return RPA_OK;
+}
+
+int rpa_profile_read(rpa_kernel_stat* stats, int max) {
+  std::vector<ProfRec> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    recs.swap(g_prof_recs);
+  }
+  std::vector<rpa_kernel_stat> agg;
+  int err = 0;
+  for (auto& r : recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess ||
+        hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
+      err = 1;
+    size_t i = 0;
+    for (; i < agg.size(); ++i)
+      if (r.name == agg[i].name) break;
+    if (i == agg.size()) {
+      rpa_kernel_stat k = {};
+      std::snprintf(k.name, sizeof(k.name), "%s", r.name.c_str());
+      agg.push_back(k);
+    }
+    agg[i].launches += 1;
+    agg[i].total_ms += ms;
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    for (auto& r : recs) {
+      g_event_pool.push_back(r.start);
+      g_event_pool.push_back(r.stop);
+    }
+  }
+  if (err) return -RPA_ERR_HIP;
+  const int n = (int)std::min<size_t>(agg.size(), (size_t)std::max(max, 0));
+  for (int i = 0; i < n; ++i) stats[i] = agg[i];
+  return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,125 @@
+// Internal declarations shared by the host library and the HIP kernels:
+// the plan the device-side planner writes into the caller's workspace, the
+// kernel parameter blocks, and the launch entry points of each kernel file.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rpa.h"
+
+namespace rpa {
+
+// ---------------------------------------------------------------------------
+// Tunables of the plan.
+// ---------------------------------------------------------------------------
+// Row-kernel work items aimed for: the KV range of a query row is cut into
+// splits of S tokens with S >= (sum of visible lengths) / kTargetItems, so
+// there are at most kTargetItems + rows items and at most 2 * kTargetItems
+// split partials (every split row has length > S).
+constexpr int kTargetItems = 2048;
+constexpr int kMinSplit = 128;        // never cut a row's KV range finer than this
+constexpr int kPlanThreads = 1024;    // the planner is one workgroup
+constexpr int kWavesPerWG = 4;        // row kernel: one item per wave
+constexpr int kPrefillBQ = 128;       // query tokens per prefill tile (4 waves x 32)
+
+// ---------------------------------------------------------------------------
+// Plan layout in the workspace (all offsets 256-byte aligned).
+// ---------------------------------------------------------------------------
+struct PlanHeader {
+  int32_t num_seqs;      // min(sum(distribution), max_num_seqs)
+  int32_t n_rows;        // query rows handled by the row kernel
+  int32_t n_items;       // (row, split) items of the row kernel
+  int32_t split;         // S, tokens per split
+  int32_t n_merge_rows;  // rows with more than one split
+  int32_t n_pf_items;    // (sequence, query tile) items of the prefill kernel
+  int32_t pad[10];
+};
+
+struct RowDesc {         // one query row of the row (decode) kernel
+  int32_t token;         // row index into queries / out
+  int32_t seq;
+  int32_t lo, hi;        // visible key range [lo, hi) of this row
+  int32_t n_split;
+  int32_t part_base;     // first partial slot (n_split > 1), else -1
+  int32_t pad[2];
+};
+
+struct ItemDesc {        // a split of one row: keys [lo, hi)
+  int32_t row;
+  int32_t lo, hi;
+  int32_t part;          // partial slot, or -1 when the row has a single split
+};
+
+struct PrefillItem {     // a query tile of one prefill sequence
+  int32_t seq;
+  int32_t q_begin, q_end;  // query offsets within the sequence, [q_begin, q_end)
+  int32_t pad;
+};
+
+struct Workspace {       // byte offsets into the caller's workspace
+  size_t header, seq_rows, rows, items, merge_rows, pf_items, part_ml, part_acc, total;
+  int32_t max_rows, max_items, max_parts, max_pf_items, max_merge_rows;
+};
+
+Workspace workspace_layout(const rpa_desc& d);
+
+// Routing of sequences: rows of sequences with q_len >= prefill_min_q go to the
+// MFMA prefill kernel (when the dtype has one), all others to the row kernel.
+int prefill_min_q(const rpa_desc& d);
+
+// ---------------------------------------------------------------------------
+// Kernel parameter blocks (passed by value).
+// ---------------------------------------------------------------------------
+struct ScatterParams {
+  const void* keys;
+  const void* values;
+  void* cache;
+  const int32_t* kv_lens;
+  const int32_t* block_tables;
+  const int32_t* qsl;
+  const int32_t* dist;
+  int32_t T, max_num_seqs, pps, page_size, Hkv, D, Dpad;
+  float inv_k_scale_src, inv_v_scale_src;  // the scales themselves (division done in-kernel)
+};
+
+struct PlanParams {
+  const int32_t* kv_lens;
+  const int32_t* qsl;
+  const int32_t* dist;
+  char* ws;
+  Workspace lay;
+  int32_t max_num_seqs, T, window, prefill_min_q;
+};
+
+struct AttnParams {
+  const void* q;
+  const void* cache;
+  const int32_t* kv_lens;
+  const int32_t* block_tables;
+  const int32_t* qsl;
+  const float* sink;
+  void* out;
+  char* ws;
+  Workspace lay;
+  int32_t Hq, Hkv, D, Dpad, page_size, pps, window;
+  float qk_scale;      // softmax_scale * q_scale * k_scale
+  float v_scale;       // 1 when none
+  float cap;           // 0 when none
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_scatter(const ScatterParams& p, rpa_dtype in_dt, rpa_dtype cache_dt,
+                          hipStream_t s);
+hipError_t launch_plan(const PlanParams& p, hipStream_t s);
+hipError_t launch_rows(const AttnParams& p, rpa_dtype q_dt, rpa_dtype cache_dt, hipStream_t s);
+hipError_t launch_merge(const AttnParams& p, rpa_dtype q_dt, hipStream_t s);
+hipError_t launch_prefill(const AttnParams& p, rpa_dtype q_dt, rpa_dtype cache_dt,
+                          hipStream_t s);
+bool prefill_supported(const rpa_desc& d);
+
+// Profiling hooks used by the launchers' caller.
+void prof_begin(const char* name, hipStream_t s);
+void prof_end(hipStream_t s);
+
+}  // namespace rpa

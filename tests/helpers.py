@@ -59,3 +59,51 @@ def poison_unused(w, include_written=True):
     else:
         flat[bad] = nan[w.cache_dtype]
     return w
+
+
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
+
+
+def tolerance(w):
+    """Max-abs-error bound on the attention output: fp32 workloads 1e-5,
+    bf16 2e-2, fp8-KV 6e-2."""
+    return TOL["fp8"] if w.cache_dtype == "fp8" else TOL[w.q_dtype]
+
+
+def gpu_forward(w, update=True, out=None, **kw):
+    """Run rpa_forward on workload `w` (tensors on the GPU).  `out` is
+    pre-filled with NaN so unwritten rows stay visible."""
+    import ragged_paged_kv_scatter_amd as rpa
+    dev = w.queries.device
+    meta = {k: torch.from_numpy(np.ascontiguousarray(getattr(w, k))).to(dev)
+            for k in ("kv_lens", "block_tables", "query_start_loc", "distribution")}
+    if out is None:
+        out = torch.full(w.queries.shape, float("nan"), dtype=w.queries.dtype, device=dev)
+    opts = w.options()
+    opts.update(kw)
+    rpa.rpa_forward(w.queries, w.keys if update else None, w.values if update else None,
+                    w.kv_cache, meta["kv_lens"], meta["block_tables"], meta["query_start_loc"],
+                    meta["distribution"], w.attention_sink, out=out, **opts)
+    return out
+
+
+def compact_pages(w, seqs, cache_dev=None):
+    """Copy to the host only the pages the given sequences use, and a block
+    table renumbered onto that compact pool (entries of other sequences 0).
+    Returns (cache_bits, block_tables)."""
+    cache_dev = w.kv_cache if cache_dev is None else cache_dev
+    pps, ps = w.pages_per_seq, w.page_size
+    bt = np.zeros_like(w.block_tables)
+    pages = []
+    index = {}
+    for s in seqs:
+        n = -(-int(w.kv_lens[s]) // ps)
+        for i in range(n):
+            p = int(w.block_tables[s * pps + i])
+            if p not in index:
+                index[p] = len(pages)
+                pages.append(p)
+            bt[s * pps + i] = index[p]
+    sel = torch.tensor(pages if pages else [0], dtype=torch.long, device=cache_dev.device)
+    sub = cache_dev.index_select(0, sel)
+    return bits(sub, w.cache_dtype), bt
