@@ -1,0 +1,207 @@
+"""Benchmark of the ragged paged attention hot path on one MI355X.
+
+A step is one rpa_forward call with the step's new keys/values: KV-cache
+update (scatter), device planning, attention and split merge, over one batch of
+synthetic input resident in HBM.  Default workload: bf16 decode (256
+sequences, kv_len ~ U{512..4096}, page_size 16, 32 q heads, 8 kv heads,
+head_dim 128).  Prints ONE JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ragged paged attn: decode KV GB/s + prefill TFLOP/s, % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
+
+
+def work_counts(w):
+    """Algorithmic work of one step.
+
+    kv_bytes: every KV token some query of a sequence can see is read once
+    per sequence, 2 * Hkv * D * elem bytes per token (K and V of all heads).
+    flops: 4 * D per visible (query, key, q head) triple (2D for q.k, 2D for p.v).
+    """
+    kvb = 0
+    pairs = 0
+    tok_bytes = 2 * w.num_kv_heads * w.head_dim * ELEM[w.cache_dtype]
+    W = w.sliding_window
+    for s in range(w.num_seqs):
+        q_len = int(w.query_start_loc[s + 1] - w.query_start_loc[s])
+        kv = int(w.kv_lens[s])
+        ctx = kv - q_len
+        if q_len == 0:
+            continue
+        lo = max(0, ctx - W + 1) if W else 0
+        kvb += (kv - lo) * tok_bytes
+        t = np.arange(q_len, dtype=np.int64)
+        vis = ctx + t + 1
+        if W:
+            vis = np.minimum(vis, W)
+        pairs += int(vis.sum())
+    flops = 4 * w.head_dim * pairs * w.num_q_heads
+    return kvb, flops
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """The oracle as it stands, timed on the host on a bounded sample of the
+    same workload: whole sequences drawn in a fixed order until ~budget_s of
+    CPU work; reported in the metric's unit scaled by the sample's share."""
+    import threadpoolctl
+
+    from oracle import rpa_oracle as O
+    from tests.helpers import bits, compact_pages
+
+    rng = np.random.default_rng(0)
+    order = rng.permutation(w.num_seqs)
+    q_bits = bits(w.queries, w.q_dtype)
+    k_bits = bits(w.keys, w.kv_in_dtype)
+    v_bits = bits(w.values, w.kv_in_dtype)
+    sink = None if w.attention_sink is None else w.attention_sink.cpu().numpy()
+    done, t_used, kvb, flops = 0, 0.0, 0, 0
+    tok_bytes = 2 * w.num_kv_heads * w.head_dim * ELEM[w.cache_dtype]
+    threads = threadpoolctl.threadpool_info()
+    nthreads = max([t.get("num_threads", 1) for t in threads] + [1])
+    for s in order:
+        s = int(s)
+        sub_cache, sub_bt = compact_pages(w, [s])
+        q0, ql, ctx, kvl = O.seq_bounds(w.query_start_loc, w.kv_lens, s)
+        pps = w.pages_per_seq
+        t0 = time.perf_counter()
+        cache = O.update_kv_cache(sub_cache, k_bits[q0:q0 + ql], v_bits[q0:q0 + ql],
+                                  np.array([kvl], np.int32), sub_bt[s * pps:(s + 1) * pps],
+                                  np.array([0, ql], np.int32), np.array([0, 0, 1], np.int32),
+                                  page_size=w.page_size, pages_per_seq=pps,
+                                  kv_in_dtype=w.kv_in_dtype, cache_dtype=w.cache_dtype,
+                                  k_scale=w.k_scale, v_scale=w.v_scale)
+        k, v = O.gather_kv(cache, 0, kvl, sub_bt[s * pps:(s + 1) * pps], page_size=w.page_size,
+                           pages_per_seq=pps, head_dim=w.head_dim, cache_dtype=w.cache_dtype,
+                           k_scale=w.k_scale, v_scale=w.v_scale)
+        q = O.to_f64(q_bits[q0:q0 + ql], w.q_dtype)
+        O.attend_sequence(q, k, v, ctx, softmax_scale=w.softmax_scale,
+                          sliding_window=w.sliding_window, logits_soft_cap=w.logits_soft_cap,
+                          q_scale=w.q_scale, sink=sink)
+        t_used += time.perf_counter() - t0
+        lo = max(0, ctx - w.sliding_window + 1) if w.sliding_window else 0
+        kvb += (kvl - lo) * tok_bytes
+        vis = ctx + np.arange(ql) + 1
+        if w.sliding_window:
+            vis = np.minimum(vis, w.sliding_window)
+        flops += 4 * w.head_dim * int(vis.sum()) * w.num_q_heads
+        done += 1
+        if t_used >= budget_s:
+            break
+    return dict(seconds=t_used, seqs=done, kv_bytes=kvb, flops=flops, threads=nthreads)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path needs no "
+              "collective and shards by kv head or by sequence with no exchange.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import ragged_paged_kv_scatter_amd as rpa
+    from ragged_paged_kv_scatter_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.make(args.workload, device=dev)
+    meta = {k: torch.from_numpy(np.ascontiguousarray(getattr(w, k))).to(dev)
+            for k in ("kv_lens", "block_tables", "query_start_loc", "distribution")}
+    out = torch.empty(w.queries.shape, dtype=w.queries.dtype, device=dev)
+    opts = w.options()
+    ws_bytes = rpa.rpa_workspace_bytes(
+        rpa._desc(w.queries, rpa._dtype(w.keys), w.kv_cache, meta["kv_lens"],
+                  meta["block_tables"]),
+        rpa._options(**opts, chunk_prefill_size=None, num_kv_pages_per_block=None,
+                     num_queries_per_block=None, vmem_limit_bytes=None))
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def step():
+        rpa.rpa_forward(w.queries, w.keys, w.values, w.kv_cache, meta["kv_lens"],
+                        meta["block_tables"], meta["query_start_loc"], meta["distribution"],
+                        w.attention_sink, out=out, workspace=workspace, **opts)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    rpa.profile_enable(True)
+    rpa.profile_read()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    rpa.profile_enable(False)
+    kstats = rpa.profile_read()
+    ms = (t1 - t0) * 1e3 / args.steps
+
+    kvb, flops = work_counts(w)
+    decode_like = args.workload != "prefill_bf16"   # prefill reports TFLOP/s, the rest KV GB/s
+    if decode_like:
+        value, unit = kvb / (ms * 1e-3) / 1e9, "GB/s"
+    else:
+        value, unit = flops / (ms * 1e-3) / 1e12, "TFLOP/s"
+    # dominant kernel: the one with the largest summed time
+    dom = max(kstats.items(), key=lambda kv: kv[1][1]) if kstats else ("none", (1, 0.0))
+    dom_name, (dom_n, dom_ms) = dom
+    dom_avg_ms = dom_ms / max(dom_n, 1)
+    if dom_name == "prefill" and not decode_like:
+        achieved = flops / (dom_avg_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=achieved, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=achieved / BF16_PEAK_TFLOPS, traffic=None)
+    else:
+        achieved = kvb / (dom_avg_ms * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=achieved / HBM_PEAK_GBS, traffic=None)
+    roof["kernel"] = dom_name
+    roof["kernel_avg_ms"] = dom_avg_ms
+
+    line = {
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.q_dtype, "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "total_tokens": w.total_tokens,
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "page_size": w.page_size,
+                   "cache_dtype": w.cache_dtype, "kv_bytes": kvb, "flops": flops,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "kernels_ms": {k: v[1] / max(v[0], 1) for k, v in kstats.items()},
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(w, args.cpu_budget)
+        if unit == "GB/s":
+            cv = cb["kv_bytes"] / cb["seconds"] / 1e9
+        else:
+            cv = cb["flops"] / cb["seconds"] / 1e12
+        line["cpu_baseline"] = dict(
+            value=cv, unit=unit, cores=cb["threads"], kind="oracle",
+            sample=f"{cb['seqs']} of {w.num_seqs} sequences (update + gather + float64 "
+                   f"attention), {cb['seconds']:.1f} s on the host")
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
