@@ -55,7 +55,7 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
 }
 
 template <typename CT, int D>
-__global__ __launch_bounds__(NT) void prefill_kernel(AttnParams p) {
+__global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
   constexpr int LS = D + 16;                       // LDS row stride (bf16 elements)
   constexpr int KS = D / 16;                       // MFMA k-steps of q.k
   constexpr int DT = D / 32;                       // 32-row d tiles of O^T
@@ -121,20 +121,29 @@ __global__ __launch_bounds__(NT) void prefill_kernel(AttnParams p) {
   float m_run = -INFINITY, l_run = 0.f;
   const bool use_cap = p.cap > 0.f;
   const float c_scale = use_cap ? p.qk_scale : p.qk_scale * kLog2e;
+  const float c_eff = use_cap ? 1.f : c_scale;   // multiplier from stored logits to log2 units
 
-  // staged loads of one key block: PER chunks of K and of V per thread
+  // Staged loads of one key block: PER chunks of K and of V per thread.  The
+  // page ids a block needs are fetched one block earlier than its data, so a
+  // data load never waits on a block-table load.
   uint4 kr[PER], vr[PER];
+  int pg[PER];
+  auto fetch_pages = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int j = k0 + (tid + NT * i) / CPR;
+      pg[i] = (j >= kv_lo && j < kv_hi) ? bt[j / ps] : -1;
+    }
+  };
   auto fetch = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int c = tid + NT * i;
       const int tok = c / CPR, cc = c - (c / CPR) * CPR;
       const int j = k0 + tok;
-      const bool ok = j >= kv_lo && j < kv_hi;
       uint4 a = make_uint4(0, 0, 0, 0), v = a;
-      if (ok) {
-        const int page = bt[j / ps];
-        const CT* src = kv_head + ((long long)page * ps + (j - (j / ps) * ps)) * row_stride +
+      if (pg[i] >= 0) {
+        const CT* src = kv_head + ((long long)pg[i] * ps + (j - (j / ps) * ps)) * row_stride +
                         cc * (16 / ESZ);
         a = *reinterpret_cast<const uint4*>(src);
         v = *reinterpret_cast<const uint4*>(src + p.Dpad);
@@ -174,13 +183,20 @@ __global__ __launch_bounds__(NT) void prefill_kernel(AttnParams p) {
 
   const int blk_first = kv_lo / BK;
   const int blk_end = (kv_hi + BK - 1) / BK;
-  if (blk_first < blk_end) fetch(blk_first * BK);
+  if (blk_first < blk_end) {
+    fetch_pages(blk_first * BK);
+    fetch(blk_first * BK);
+    if (blk_first + 1 < blk_end) fetch_pages((blk_first + 1) * BK);
+  }
   for (int blk = blk_first; blk < blk_end; ++blk) {
     const int k0 = blk * BK;
     __syncthreads();                      // previous block fully consumed
     stage();
     __syncthreads();                      // block visible to all waves
-    if (blk + 1 < blk_end) fetch(k0 + BK);  // next block in flight during the math
+    if (blk + 1 < blk_end) {              // next block in flight during the math
+      fetch(k0 + BK);
+      if (blk + 2 < blk_end) fetch_pages(k0 + 2 * BK);
+    }
 
     // does this wave see any key of the block, and does it need a mask?
     const bool needed = wave_live && k0 <= wpos_hi && (W <= 0 || k0 + BK - 1 > wpos_lo - W);
@@ -200,7 +216,8 @@ __global__ __launch_bounds__(NT) void prefill_kernel(AttnParams p) {
         sacc[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc[hf], 0, 0, 0);
       }
     }
-    // ---- logits, mask, block max ----
+    // ---- logits (log2 units), mask, block max ----
+    // Without a cap the scale is folded into the exponent: p = 2^(s*c - m).
     float mx = -INFINITY;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
@@ -208,7 +225,6 @@ __global__ __launch_bounds__(NT) void prefill_kernel(AttnParams p) {
       for (int i = 0; i < 16; ++i) {
         float s = sacc[hf][i];
         if (use_cap) s = p.cap * tanhf(s * c_scale / p.cap) * kLog2e;
-        else s = s * c_scale;
         if (!full) {
           const int j = k0 + hf * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
           const bool vis = j <= pos && (W <= 0 || pos - j < W);
@@ -218,25 +234,31 @@ __global__ __launch_bounds__(NT) void prefill_kernel(AttnParams p) {
         mx = fmaxf(mx, s);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c_eff;
+    // Lazy rescaling: the running max only moves (and acc / l are only
+    // rescaled) when some row of the wave grows by more than 2^8; until then
+    // p <= 2^8, harmless in fp32 sums and in bf16.
+    if (__any(mx > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float lsum = 0.f;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(sacc[hf][i] - m_use);
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[hf][i], c_eff, -m_use));
         sacc[hf][i] = pv;
         lsum += pv;
       }
-    l_run = l_run * alpha + lsum;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+    l_run += lsum;
 
     // ---- O^T += V^T P^T over four 16-key steps ----
     const int grp = lane >> 4, r16 = lane & 15;
