@@ -209,18 +209,23 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
   float* part_acc = reinterpret_cast<float*>(p.ws + p.lay.part_acc);
 
   const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
   const int slot = lane / LPT;          // token slot within a load row
   const int dl = lane % LPT;            // d-slice
   const int my_head = dl >> (B - LG);   // head whose logit this lane holds after the scatter
   const int Hkv = p.Hkv;
   const long long total = (long long)hdr->n_items * Hkv;
-  const int ps = p.page_size;
-  const long long row_stride = 2LL * Hkv * p.Dpad;  // elements per cache token row
+  const int sh = p.ps_shift;                        // page_size = 1 << sh
+  const int pmask = (1 << sh) - 1;
+  const uint32_t row_bytes = 2u * Hkv * p.Dpad * (uint32_t)sizeof(CT);  // one cache token row
+  const uint32_t head_bytes = p.Dpad * (uint32_t)sizeof(CT);            // K -> V of a head
   const CT* cache = static_cast<const CT*>(p.cache);
   const bool use_cap = p.cap > 0.f;
   const float c_log2 = p.qk_scale * kLog2e;
 
+  // The grid is the number of resident waves; wave w walks items w, w + grid,
+  // ...  The planner lists full-size splits first, so every wave ends on the
+  // short remainder splits and the launch has no long tail.
+  const int wave = threadIdx.x >> 6;
   for (long long idx = (long long)blockIdx.x * kWavesPerWG + wave; idx < total;
        idx += (long long)gridDim.x * kWavesPerWG) {
     const int item_i = (int)(idx / Hkv);
@@ -254,30 +259,31 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
       for (int e = 0; e < EPL; ++e) acc[i][e] = 0.f;
     float m_own = -INFINITY, l_own = 0.f;  // softmax state of head my_head
 
-    const int last_page = (it.hi - 1) / ps;
+    const int last_page = (it.hi - 1) >> sh;
     int pw0 = -(1 << 30);
     int page_reg = 0;
-    const CT* kv_head = cache + 2LL * g * p.Dpad + dl * EPL;
+    const char* kv_head =
+        reinterpret_cast<const char*>(cache + 2LL * g * p.Dpad + dl * EPL);
 
     uint32_t kA[NR][NW], vA[NR][NW], kB[NR][NW], vB[NR][NW];
 
+    // Loads of one step.  Tokens past the item are clamped to its last token
+    // (valid memory, masked out of the softmax), so every load is unconditional.
     auto load_step = [&](int k0, uint32_t (*kw)[NW], uint32_t (*vw)[NW]) {
       const int need_hi = min(k0 + STEP, it.hi) - 1;
-      if (need_hi / ps >= pw0 + 64 || k0 / ps < pw0) {
-        pw0 = k0 / ps;
+      if ((need_hi >> sh) >= pw0 + 64 || (k0 >> sh) < pw0) {
+        pw0 = k0 >> sh;
         const int pi = pw0 + lane;
         page_reg = (pi <= last_page) ? bt[pi] : 0;
       }
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        const int tok = k0 + r * TPR + slot;
-        const bool valid = tok < it.hi;
-        const int rel = valid ? (tok / ps - pw0) : 0;
-        const int page = __shfl(page_reg, rel);
-        const long long row = (long long)page * ps + (tok - (tok / ps) * ps);
-        const CT* kp = kv_head + row * row_stride;
-        load_chunk<CT, EPL>(kp, valid, kw[r]);
-        load_chunk<CT, EPL>(kp + p.Dpad, valid, vw[r]);
+        const int tok = min(k0 + r * TPR + slot, it.hi - 1);
+        const int page = __builtin_amdgcn_ds_bpermute(((tok >> sh) - pw0) << 2, page_reg);
+        const uint32_t row = ((uint32_t)page << sh) | (uint32_t)(tok & pmask);
+        const char* kp = kv_head + (uint64_t)row * row_bytes;
+        load_chunk<CT, EPL>(reinterpret_cast<const CT*>(kp), true, kw[r]);
+        load_chunk<CT, EPL>(reinterpret_cast<const CT*>(kp + head_bytes), true, vw[r]);
       }
     };
 
@@ -494,7 +500,17 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
   }
 }
 
-constexpr int kRowGrid = 2048;  // persistent grid of the row kernel (x4 waves)
+
+// Workgroups of `kernel` that fit on the device at once (occupancy x CUs).
+int resident_blocks(const void* kernel, int block_threads, size_t lds) {
+  int per_cu = 0, dev = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block_threads, lds) !=
+          hipSuccess ||
+      hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 1024;
+  return per_cu * cus > 0 ? per_cu * cus : 1024;
+}
 
 template <typename QT, typename CT, int D, int G>
 hipError_t launch_rows_t(const AttnParams& p, hipStream_t s) {
@@ -502,9 +518,11 @@ hipError_t launch_rows_t(const AttnParams& p, hipStream_t s) {
   constexpr int E16 = 16 / (int)sizeof(CT);
   constexpr int EPL = (E16 * G > 64) ? (64 / G) : E16;
   constexpr int NR = 4;
+  static const int cap = resident_blocks(
+      reinterpret_cast<const void*>(&row_kernel<QT, CT, D, G, EPL, NR>), 64 * kWavesPerWG, 0);
   const long long waves = (long long)p.lay.max_items * p.Hkv;
   const long long wgs = (waves + kWavesPerWG - 1) / kWavesPerWG;
-  dim3 grid((unsigned)(wgs < kRowGrid ? (wgs > 0 ? wgs : 1) : kRowGrid));
+  dim3 grid((unsigned)(wgs < cap ? (wgs > 0 ? wgs : 1) : cap));
   row_kernel<QT, CT, D, G, EPL, NR><<<grid, 64 * kWavesPerWG, 0, s>>>(p);
   return hipGetLastError();
 }

@@ -63,6 +63,9 @@ __global__ __launch_bounds__(kT) void plan_kernel(PlanParams p) {
 
   const int num_seqs = min(max(p.dist[0] + p.dist[1] + p.dist[2], 0), p.max_num_seqs);
   const int W = p.window;
+  // zero row the prefill kernel reads for keys outside a tile's visible range
+  for (int i = threadIdx.x; i < kZeroBytes / 4; i += kT)
+    reinterpret_cast<int32_t*>(ws + p.lay.zeros)[i] = 0;
 
   // ---- pass 1: per-sequence row counts, prefill tiles, visible-key totals ----
   int row_base = 0, pf_base = 0;
@@ -111,38 +114,62 @@ __global__ __launch_bounds__(kT) void plan_kernel(PlanParams p) {
   __syncthreads();
   const int n_rows = min(row_base, p.lay.max_rows);
 
-  // ---- split size ----
-  long long S = (vis_total + kTargetItems - 1) / kTargetItems;
+  // ---- split size: about kTargetWaves waves of work over all kv heads ----
+  const long long target_items = max(1, min(kTargetItems, kTargetWaves / max(p.Hkv, 1)));
+  long long S = (vis_total + target_items - 1) / target_items;
   S = (S + 15) / 16 * 16;
   if (S < kMinSplit) S = kMinSplit;
   const int split = (int)min(S, (long long)0x40000000);
 
-  // ---- pass 2: rows and their items ----
-  int item_base = 0, part_base = 0, merge_base = 0;
+  // row r -> (seq, token, visible range [lo, hi))
+  auto row_info = [&](int r, int& seq, int& token, int& lo, int& hi) {
+    int a = 0, b = num_seqs - 1;                    // largest s with s_seq_rows[s] <= r
+    while (a < b) {
+      const int mid = (a + b + 1) >> 1;
+      if (s_seq_rows[mid] <= r) a = mid; else b = mid - 1;
+    }
+    seq = a;
+    const int t = r - s_seq_rows[seq];
+    const int q0 = p.qsl[seq];
+    const int q_len = p.qsl[seq + 1] - q0;
+    const int pos = p.kv_lens[seq] - q_len + t;
+    token = q0 + t;
+    hi = pos + 1;
+    lo = (W > 0) ? max(0, pos - W + 1) : 0;
+  };
+
+  // ---- pass 2a: number of full-size splits (they are scheduled first) ----
+  int n_full_total = 0;
   for (int base = 0; base < n_rows; base += kT) {
     const int r = base + threadIdx.x;
-    int n_split = 0, seq = 0, lo = 0, hi = 0, token = 0;
+    int n_full = 0;
     if (r < n_rows) {
-      int a = 0, b = num_seqs - 1;                  // largest s with s_seq_rows[s] <= r
-      while (a < b) {
-        const int mid = (a + b + 1) >> 1;
-        if (s_seq_rows[mid] <= r) a = mid; else b = mid - 1;
-      }
-      seq = a;
-      const int t = r - s_seq_rows[seq];
-      const int q0 = p.qsl[seq];
-      const int q_len = p.qsl[seq + 1] - q0;
-      const int pos = p.kv_lens[seq] - q_len + t;
-      token = q0 + t;
-      hi = pos + 1;
-      lo = (W > 0) ? max(0, pos - W + 1) : 0;
+      int seq, token, lo, hi;
+      row_info(r, seq, token, lo, hi);
+      n_full = (hi - lo) / split;
+    }
+    int tot;
+    block_exclusive_scan(n_full, &tot, s_w32);
+    n_full_total += tot;
+  }
+
+  // ---- pass 2b: rows, their items (full splits first, then the remainders) ----
+  int full_base = 0, rem_base = n_full_total, part_base = 0, merge_base = 0;
+  for (int base = 0; base < n_rows; base += kT) {
+    const int r = base + threadIdx.x;
+    int n_split = 0, n_full = 0, seq = 0, lo = 0, hi = 0, token = 0;
+    if (r < n_rows) {
+      row_info(r, seq, token, lo, hi);
+      n_full = (hi - lo) / split;
       n_split = (hi - lo + split - 1) / split;
     }
-    int tot_items, tot_parts, tot_merge;
-    const int my_item = block_exclusive_scan(n_split, &tot_items, s_w32) + item_base;
+    const int has_rem = n_split - n_full;
+    int tot_full, tot_rem, tot_parts, tot_merge;
+    const int my_full = block_exclusive_scan(n_full, &tot_full, s_w32) + full_base;
+    const int my_rem = block_exclusive_scan(has_rem, &tot_rem, s_w32b) + rem_base;
     const int my_part =
-        block_exclusive_scan(n_split > 1 ? n_split : 0, &tot_parts, s_w32b) + part_base;
-    const int my_merge = block_exclusive_scan(n_split > 1 ? 1 : 0, &tot_merge, s_w32c) +
+        block_exclusive_scan(n_split > 1 ? n_split : 0, &tot_parts, s_w32c) + part_base;
+    const int my_merge = block_exclusive_scan(n_split > 1 ? 1 : 0, &tot_merge, s_w32) +
                          merge_base;
     if (r < n_rows) {
       RowDesc rd;
@@ -154,20 +181,24 @@ __global__ __launch_bounds__(kT) void plan_kernel(PlanParams p) {
       rd.part_base = n_split > 1 ? my_part : -1;
       rd.pad[0] = rd.pad[1] = 0;
       rows[r] = rd;
-      for (int j = 0; j < n_split && my_item + j < p.lay.max_items; ++j) {
+      for (int j = 0; j < n_split; ++j) {
+        const int slot = (j < n_full) ? my_full + j : my_rem;
+        if (slot >= p.lay.max_items) break;
         ItemDesc it;
         it.row = r;
         it.lo = lo + j * split;
         it.hi = min(hi, lo + (j + 1) * split);
         it.part = n_split > 1 ? my_part + j : -1;
-        items[my_item + j] = it;
+        items[slot] = it;
       }
       if (n_split > 1 && my_merge < p.lay.max_merge_rows) merge_rows[my_merge] = r;
     }
-    item_base += tot_items;
+    full_base += tot_full;
+    rem_base += tot_rem;
     part_base += tot_parts;
     merge_base += tot_merge;
   }
+  const int item_base = rem_base;
   if (threadIdx.x == 0) {
     PlanHeader h = {};
     h.num_seqs = num_seqs;
@@ -176,6 +207,8 @@ __global__ __launch_bounds__(kT) void plan_kernel(PlanParams p) {
     h.split = split;
     h.n_merge_rows = min(merge_base, p.lay.max_merge_rows);
     h.n_pf_items = min(pf_base, p.lay.max_pf_items);
+    h.row_next = 0;
+    h.pf_next = 0;
     *hdr = h;
   }
 }

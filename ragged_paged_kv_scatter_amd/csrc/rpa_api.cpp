@@ -147,7 +147,8 @@ Workspace workspace_layout(const rpa_desc& d) {
   size_t off = 0;
   w.header = off;
   off = align256(off + sizeof(PlanHeader));
-  w.seq_rows = off;
+  w.zeros = off;
+  off = align256(off + kZeroBytes);
   w.rows = off;
   off = align256(off + (size_t)w.max_rows * sizeof(RowDesc));
   w.items = off;
@@ -249,6 +250,7 @@ int rpa_forward(const rpa_desc* desc, const rpa_options* opts, const void* queri
   pp.T = desc->total_tokens;
   pp.window = opts->sliding_window;
   pp.prefill_min_q = prefill_min_q(*desc);
+  pp.Hkv = desc->num_kv_heads;
   prof_begin("plan", s);
   hipError_t e = launch_plan(pp, s);
   prof_end(s);
@@ -269,6 +271,7 @@ int rpa_forward(const rpa_desc* desc, const rpa_options* opts, const void* queri
   ap.D = desc->head_dim;
   ap.Dpad = desc->head_dim_padded;
   ap.page_size = desc->page_size;
+  ap.ps_shift = __builtin_ctz((unsigned)desc->page_size);
   ap.pps = desc->pages_per_seq;
   ap.window = opts->sliding_window;
   const float qs = opts->q_scale > 0.f ? opts->q_scale : 1.f;

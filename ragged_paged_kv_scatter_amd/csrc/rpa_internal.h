@@ -14,10 +14,12 @@ namespace rpa {
 // Tunables of the plan.
 // ---------------------------------------------------------------------------
 // Row-kernel work items aimed for: the KV range of a query row is cut into
-// splits of S tokens with S >= (sum of visible lengths) / kTargetItems, so
-// there are at most kTargetItems + rows items and at most 2 * kTargetItems
-// split partials (every split row has length > S).
-constexpr int kTargetItems = 2048;
+// splits of S tokens with S >= (sum of visible lengths) / (kTargetWaves / Hkv)
+// (each item is one wave per kv head), so there are at most
+// kTargetItems + rows items and at most 2 * kTargetItems split partials
+// (every split row has length > S).
+constexpr int kTargetWaves = 16384;
+constexpr int kTargetItems = 2048;    // upper bound of kTargetWaves / Hkv used for sizing
 constexpr int kMinSplit = 128;        // never cut a row's KV range finer than this
 constexpr int kPlanThreads = 1024;    // the planner is one workgroup
 constexpr int kWavesPerWG = 4;        // row kernel: one item per wave
@@ -33,7 +35,9 @@ struct PlanHeader {
   int32_t split;         // S, tokens per split
   int32_t n_merge_rows;  // rows with more than one split
   int32_t n_pf_items;    // (sequence, query tile) items of the prefill kernel
-  int32_t pad[10];
+  int32_t row_next;      // work counter of the row kernel (zeroed by the planner)
+  int32_t pf_next;       // work counter of the prefill kernel (zeroed by the planner)
+  int32_t pad[8];
 };
 
 struct RowDesc {         // one query row of the row (decode) kernel
@@ -57,8 +61,10 @@ struct PrefillItem {     // a query tile of one prefill sequence
   int32_t pad;
 };
 
+constexpr int kZeroBytes = 1024;      // zero-filled source row for masked key loads
+
 struct Workspace {       // byte offsets into the caller's workspace
-  size_t header, seq_rows, rows, items, merge_rows, pf_items, part_ml, part_acc, total;
+  size_t header, zeros, rows, items, merge_rows, pf_items, part_ml, part_acc, total;
   int32_t max_rows, max_items, max_parts, max_pf_items, max_merge_rows;
 };
 
@@ -89,7 +95,7 @@ struct PlanParams {
   const int32_t* dist;
   char* ws;
   Workspace lay;
-  int32_t max_num_seqs, T, window, prefill_min_q;
+  int32_t max_num_seqs, T, window, prefill_min_q, Hkv;
 };
 
 struct AttnParams {
@@ -103,6 +109,7 @@ struct AttnParams {
   char* ws;
   Workspace lay;
   int32_t Hq, Hkv, D, Dpad, page_size, pps, window;
+  int32_t ps_shift;    // log2(page_size)
   float qk_scale;      // softmax_scale * q_scale * k_scale
   float v_scale;       // 1 when none
   float cap;           // 0 when none

@@ -30,17 +30,25 @@ __device__ __forceinline__ int find_seq(const int32_t* qsl, int num_seqs, int to
 }
 
 // IN: element type of keys/values; C: element type of the cache.
+constexpr int kSeqsInLds = 1024;   // query_start_loc is searched in LDS up to this many seqs
+
 template <typename IN, typename C>
 __global__ __launch_bounds__(kThreads) void scatter_kernel(ScatterParams p) {
   __shared__ long long s_row[kTokensPerWG];  // destination cache row (element index), -1 = skip
+  __shared__ int32_t s_qsl[kSeqsInLds + 1];
   const int tok0 = blockIdx.x * kTokensPerWG;
   const int num_seqs = min(max(p.dist[0] + p.dist[1] + p.dist[2], 0), p.max_num_seqs);
-  const int n_valid = num_seqs > 0 ? p.qsl[num_seqs] : 0;
+  const bool qsl_in_lds = num_seqs <= kSeqsInLds;
+  if (qsl_in_lds) {
+    for (int i = threadIdx.x; i <= num_seqs; i += kThreads) s_qsl[i] = p.qsl[i];
+    __syncthreads();
+  }
+  const int n_valid = num_seqs > 0 ? (qsl_in_lds ? s_qsl[num_seqs] : p.qsl[num_seqs]) : 0;
   if (threadIdx.x < kTokensPerWG) {
     const int tok = tok0 + threadIdx.x;
     long long row = -1;
     if (tok < n_valid && tok < p.T) {
-      const int s = find_seq(p.qsl, num_seqs, tok);
+      const int s = qsl_in_lds ? find_seq(s_qsl, num_seqs, tok) : find_seq(p.qsl, num_seqs, tok);
       const int q0 = p.qsl[s];
       const int q_len = p.qsl[s + 1] - q0;
       const int pos = p.kv_lens[s] - q_len + (tok - q0);
