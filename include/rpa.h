@@ -27,8 +27,8 @@
  *                        in cache_dtype.  This is the same memory as the v3
  *                        shape [num_pages, page_size, 2*num_kv_heads/kv_packing,
  *                        kv_packing, head_dim_padded]: combined head 2h holds
- *                        K of kv head h and 2h+1 holds its V ("k and v are
- *                        packed together", v3 kernel diff).  Lanes
+ *                        K of kv head h and 2h+1 holds its V (the v3 kernel
+ *                        diff keeps a head's K and V in one packed row).  Lanes
  *                        [head_dim, head_dim_padded) are zero-filled on update.
  *     kv_lens            int32[max_num_seqs]   kv length INCLUDING the new tokens
  *     block_tables       int32[max_num_seqs * pages_per_seq]  page ids per sequence
