@@ -104,6 +104,63 @@ def cpu_baseline(w, budget_s=15.0):
     return dict(seconds=t_used, seqs=done, kv_bytes=kvb, flops=flops, threads=nthreads)
 
 
+KERNEL_SOURCES = {  # kernel -> sources whose hash identifies a counter summary
+    "decode": ["decode.hip", "device_common.h", "rpa_internal.h"],
+    "prefill": ["prefill.hip", "device_common.h", "rpa_internal.h"],
+}
+KERNEL_SYMBOL = {"decode": "row_kernel", "prefill": "prefill_kernel"}
+
+
+def source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "ragged_paged_kv_scatter_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
+def read_counter_csv(path):
+    """{dispatch_id: (kernel_name, {counter: summed value})} from a rocprofv3
+    counter_collection.csv (values summed over the counter's instances)."""
+    import csv
+    out = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            d = out.setdefault(r["Dispatch_Id"], (r["Kernel_Name"], {}))
+            d[1][r["Counter_Name"]] = d[1].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def summarize_counters(workload, kernel, fetch_csv, write_csv, copy_bytes):
+    """HBM traffic of one launch of `kernel` from a FETCH_SIZE run and a
+    WRITE_SIZE run (KiB per dispatch), each scaled by what the same counter
+    reads for the calibration copy of `copy_bytes` (read once, written once)."""
+    sym = KERNEL_SYMBOL[kernel]
+    res = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        disp = read_counter_csv(path)
+        copies = [c[name] for k, c in disp.values() if "copy" in k.lower() and name in c]
+        ours = [c[name] for k, c in disp.values() if sym in k and name in c]
+        if not copies or not ours:
+            raise SystemExit(f"no copy or {sym} dispatch with {name} in {path}")
+        copy_kib = max(copies)
+        factor = copy_bytes / (copy_kib * 1024.0)
+        res[name] = dict(kernel_kib=sum(ours) / len(ours), dispatches=len(ours),
+                         copy_kib=copy_kib, factor=factor,
+                         bytes=sum(ours) / len(ours) * 1024.0 * factor)
+    out = dict(workload=workload, kernel=kernel, source_hash=source_hash(kernel),
+               copy_bytes=copy_bytes, fetch=res["FETCH_SIZE"], write=res["WRITE_SIZE"],
+               traffic_bytes=res["FETCH_SIZE"]["bytes"] + res["WRITE_SIZE"]["bytes"])
+    with open(traffic_file(workload), "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,7 +169,15 @@ def main():
     ap.add_argument("--workload", default="decode_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one device copy of this size first (counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("KERNEL", "FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc runs")
     args = ap.parse_args()
+    if args.summarize_counters:
+        k, f, wcsv = args.summarize_counters
+        summarize_counters(args.workload, k, f, wcsv, args.calib_copy_mib * 2 ** 20)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path needs no "
               "collective and shards by kv head or by sequence with no exchange.", file=sys.stderr)
@@ -142,6 +207,13 @@ def main():
                         meta["block_tables"], meta["query_start_loc"], meta["distribution"],
                         w.attention_sink, out=out, workspace=workspace, **opts)
 
+    if args.calib_copy_mib:
+        src = torch.ones(args.calib_copy_mib * 2 ** 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -177,6 +249,14 @@ def main():
                     frac=achieved / HBM_PEAK_GBS, traffic=None)
     roof["kernel"] = dom_name
     roof["kernel_avg_ms"] = dom_avg_ms
+    # HBM traffic per launch from a committed counter summary, only while the
+    # kernel's sources are the ones the counters were taken on
+    tf = traffic_file(w.name)
+    if os.path.exists(tf) and dom_name in KERNEL_SOURCES:
+        with open(tf) as fh:
+            t = json.load(fh)
+        if t.get("kernel") == dom_name and t.get("source_hash") == source_hash(dom_name):
+            roof["traffic"] = t["traffic_bytes"]
 
     line = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
