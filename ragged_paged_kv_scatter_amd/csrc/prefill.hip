@@ -19,7 +19,7 @@
 //
 // LDS rows are unpadded (D bf16) with the 16-byte chunks of row r stored at
 // chunk ^ swz(r), which keeps both the K reads (16 rows, one chunk) and the
-// transposed V reads (4 rows, two chunks) free of bank conflicts.
+// transposed V reads (4 rows, four chunks per 32 lanes) free of bank conflicts.
 // bf16 caches are copied global -> LDS directly (global_load_lds, no staging
 // registers) into two stages, so the next block is in flight while the
 // current one is multiplied; keys outside the tile's range are read from a
@@ -50,10 +50,13 @@ template <typename CT> struct CacheElem;
 template <> struct CacheElem<uint16_t> { static constexpr int size = 2; };
 template <> struct CacheElem<uint8_t> { static constexpr int size = 1; };
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> two bf16 (RNE) in one word: one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  const uint32_t a = __builtin_bit_cast(uint16_t, (__bf16)lo);
-  const uint32_t b = __builtin_bit_cast(uint16_t, (__bf16)hi);
-  return a | (b << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // two e4m3 codes (bytes 0/1, or 2/3 with HI) -> two bf16 packed in one word (exact)
@@ -65,14 +68,23 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
 }
 
 // Physical 16-byte chunk of logical chunk c in LDS row r.
-// Any 8 consecutive rows get distinct low 3 bits (K reads, 8 lanes per LDS
-// cycle at 128 B); 4 rows x 2 chunks of a transposed V read land on 8 distinct
-// chunks; with 16 chunks per row the 4th bit separates rows r and r + 8.
+// Chunk swizzle of LDS row r (LDS serves 256 bytes per cycle: 16 lanes of a
+// ds_read_b128, 32 lanes of a ds_read_b64_tr_b16).
+//  D = 128 (16 chunks, one row per 256 B): f(r) is a bijection on r mod 16, so
+//    16 consecutive rows at one logical chunk hit 16 distinct chunks (K
+//    reads); bits 2-3 of f are r & 3, so 4 consecutive rows x chunks
+//    4dt..4dt+3 hit 16 distinct chunks (transposed V reads).
+//  D = 64 (8 chunks, two rows per 256 B): rows of equal parity in a 16-row
+//    window get distinct f; rows r, r + 2 differ in bit 2 of f.
+// Rows r and r + 8 always differ by f ^ 2.
+template <int D>
+__device__ __forceinline__ int swz_f(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
 template <int D>
 __device__ __forceinline__ int swz_chunk(int r, int c) {
-  const int f = ((r & 3) << 1) | ((r >> 2) & 1);
-  if constexpr (D == 128) return c ^ (f | (r & 8));
-  else return c ^ f;
+  return c ^ swz_f<D>(r);
 }
 
 __device__ __forceinline__ void wait_vmem_all() {
@@ -269,25 +281,60 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
     };
 
     // ---- the math on one block held in LDS ----
+    // Per-lane LDS byte offsets inside a stage (fixed for the kernel):
+    //  K read (half hf, k-step ks): row hf*32 + col, logical chunk 2ks + kg,
+    //    offset = (k_off ^ (ks << 5)) + hf * 32 * RB  (swz_f depends on row mod 16)
+    //  V^T reads (k-step ks, d tile dt): rows 16ks + rr and 16ks + rr + 8,
+    //    offsets = (v_off1 ^ (dt << 6)) + ks * 16 * RB and (v_off2 ^ (dt << 6)) + (16ks + 8) * RB
+    const int fk = swz_f<D>(col);
+    const uint32_t k_off = col * RB + ((((fk >> 1) << 1) | (kg ^ (fk & 1))) << 4);
+    const int grp = lane >> 4, r16 = lane & 15;
+    const int rr = (grp >> 1) * 4 + (r16 >> 2);
+    const int g1 = (2 * (grp & 1) + ((r16 & 3) >> 1)) ^ swz_f<D>(rr);
+    const uint32_t v_off1 = rr * RB + (g1 << 4) + (r16 & 1) * 8;
+    const uint32_t v_off2 = v_off1 ^ 32u;  // row rr + 8: chunk ^ 2
+
+    auto ld_k = [&](const char* kb, int ks, int hf) -> bf16x8 {
+      const char* a = kb + ((k_off ^ (uint32_t)(ks << 5)) + hf * 32 * RB);
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(a));
+    };
+    auto ld_vt = [&](const char* vb, int ks, int dt) -> bf16x8 {
+      const char* a1 = vb + ((v_off1 ^ (uint32_t)(dt << 6)) + ks * 16 * RB);
+      const char* a2 = vb + ((v_off2 ^ (uint32_t)(dt << 6)) + (ks * 16 + 8) * RB);
+      const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(a1));
+      const i16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(a2));
+      const i16x8 av = {x1[0], x1[1], x1[2], x1[3], x2[0], x2[1], x2[2], x2[3]};
+      return __builtin_bit_cast(bf16x8, av);
+    };
+
     auto compute = [&](int k0, const char* kb, const char* vb) {
       const bool needed = wave_live && k0 <= wpos_hi && (W <= 0 || k0 + BK - 1 > wpos_lo - W);
       if (!needed) return;
       const bool full = (k0 + BK - 1 <= wpos_lo) && (W <= 0 || wpos_hi - k0 < W);
-      // S^T = K Q^T: two 32-key halves
+      // S^T = K Q^T: two independent 32-key chains, K fragments read one k-step ahead
       f32x16 sacc[2];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
+      for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[hf][i] = 0.f;
-        const int row = hf * 32 + col;
-        const char* kr_ = kb + row * RB;
+      bf16x8 a0 = ld_k(kb, 0, 0), a1 = ld_k(kb, 0, 1);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const uint4*>(kr_ + (swz_chunk<D>(row, 2 * ks + kg) << 4)));
-          sacc[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc[hf], 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 n0 = a0, n1 = a1;
+        if (ks + 1 < KS) {
+          n0 = ld_k(kb, ks + 1, 0);
+          n1 = ld_k(kb, ks + 1, 1);
         }
+        // keep the next k-step's reads ahead of this k-step's MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], sacc[0], 0, 0, 0);
+        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], sacc[1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        a0 = n0;
+        a1 = n1;
       }
+      // first V^T fragment of p.v: independent of p, in flight during the softmax
+      bf16x8 va = ld_vt(vb, 0, 0);
       // logits (log2 units after c_eff), mask, block max
       float mx = -INFINITY;
 #pragma unroll
@@ -334,8 +381,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
           lsum += pv;
         }
       l_run += lsum;
-      // O^T += V^T P^T over four 16-key steps
-      const int grp = lane >> 4, r16 = lane & 15;
+      // O^T += V^T P^T over four 16-key steps, V^T fragments one step ahead
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int hf = ks >> 1, qq = ks & 1;
@@ -345,19 +391,15 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
         pw.z = pack_bf16(sacc[hf][8 * qq + 4], sacc[hf][8 * qq + 5]);
         pw.w = pack_bf16(sacc[hf][8 * qq + 6], sacc[hf][8 * qq + 7]);
         const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-        const int r1 = 16 * ks + (grp >> 1) * 4 + (r16 >> 2);  // the lane's first key row
-        const int r2 = r1 + 8;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const int x = dt * 32 + (grp & 1) * 16 + 4 * (r16 & 3);  // first of the 4 d read
-          const int inner = (x & 7) * 2;
-          const char* a1 = vb + r1 * RB + (swz_chunk<D>(r1, x >> 3) << 4) + inner;
-          const char* a2 = vb + r2 * RB + (swz_chunk<D>(r2, x >> 3) << 4) + inner;
-          const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(a1));
-          const i16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(a2));
-          const i16x8 av = {x1[0], x1[1], x1[2], x1[3], x2[0], x2[1], x2[2], x2[3]};
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb,
-                                                             oacc[dt], 0, 0, 0);
+          bf16x8 vn = va;
+          if (dt + 1 < DT) vn = ld_vt(vb, ks, dt + 1);
+          else if (ks + 1 < 4) vn = ld_vt(vb, ks + 1, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[dt], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          va = vn;
         }
       }
     };
