@@ -27,6 +27,8 @@
 // way.  k_scale is folded into the logit scale and v_scale into 1/l.
 #include <math.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "rpa_internal.h"
 
@@ -41,7 +43,6 @@ typedef i16x4 __attribute__((address_space(3))) * lds_i16x4_ptr;
 
 constexpr int BK = 64;          // keys per block
 constexpr int NT = 256;         // threads per workgroup
-constexpr int NS = 2;           // LDS stages (bf16 caches)
 constexpr int kPT = 512;        // page ids cached in LDS per refill
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr long long kPrefillGrid = 1024;  // fallback persistent grid (multiple of 8)
@@ -92,10 +93,11 @@ __device__ __forceinline__ void wait_vmem_all() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-// 16 bytes per lane global -> LDS at lds_base + 16 * lane (global_load_lds_dwordx4).
-// Issued from asm so that the compiler does not serialise the LDS reads of the
-// other stage behind these loads; the kernel orders them itself with
-// wait_vmem_all() + a barrier before the stage is read.
+// 16 bytes per lane global -> LDS at lds_base + 16 * lane (global_load_lds_dwordx4),
+// from a per-lane 64-bit address.  Issued from asm so that the compiler does
+// not serialise the LDS reads of the other buffers behind these loads; the
+// kernel orders them itself with wait_vmem_all() + a barrier before a buffer
+// is read.
 __device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                :
@@ -103,7 +105,42 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
                : "memory", "m0");
 }
 
-template <typename CT, int D>
+// The same from a wave-uniform base (SGPR pair) plus a per-lane 32-bit offset.
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// A wave-uniform pointer, forced into an SGPR pair.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(p));
+}
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100;
+
+// CAP: logits soft cap on (p.cap > 0), chosen at launch so that the
+// per-logit code has no branch on it.
+//
+// Block pipeline (per workgroup, blocks b = 64 keys): K is fetched one block
+// ahead of V, into two K buffers and two V buffers by block parity.  Step b
+//   - waits for K(b+1) and V(b), then starts K(b+2) and V(b+1);
+//   - exponentiates the logits of block b (computed in step b-1) while the
+//     MFMAs of S(b+1) = K(b+1) Q^T run;
+//   - multiplies P(b) V(b) while the row max of S(b+1) is formed.
+// So MFMA and VALU work of one wave overlap, and every buffer is rewritten
+// only after the barrier that follows its last reader.
+template <typename CT, int D, bool CAP>
 __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
   constexpr bool DIRECT = sizeof(CT) == 2;         // bf16 cache: global -> LDS directly
   constexpr int RB = D * 2;                        // LDS row bytes (bf16)
@@ -116,29 +153,67 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
   constexpr int ESZ = CacheElem<CT>::size;
   constexpr int GCPR = D * ESZ / 16;               // 16-byte chunks of a cached head row
   constexpr int PER = BK * GCPR / NT;              // staged chunks per thread (e4m3 path)
-  constexpr int NSTAGE = DIRECT ? NS : 1;
-  static_assert(!DIRECT || IPW >= 1, "direct split");
+  constexpr int EPK = 32 / KS;                     // logits exponentiated per q.k k-step
+  constexpr int EPM = 32 / (4 * DT);               // logits max-reduced per p.v MFMA
+  static_assert(!DIRECT || IPW * RPI == 16, "a wave loads 16 consecutive rows");
   static_assert(DIRECT || (PER >= 1 && BK * GCPR % NT == 0), "staged split");
-  // stage buffers are distinct objects so the compiler can tell that the
-  // loads streaming into one stage do not alias the reads of the other
-  __shared__ __attribute__((aligned(1024))) char smem[2 * BLKB];
-  __shared__ __attribute__((aligned(1024))) char smem1[DIRECT ? 2 * BLKB : 16];
+  __shared__ __attribute__((aligned(1024))) char s_k[2 * BLKB];
+  __shared__ __attribute__((aligned(1024))) char s_v[2 * BLKB];
   __shared__ int s_pt[kPT];
 
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(p.ws + p.lay.header);
   const PrefillItem* items = reinterpret_cast<const PrefillItem*>(p.ws + p.lay.pf_items);
-  const uint16_t* zero_row = reinterpret_cast<const uint16_t*>(p.ws + p.lay.zeros);
+  const char* zero_row = reinterpret_cast<const char*>(p.ws + p.lay.zeros);
   const int Hq = p.Hq, Hkv = p.Hkv, G = Hq / Hkv;
   const long long n_units = (long long)hdr->n_pf_items * Hq;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = lane >> 5, col = lane & 31;
-  const int sh = p.ps_shift;                       // page_size = 1 << sh
+  const int sh = p.ps_shift;                       // page_size = 1 << sh (>= 16)
   const int pmask = (1 << sh) - 1;
   const uint32_t row_bytes = 2u * Hkv * p.Dpad * (uint32_t)ESZ;  // one cache token row
-  const bool use_cap = p.cap > 0.f;
-  const float c_scale = use_cap ? p.qk_scale : p.qk_scale * kLog2e;
-  const float c_eff = use_cap ? 1.f : c_scale;   // stored logits -> log2 units
+  const uint32_t v_bytes = (uint32_t)p.Dpad * ESZ;               // K row -> V row
+  const float c_scale = CAP ? p.qk_scale : p.qk_scale * kLog2e;
+  const float c_eff = CAP ? 1.f : c_scale;       // stored logits -> log2 units
+  const float cap_k = CAP ? c_scale * 2.f * kLog2e / p.cap : 0.f;
+  const float cap_l2 = CAP ? p.cap * kLog2e : 0.f;
+
+  // Direct loads: instruction j of a wave writes LDS rows 16 wave + RPI j +
+  // lane / CPR, physical chunk lane % CPR, which holds logical chunk
+  // (lane % CPR) ^ swz(row); the rows' source offsets from the wave's first
+  // token row are fixed per lane.
+  uint32_t dma_off[DIRECT ? IPW : 1];
+#pragma unroll
+  for (int j = 0; j < (DIRECT ? IPW : 1); ++j) {
+    const int r = RPI * j + lane / CPR;
+    dma_off[j] = r * row_bytes + (swz_chunk<D>(r, lane % CPR) << 4);
+  }
+
+  // LDS byte offsets inside a K / V buffer (fixed per lane):
+  //  K read (half hf, k-step ks): row hf*32 + col, logical chunk 2ks + kg,
+  //    offset = (k_off ^ (ks << 5)) + hf * 32 * RB  (swz_f depends on row mod 16)
+  //  V^T reads (k-step ks, d tile dt): rows 16ks + rr and 16ks + rr + 8,
+  //    offsets = (v_off1 ^ (dt << 6)) + ks * 16 * RB and (v_off2 ^ (dt << 6)) + (16ks + 8) * RB
+  const int fk = swz_f<D>(col);
+  const uint32_t k_off = col * RB + ((((fk >> 1) << 1) | (kg ^ (fk & 1))) << 4);
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int rr = (grp >> 1) * 4 + (r16 >> 2);
+  const int g1 = (2 * (grp & 1) + ((r16 & 3) >> 1)) ^ swz_f<D>(rr);
+  const uint32_t v_off1 = rr * RB + (g1 << 4) + (r16 & 1) * 8;
+  const uint32_t v_off2 = v_off1 ^ 32u;  // row rr + 8: chunk ^ 2
+
+  auto ld_k = [&](const char* kb, int ks, int hf) -> bf16x8 {
+    const char* a = kb + ((k_off ^ (uint32_t)(ks << 5)) + hf * 32 * RB);
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(a));
+  };
+  auto ld_vt = [&](const char* vb, int ks, int dt) -> bf16x8 {
+    const char* a1 = vb + ((v_off1 ^ (uint32_t)(dt << 6)) + ks * 16 * RB);
+    const char* a2 = vb + ((v_off2 ^ (uint32_t)(dt << 6)) + (ks * 16 + 8) * RB);
+    const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(a1));
+    const i16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(a2));
+    const i16x8 av = {x1[0], x1[1], x1[2], x1[3], x2[0], x2[1], x2[2], x2[3]};
+    return __builtin_bit_cast(bf16x8, av);
+  };
 
   // Persistent grid (a multiple of 8 blocks): block b takes units b, b + grid,
   // ...  Consecutive units sit on different XCDs; the head slot -> (kv head =
@@ -157,36 +232,26 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
     const int kv_lo = W > 0 ? max(0, ctx + it.q_begin - W + 1) : 0;
     const int kv_hi = ctx + it.q_end;               // exclusive
     const int* bt = p.block_tables + (long long)seq * p.pps;
-    const CT* kv_head = static_cast<const CT*>(p.cache) + 2LL * g * p.Dpad;
+    const char* kv_head = static_cast<const char*>(p.cache) + 2LL * g * p.Dpad * ESZ;
 
     const int row_q = it.q_begin + wave * 32 + col;  // this lane's query row (within the seq)
     const bool row_ok = row_q < it.q_end;
     const int pos = ctx + row_q;
-    const int wave_q_lo = it.q_begin + wave * 32;
-    const bool wave_live = wave_q_lo < it.q_end;
-    const int wpos_lo = ctx + wave_q_lo;
-    const int wpos_hi = ctx + min(it.q_end, wave_q_lo + 32) - 1;
-
-    // Q^T operand: 8 bf16 of row row_q, d = 16 ks + 8 kg .. +7
-    bf16x8 qreg[KS];
-    {
-      const uint16_t* qp = static_cast<const uint16_t*>(p.q) +
-                           ((long long)(q0 + (row_ok ? row_q : it.q_begin)) * Hq + h) * D + 8 * kg;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qp + 16 * ks) : make_uint4(0, 0, 0, 0);
-        qreg[ks] = __builtin_bit_cast(bf16x8, v);
-      }
-    }
-    f32x16 oacc[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+    const bool wave_live = it.q_begin + wave * 32 < it.q_end;
 
     const int blk_first = kv_lo / BK;
     const int blk_end = (kv_hi + BK - 1) / BK;
+    // Blocks [f_lo, f_hi) are visible in full to every row of the tile
+    // (causal: last key <= first row's position; window: first key within W
+    // of the last row's position); every other block is masked per logit.
+    const int tpos_lo = ctx + it.q_begin, tpos_hi = kv_hi - 1;
+    int f_lo = blk_first;
+    if (W > 0 && tpos_hi - W >= 0) f_lo = max(f_lo, (tpos_hi - W) / BK + 1);
+    f_lo = min(f_lo, blk_end);
+    const int f_hi = min(max((tpos_lo + 1) / BK, f_lo), blk_end);
+    // step b needs the mask for block b + 1: unmasked steps are [A, B)
+    const int A = min(max(blk_first, f_lo - 1), blk_end);
+    const int B = max(A, f_hi - 1);
 
     // page ids of the unit's key range, kPT at a time, in LDS
     int pt_base = -(1 << 30);
@@ -205,162 +270,146 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
       }
     };
 
-    // ---- loads of one block ----
-    auto issue_direct = [&](int blk, char* stage) {  // bf16: global -> LDS, IPW x 2 per wave
-      const int k0 = blk * BK;
-      char* ks_ = stage;
-      char* vs_ = stage + BLKB;
+    // ---- loads of one K or V block (vofs = 0: K rows, v_bytes: V rows) ----
+    auto issue_direct = [&](int blk, char* buf, uint32_t vofs) __attribute__((always_inline)) {
+      const int t0 = blk * BK + 16 * wave;           // the wave's first token
+      const uint32_t lds0 = lds_addr(buf + wave * IPW * 1024);
+      if (t0 >= kv_lo && t0 + 16 <= kv_hi) {
+        // 16 tokens of one page (page_size >= 16): uniform base + lane offsets
+        const int page = __builtin_amdgcn_readfirstlane(s_pt[(t0 >> sh) - pt_base]);
+        const uint32_t crow = ((uint32_t)page << sh) | (uint32_t)(t0 & pmask);
+        const char* base = uniform_ptr(kv_head + vofs + (uint64_t)crow * row_bytes);
 #pragma unroll
-      for (int j = 0; j < IPW; ++j) {
-        const int inst = wave * IPW + j;
-        const int row = inst * RPI + lane / CPR;
-        const int c = swz_chunk<D>(row, lane % CPR);
-        const int tok = k0 + row;
-        const uint16_t* ksrc = zero_row + c * 8;
-        const uint16_t* vsrc = ksrc;
-        if (tok >= kv_lo && tok < kv_hi) {
-          const int page = s_pt[(tok >> sh) - pt_base];
-          const uint32_t crow = ((uint32_t)page << sh) | (uint32_t)(tok & pmask);
-          ksrc = reinterpret_cast<const uint16_t*>(
-              reinterpret_cast<const char*>(kv_head) + (uint64_t)crow * row_bytes + c * 16);
-          vsrc = ksrc + p.Dpad;
+        for (int j = 0; j < IPW; ++j) dma16_s(base, dma_off[j], lds0 + j * 1024);
+      } else {
+        // range edge: rows outside [kv_lo, kv_hi) come from the zero row
+#pragma unroll
+        for (int j = 0; j < IPW; ++j) {
+          const int r = RPI * j + lane / CPR;
+          const int tok = t0 + r;
+          const char* src = zero_row + (swz_chunk<D>(r, lane % CPR) << 4);
+          if (tok >= kv_lo && tok < kv_hi) {
+            const int page = s_pt[(tok >> sh) - pt_base];
+            const uint32_t crow = ((uint32_t)page << sh) | (uint32_t)(tok & pmask);
+            src = kv_head + vofs + (uint64_t)crow * row_bytes + (swz_chunk<D>(r, lane % CPR) << 4);
+          }
+          dma16(src, lds0 + j * 1024);
         }
-        const uint32_t kdst = __builtin_amdgcn_readfirstlane(
-            (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(ks_ + inst * 1024));
-        const uint32_t vdst = __builtin_amdgcn_readfirstlane(
-            (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(vs_ + inst * 1024));
-        dma16(ksrc, kdst);
-        dma16(vsrc, vdst);
       }
     };
     uint4 kr[DIRECT ? 1 : PER], vr[DIRECT ? 1 : PER];
-    auto fetch_staged = [&](int blk) {       // e4m3: global -> registers
+    auto fetch_staged = [&](int blk, uint4* regs, uint32_t vofs) {   // e4m3: global -> registers
 #pragma unroll
       for (int i = 0; i < (DIRECT ? 0 : PER); ++i) {
         const int cidx = tid + NT * i;
         const int tok = blk * BK + cidx / GCPR, cc = cidx % GCPR;
-        uint4 a = make_uint4(0, 0, 0, 0), v = a;
+        uint4 a = make_uint4(0, 0, 0, 0);
         if (tok >= kv_lo && tok < kv_hi) {
           const int page = s_pt[(tok >> sh) - pt_base];
           const uint32_t crow = ((uint32_t)page << sh) | (uint32_t)(tok & pmask);
-          const CT* src = reinterpret_cast<const CT*>(
-              reinterpret_cast<const char*>(kv_head) + (uint64_t)crow * row_bytes + cc * 16);
-          a = *reinterpret_cast<const uint4*>(src);
-          v = *reinterpret_cast<const uint4*>(src + p.Dpad);
+          a = *reinterpret_cast<const uint4*>(kv_head + vofs + (uint64_t)crow * row_bytes + cc * 16);
         }
-        kr[i] = a;
-        vr[i] = v;
+        regs[i] = a;
       }
     };
-    auto stage_staged = [&]() {              // e4m3 -> bf16 into the swizzled rows
+    auto stage_staged = [&](const uint4* regs, char* buf) {  // e4m3 -> bf16 into swizzled rows
 #pragma unroll
       for (int i = 0; i < (DIRECT ? 0 : PER); ++i) {
         const int cidx = tid + NT * i;
         const int row = cidx / GCPR, cc = cidx % GCPR;
-        const uint32_t kw[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
-        const uint32_t vw[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
-        uint32_t ko[8], vo[8];
+        const uint32_t w[4] = {regs[i].x, regs[i].y, regs[i].z, regs[i].w};
+        uint32_t o[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          ko[2 * e] = fp8x2_to_bf16x2<false>(kw[e]);
-          ko[2 * e + 1] = fp8x2_to_bf16x2<true>(kw[e]);
-          vo[2 * e] = fp8x2_to_bf16x2<false>(vw[e]);
-          vo[2 * e + 1] = fp8x2_to_bf16x2<true>(vw[e]);
+          o[2 * e] = fp8x2_to_bf16x2<false>(w[e]);
+          o[2 * e + 1] = fp8x2_to_bf16x2<true>(w[e]);
         }
-        char* kb = smem + row * RB;
-        char* vb = smem + BLKB + row * RB;
-        *reinterpret_cast<uint4*>(kb + (swz_chunk<D>(row, 2 * cc) << 4)) =
-            make_uint4(ko[0], ko[1], ko[2], ko[3]);
-        *reinterpret_cast<uint4*>(kb + (swz_chunk<D>(row, 2 * cc + 1) << 4)) =
-            make_uint4(ko[4], ko[5], ko[6], ko[7]);
-        *reinterpret_cast<uint4*>(vb + (swz_chunk<D>(row, 2 * cc) << 4)) =
-            make_uint4(vo[0], vo[1], vo[2], vo[3]);
-        *reinterpret_cast<uint4*>(vb + (swz_chunk<D>(row, 2 * cc + 1) << 4)) =
-            make_uint4(vo[4], vo[5], vo[6], vo[7]);
+        char* rb = buf + row * RB;
+        *reinterpret_cast<uint4*>(rb + (swz_chunk<D>(row, 2 * cc) << 4)) =
+            make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4*>(rb + (swz_chunk<D>(row, 2 * cc + 1) << 4)) =
+            make_uint4(o[4], o[5], o[6], o[7]);
+      }
+    };
+    auto kbuf = [&](int blk) -> char* { return s_k + (blk & 1) * BLKB; };
+    auto vbuf = [&](int blk) -> char* { return s_v + (blk & 1) * BLKB; };
+    auto load_k = [&](int blk) {
+      if constexpr (DIRECT) issue_direct(blk, kbuf(blk), 0);
+      else fetch_staged(blk, kr, 0);
+    };
+    auto load_v = [&](int blk) {
+      if constexpr (DIRECT) issue_direct(blk, vbuf(blk), v_bytes);
+      else fetch_staged(blk, vr, v_bytes);
+    };
+    // step b, first part: K(b+1), V(b) are in LDS; start K(b+2), V(b+1)
+    auto begin_step = [&](int blk) __attribute__((always_inline)) {
+      if constexpr (DIRECT) wait_vmem_all();      // this wave's loads have landed
+      __syncthreads();                            // everyone's; last readers are done
+      if (blk + 1 < blk_end) load_v(blk + 1);     // its pages are in the table already
+      if (blk + 2 < blk_end) {
+        ensure_pages(blk + 2);
+        load_k(blk + 2);
+      }
+    };
+    // step b, last part (e4m3): widen the fetched rows into their buffers
+    auto end_step = [&](int blk) __attribute__((always_inline)) {
+      if constexpr (!DIRECT) {
+        if (blk + 1 < blk_end) stage_staged(vr, vbuf(blk + 1));
+        if (blk + 2 < blk_end) stage_staged(kr, kbuf(blk + 2));
       }
     };
 
-    // ---- the math on one block held in LDS ----
-    // Per-lane LDS byte offsets inside a stage (fixed for the kernel):
-    //  K read (half hf, k-step ks): row hf*32 + col, logical chunk 2ks + kg,
-    //    offset = (k_off ^ (ks << 5)) + hf * 32 * RB  (swz_f depends on row mod 16)
-    //  V^T reads (k-step ks, d tile dt): rows 16ks + rr and 16ks + rr + 8,
-    //    offsets = (v_off1 ^ (dt << 6)) + ks * 16 * RB and (v_off2 ^ (dt << 6)) + (16ks + 8) * RB
-    const int fk = swz_f<D>(col);
-    const uint32_t k_off = col * RB + ((((fk >> 1) << 1) | (kg ^ (fk & 1))) << 4);
-    const int grp = lane >> 4, r16 = lane & 15;
-    const int rr = (grp >> 1) * 4 + (r16 >> 2);
-    const int g1 = (2 * (grp & 1) + ((r16 & 3) >> 1)) ^ swz_f<D>(rr);
-    const uint32_t v_off1 = rr * RB + (g1 << 4) + (r16 & 1) * 8;
-    const uint32_t v_off2 = v_off1 ^ 32u;  // row rr + 8: chunk ^ 2
-
-    auto ld_k = [&](const char* kb, int ks, int hf) -> bf16x8 {
-      const char* a = kb + ((k_off ^ (uint32_t)(ks << 5)) + hf * 32 * RB);
-      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(a));
-    };
-    auto ld_vt = [&](const char* vb, int ks, int dt) -> bf16x8 {
-      const char* a1 = vb + ((v_off1 ^ (uint32_t)(dt << 6)) + ks * 16 * RB);
-      const char* a2 = vb + ((v_off2 ^ (uint32_t)(dt << 6)) + (ks * 16 + 8) * RB);
-      const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(a1));
-      const i16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(a2));
-      const i16x8 av = {x1[0], x1[1], x1[2], x1[3], x2[0], x2[1], x2[2], x2[3]};
-      return __builtin_bit_cast(bf16x8, av);
-    };
-
-    auto compute = [&](int k0, const char* kb, const char* vb) {
-      const bool needed = wave_live && k0 <= wpos_hi && (W <= 0 || k0 + BK - 1 > wpos_lo - W);
-      if (!needed) return;
-      const bool full = (k0 + BK - 1 <= wpos_lo) && (W <= 0 || wpos_hi - k0 < W);
-      // S^T = K Q^T: two independent 32-key chains, K fragments read one k-step ahead
-      f32x16 sacc[2];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[hf][i] = 0.f;
-      bf16x8 a0 = ld_k(kb, 0, 0), a1 = ld_k(kb, 0, 1);
+    // ---- per-lane state: Q^T operand, O^T accumulators, softmax state ----
+    bf16x8 qreg[KS];   // 8 bf16 of row row_q, d = 16 ks + 8 kg .. +7
+    {
+      const uint16_t* qp = static_cast<const uint16_t*>(p.q) +
+                           ((long long)(q0 + (row_ok ? row_q : it.q_begin)) * Hq + h) * D + 8 * kg;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 n0 = a0, n1 = a1;
-        if (ks + 1 < KS) {
-          n0 = ld_k(kb, ks + 1, 0);
-          n1 = ld_k(kb, ks + 1, 1);
-        }
-        // keep the next k-step's reads ahead of this k-step's MFMAs
-        __builtin_amdgcn_sched_barrier(0);
-        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], sacc[0], 0, 0, 0);
-        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], sacc[1], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        a0 = n0;
-        a1 = n1;
+        uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qp + 16 * ks) : make_uint4(0, 0, 0, 0);
+        qreg[ks] = __builtin_bit_cast(bf16x8, v);
       }
-      // first V^T fragment of p.v: independent of p, in flight during the softmax
-      bf16x8 va = ld_vt(vb, 0, 0);
-      // logits (log2 units after c_eff), mask, block max
-      float mx = -INFINITY;
+    }
+    f32x16 oacc[DT];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float s = sacc[hf][i];
-          if (use_cap) {
-            // cap * tanh(s * scale / cap) in log2 units, tanh(x) = 1 - 2 / (e^{2x} + 1)
-            const float e2 = __builtin_amdgcn_exp2f(s * (c_scale * 2.f * kLog2e / p.cap));
-            s = p.cap * kLog2e * (1.f - 2.f * __builtin_amdgcn_rcpf(e2 + 1.f));
-          }
-          if (!full) {
-            const int j = k0 + hf * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
-            const bool vis = j <= pos && (W <= 0 || pos - j < W);
-            s = vis ? s : -INFINITY;
-          }
-          sacc[hf][i] = s;
-          mx = fmaxf(mx, s);
-        }
+      for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    // S^T of a block (lane: 16 keys x its row), alternating between sa and sb
+    // so that the steps of a pair name their buffers statically
+    f32x16 sa[2], sb[2];
+    float mx = -INFINITY;    // row max of the current block, log2 units
+
+    // logit e (0..31) of the block starting at key k0: key
+    // k0 + 32 (e >> 4) + 8 ((e & 15) >> 2) + 4 kg + (e & 3)
+    auto logit = [&](auto masked, int k0, float s, int e) __attribute__((always_inline)) -> float {
+      if constexpr (CAP) {
+        // cap * tanh(s * scale / cap) in log2 units, tanh(x) = 1 - 2 / (e^{2x} + 1)
+        const float e2 = __builtin_amdgcn_exp2f(s * cap_k);
+        s = cap_l2 * (1.f - 2.f * __builtin_amdgcn_rcpf(e2 + 1.f));
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c_eff;
-      // Lazy rescaling: the running max only moves (and acc / l are only
-      // rescaled) when some row of the wave grows by more than 2^8; until then
-      // p <= 2^8, harmless in fp32 sums and in bf16.
-      if (__any(mx > m_run + 8.f)) {
+      if constexpr (decltype(masked)::value) {
+        // key j = k0 + 4 kg + ko with ko a constant: visible iff
+        // j <= pos and (no window or j > pos - W)
+        const int ko = (e >> 4) * 32 + ((e & 15) >> 2) * 8 + (e & 3);
+        const int lim = pos - k0 - 4 * kg;
+        const bool vis = ko <= lim && (W <= 0 || ko > lim - W);
+        s = vis ? s : -INFINITY;
+      }
+      return s;
+    };
+
+    // One pipeline step on block blk (see above): sacc holds S(blk), s2
+    // receives S(blk + 1).  MASK_NEXT: block blk + 1 needs per-logit masking.
+    // The running max moves to this block's max every step; the rescale of
+    // the accumulators runs under the MFMAs, and keeping it unconditional
+    // keeps the loop free of joins (which would cost accumulator copies).
+    auto step = [&](auto mask_next, int blk, f32x16(&sacc)[2], f32x16(&s2)[2])
+                    __attribute__((always_inline)) {
+      constexpr bool MASK_NEXT = decltype(mask_next)::value;
+      begin_step(blk);
+      {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
@@ -371,78 +420,147 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
           for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
       }
       const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      float lsum = 0.f;
+      const char* kn = kbuf(blk + 1);
+      const char* vb = vbuf(blk);
+      __builtin_amdgcn_sched_barrier(0);
+
+      // (1) P(b) = 2^(S(b) - m) packed to bf16, under the MFMAs of S(b+1)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[hf][i], c_eff, -m_use));
-          sacc[hf][i] = pv;
-          lsum += pv;
+        for (int i = 0; i < 16; ++i) s2[hf][i] = 0.f;
+      uint32_t pk[16];
+      float ls0 = 0.f, ls1 = 0.f;
+      bf16x8 a0 = ld_k(kn, 0, 0), a1 = ld_k(kn, 0, 1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 n0 = a0, n1 = a1;
+        if (ks + 1 < KS) {
+          n0 = ld_k(kn, ks + 1, 0);
+          n1 = ld_k(kn, ks + 1, 1);
         }
-      l_run += lsum;
-      // O^T += V^T P^T over four 16-key steps, V^T fragments one step ahead
+        s2[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], s2[0], 0, 0, 0);
+        s2[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s2[1], 0, 0, 0);
+#pragma unroll
+        for (int e = ks * EPK; e < (ks + 1) * EPK; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 4][e & 15], c_eff, -m_use));
+          const float p1 =
+              __builtin_amdgcn_exp2f(fmaf(sacc[(e + 1) >> 4][(e + 1) & 15], c_eff, -m_use));
+          ls0 += p0;
+          ls1 += p1;
+          pk[e >> 1] = pack_bf16(p0, p1);
+        }
+        a0 = n0;
+        a1 = n1;
+      }
+      l_run += ls0 + ls1;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgValu, 7 * EPK / 4, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgValu, 7 * EPK / 4, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
+      // (2) O^T += V^T(b) P^T(b), under the mask / cap / max of S(b+1)
+      const int k0n = (blk + 1) * BK;
+      float m0 = -INFINITY, m1 = -INFINITY;
+      bf16x8 va = ld_vt(vb, 0, 0);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int hf = ks >> 1, qq = ks & 1;
-        uint4 pw;
-        pw.x = pack_bf16(sacc[hf][8 * qq + 0], sacc[hf][8 * qq + 1]);
-        pw.y = pack_bf16(sacc[hf][8 * qq + 2], sacc[hf][8 * qq + 3]);
-        pw.z = pack_bf16(sacc[hf][8 * qq + 4], sacc[hf][8 * qq + 5]);
-        pw.w = pack_bf16(sacc[hf][8 * qq + 6], sacc[hf][8 * qq + 7]);
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+        const bf16x8 pb = __builtin_bit_cast(
+            bf16x8, make_uint4(pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]));
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           bf16x8 vn = va;
           if (dt + 1 < DT) vn = ld_vt(vb, ks, dt + 1);
           else if (ks + 1 < 4) vn = ld_vt(vb, ks + 1, 0);
-          __builtin_amdgcn_sched_barrier(0);
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[dt], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int q = 0; q < EPM; ++q) {
+            const int e = (ks * DT + dt) * EPM + q;
+            const float s = logit(mask_next, k0n, s2[e >> 4][e & 15], e);
+            s2[e >> 4][e & 15] = s;
+            if (q & 1) m1 = fmaxf(m1, s);
+            else m0 = fmaxf(m0, s);
+          }
           va = vn;
         }
       }
+#pragma unroll
+      for (int m = 0; m < 4 * DT; ++m) {
+        if (m + 1 < 4 * DT) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(
+            kSgValu, EPM * (1 + (MASK_NEXT ? 4 : 0) + (CAP ? 6 : 0)), 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mx = fmaxf(m0, m1);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c_eff;
+      end_step(blk);
+    };
+    // steps [blk, end) in pairs; on return S(blk) is in sa again
+    auto run = [&](auto mask_next, int& blk, int end) __attribute__((always_inline)) {
+      for (; blk + 1 < end; blk += 2) {
+        step(mask_next, blk, sa, sb);
+        step(mask_next, blk + 1, sb, sa);
+      }
+      if (blk < end) {
+        step(mask_next, blk, sa, sb);
+        sa[0] = sb[0];
+        sa[1] = sb[1];
+        ++blk;
+      }
     };
 
-    if constexpr (DIRECT) {
-      // two LDS stages: block blk + 1 streams in while block blk is multiplied
-      // (unrolled by two so each half names its stage buffer statically)
-      if (blk_first < blk_end) {
-        ensure_pages(blk_first);
-        issue_direct(blk_first, smem);
+    // ---- prologue: K(b0) in, then K(b0+1) and V(b0) in flight, S(b0) ----
+    const int b0 = blk_first;
+    ensure_pages(b0);
+    load_k(b0);
+    if constexpr (!DIRECT) stage_staged(kr, kbuf(b0));
+    if constexpr (DIRECT) wait_vmem_all();
+    __syncthreads();
+    load_v(b0);
+    if (b0 + 1 < blk_end) {
+      ensure_pages(b0 + 1);
+      load_k(b0 + 1);
+    }
+    if (wave_live) {
+      const char* kb = kbuf(b0);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sa[hf][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sa[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_k(kb, ks, 0), qreg[ks], sa[0], 0, 0, 0);
+        sa[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_k(kb, ks, 1), qreg[ks], sa[1], 0, 0, 0);
       }
-      for (int blk = blk_first; blk < blk_end; blk += 2) {
-        wait_vmem_all();                    // this wave's part of block blk has landed
-        __syncthreads();                    // all parts landed; block blk - 1 fully consumed
-        if (blk + 1 < blk_end) {
-          ensure_pages(blk + 1);
-          issue_direct(blk + 1, smem1);
-        }
-        compute(blk * BK, smem, smem + BLKB);
-        if (blk + 1 < blk_end) {
-          wait_vmem_all();
-          __syncthreads();
-          if (blk + 2 < blk_end) {
-            ensure_pages(blk + 2);
-            issue_direct(blk + 2, smem);
-          }
-          compute((blk + 1) * BK, smem1, smem1 + BLKB);
-        }
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const float s = logit(std::true_type{}, b0 * BK, sa[e >> 4][e & 15], e);
+        sa[e >> 4][e & 15] = s;
+        mx = fmaxf(mx, s);
       }
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c_eff;
+    }
+    if constexpr (!DIRECT) {
+      stage_staged(vr, vbuf(b0));
+      if (b0 + 1 < blk_end) stage_staged(kr, kbuf(b0 + 1));
+    }
+
+    // ---- the steps: masked [b0, A), unmasked [A, B), masked [B, end) ----
+    if (wave_live) {
+      int blk = b0;
+      run(std::true_type{}, blk, A);
+      run(std::false_type{}, blk, B);
+      run(std::true_type{}, blk, blk_end);
     } else {
-      if (blk_first < blk_end) {
-        ensure_pages(blk_first);
-        fetch_staged(blk_first);
-      }
-      for (int blk = blk_first; blk < blk_end; ++blk) {
-        __syncthreads();                    // previous block fully consumed
-        stage_staged();
-        __syncthreads();                    // block visible to all waves
-        if (blk + 1 < blk_end) {
-          ensure_pages(blk + 1);
-          fetch_staged(blk + 1);
-        }
-        compute(blk * BK, smem, smem + BLKB);
+      for (int blk = b0; blk < blk_end; ++blk) {  // same barriers and loads, no math
+        begin_step(blk);
+        end_step(blk);
       }
     }
 
@@ -452,9 +570,9 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
       float f = 1.f;
       if (p.sink) {
         const float sg = p.sink[h] * kLog2e;
-        const float mx = fmaxf(m_run, sg);
-        f = __builtin_amdgcn_exp2f(m_run - mx);
-        l_tot = l_tot * f + __builtin_amdgcn_exp2f(sg - mx);
+        const float mxs = fmaxf(m_run, sg);
+        f = __builtin_amdgcn_exp2f(m_run - mxs);
+        l_tot = l_tot * f + __builtin_amdgcn_exp2f(sg - mxs);
       }
       const float sc = f * p.v_scale / l_tot;
       if (row_ok) {
@@ -487,21 +605,24 @@ long long resident_grid(const void* kernel) {
   return (long long)(per_cu * cus) / 8 * 8;
 }
 
-template <typename CT>
-hipError_t launch_t(const AttnParams& p, hipStream_t s) {
-  long long blocks = (long long)p.lay.max_pf_items * p.Hq;
-  if (blocks <= 0) return hipSuccess;
+template <typename CT, int D, bool CAP>
+hipError_t launch_d(const AttnParams& p, long long blocks, hipStream_t s) {
   // persistent grid: the resident workgroups, rounded down to a multiple of 8
   // so that block b and its later units b + grid sit on the same XCD
-  static const long long cap64 =
-      resident_grid(reinterpret_cast<const void*>(&prefill_kernel<CT, 64>));
-  static const long long cap128 =
-      resident_grid(reinterpret_cast<const void*>(&prefill_kernel<CT, 128>));
-  const long long cap = p.D == 64 ? cap64 : cap128;
-  if (blocks > cap) blocks = cap;
-  if (p.D == 64) prefill_kernel<CT, 64><<<dim3((unsigned)blocks), NT, 0, s>>>(p);
-  else prefill_kernel<CT, 128><<<dim3((unsigned)blocks), NT, 0, s>>>(p);
+  static const long long resident =
+      resident_grid(reinterpret_cast<const void*>(&prefill_kernel<CT, D, CAP>));
+  if (blocks > resident) blocks = resident;
+  prefill_kernel<CT, D, CAP><<<dim3((unsigned)blocks), NT, 0, s>>>(p);
   return hipGetLastError();
+}
+
+template <typename CT>
+hipError_t launch_t(const AttnParams& p, hipStream_t s) {
+  const long long blocks = (long long)p.lay.max_pf_items * p.Hq;
+  if (blocks <= 0) return hipSuccess;
+  const bool cap = p.cap > 0.f;
+  if (p.D == 64) return cap ? launch_d<CT, 64, true>(p, blocks, s) : launch_d<CT, 64, false>(p, blocks, s);
+  return cap ? launch_d<CT, 128, true>(p, blocks, s) : launch_d<CT, 128, false>(p, blocks, s);
 }
 
 }  // namespace
