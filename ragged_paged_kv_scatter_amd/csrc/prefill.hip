@@ -126,9 +126,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(p));
 }
 
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100;
-
 // CAP: logits soft cap on (p.cap > 0), chosen at launch so that the
 // per-logit code has no branch on it.
 //
@@ -402,14 +399,14 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
 
     // One pipeline step on block blk (see above): sacc holds S(blk), s2
     // receives S(blk + 1).  MASK_NEXT: block blk + 1 needs per-logit masking.
-    // The running max moves to this block's max every step; the rescale of
-    // the accumulators runs under the MFMAs, and keeping it unconditional
-    // keeps the loop free of joins (which would cost accumulator copies).
     auto step = [&](auto mask_next, int blk, f32x16(&sacc)[2], f32x16(&s2)[2])
                     __attribute__((always_inline)) {
       constexpr bool MASK_NEXT = decltype(mask_next)::value;
       begin_step(blk);
-      {
+      // Lazy rescaling: the running max only moves (and acc / l are only
+      // rescaled) when some row of the wave grows by more than 2^8; until
+      // then p <= 2^8, harmless in fp32 sums and in bf16.
+      if (__any(mx > m_run + 8.f)) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
@@ -431,6 +428,21 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
         for (int i = 0; i < 16; ++i) s2[hf][i] = 0.f;
       uint32_t pk[16];
       float ls0 = 0.f, ls1 = 0.f;
+      // exponentiate logits [e0, e0 + n) of sacc, packing pairs into pk
+      auto exps = [&](int e0, int n) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = e0; e < e0 + n; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 4][e & 15], c_eff, -m_use));
+          const float p1 =
+              __builtin_amdgcn_exp2f(fmaf(sacc[(e + 1) >> 4][(e + 1) & 15], c_eff, -m_use));
+          ls0 += p0;
+          ls1 += p1;
+          pk[e >> 1] = pack_bf16(p0, p1);
+        }
+      };
+      // Source order is kept by fences: each chunk is one MFMA and its share
+      // of VALU work, and the LDS reads of the next k-step are issued a chunk
+      // ahead of their MFMAs.
       bf16x8 a0 = ld_k(kn, 0, 0), a1 = ld_k(kn, 0, 1);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -439,30 +451,17 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
           n0 = ld_k(kn, ks + 1, 0);
           n1 = ld_k(kn, ks + 1, 1);
         }
+        __builtin_amdgcn_sched_barrier(0);
         s2[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], s2[0], 0, 0, 0);
+        exps(ks * EPK, EPK / 2);
+        __builtin_amdgcn_sched_barrier(0);
         s2[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s2[1], 0, 0, 0);
-#pragma unroll
-        for (int e = ks * EPK; e < (ks + 1) * EPK; e += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 4][e & 15], c_eff, -m_use));
-          const float p1 =
-              __builtin_amdgcn_exp2f(fmaf(sacc[(e + 1) >> 4][(e + 1) & 15], c_eff, -m_use));
-          ls0 += p0;
-          ls1 += p1;
-          pk[e >> 1] = pack_bf16(p0, p1);
-        }
+        exps(ks * EPK + EPK / 2, EPK / 2);
+        __builtin_amdgcn_sched_barrier(0);
         a0 = n0;
         a1 = n1;
       }
       l_run += ls0 + ls1;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 1 < KS) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgValu, 7 * EPK / 4, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgValu, 7 * EPK / 4, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
 
       // (2) O^T += V^T(b) P^T(b), under the mask / cap / max of S(b+1)
       const int k0n = (blk + 1) * BK;
@@ -477,6 +476,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
           bf16x8 vn = va;
           if (dt + 1 < DT) vn = ld_vt(vb, ks, dt + 1);
           else if (ks + 1 < 4) vn = ld_vt(vb, ks + 1, 0);
+          __builtin_amdgcn_sched_barrier(0);
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[dt], 0, 0, 0);
 #pragma unroll
           for (int q = 0; q < EPM; ++q) {
@@ -486,17 +486,10 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
             if (q & 1) m1 = fmaxf(m1, s);
             else m0 = fmaxf(m0, s);
           }
+          __builtin_amdgcn_sched_barrier(0);
           va = vn;
         }
       }
-#pragma unroll
-      for (int m = 0; m < 4 * DT; ++m) {
-        if (m + 1 < 4 * DT) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(
-            kSgValu, EPM * (1 + (MASK_NEXT ? 4 : 0) + (CAP ? 6 : 0)), 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
       mx = fmaxf(m0, m1);
       mx = fmaxf(mx, __shfl_xor(mx, 32)) * c_eff;
       end_step(blk);
