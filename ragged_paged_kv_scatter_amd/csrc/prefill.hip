@@ -53,6 +53,7 @@ template <> struct CacheElem<uint8_t> { static constexpr int size = 1; };
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 // two floats -> two bf16 (RNE) in one word: one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
@@ -150,8 +151,6 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
   constexpr int ESZ = CacheElem<CT>::size;
   constexpr int GCPR = D * ESZ / 16;               // 16-byte chunks of a cached head row
   constexpr int PER = BK * GCPR / NT;              // staged chunks per thread (e4m3 path)
-  constexpr int EPK = 32 / KS;                     // logits exponentiated per q.k k-step
-  constexpr int EPM = 32 / (4 * DT);               // logits max-reduced per p.v MFMA
   static_assert(!DIRECT || IPW * RPI == 16, "a wave loads 16 consecutive rows");
   static_assert(DIRECT || (PER >= 1 && BK * GCPR % NT == 0), "staged split");
   __shared__ __attribute__((aligned(1024))) char s_k[2 * BLKB];
@@ -426,23 +425,28 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s2[hf][i] = 0.f;
+      // p of logit e of sacc; odd e also packs the pair into pk and adds it
+      // (as rounded to bf16, the values the p.v MFMAs use) to the row sum
+      float pf[32];
       uint32_t pk[16];
       float ls0 = 0.f, ls1 = 0.f;
-      // exponentiate logits [e0, e0 + n) of sacc, packing pairs into pk
-      auto exps = [&](int e0, int n) __attribute__((always_inline)) {
-#pragma unroll
-        for (int e = e0; e < e0 + n; e += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 4][e & 15], c_eff, -m_use));
-          const float p1 =
-              __builtin_amdgcn_exp2f(fmaf(sacc[(e + 1) >> 4][(e + 1) & 15], c_eff, -m_use));
-          ls0 += p0;
-          ls1 += p1;
-          pk[e >> 1] = pack_bf16(p0, p1);
+      auto expo = [&](int e) __attribute__((always_inline)) {
+        pf[e] = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 4][e & 15], c_eff, -m_use));
+        if (e & 1) {
+          pk[e >> 1] = pack_bf16(pf[e - 1], pf[e]);
+          const bf16x2 pw = __builtin_bit_cast(bf16x2, pk[e >> 1]);
+          if (e & 2) ls1 = __builtin_amdgcn_fdot2_f32_bf16(pw, kOnes2, ls1, false);
+          else ls0 = __builtin_amdgcn_fdot2_f32_bf16(pw, kOnes2, ls0, false);
         }
       };
       // Source order is kept by fences: each chunk is one MFMA and its share
       // of VALU work, and the LDS reads of the next k-step are issued a chunk
-      // ahead of their MFMAs.
+      // ahead of their MFMAs.  The q.k MFMAs carry the p of logits 0..15, the
+      // first half of the p.v MFMAs (k-steps 0, 1, which use only those) the
+      // p of logits 16..31, the second half the mask / cap / max of S(b+1).
+      constexpr int XA = 8 / KS;          // logits exponentiated per q.k MFMA
+      constexpr int XB = 8 / DT;          // per p.v MFMA of k-steps 0, 1
+      constexpr int MB = 16 / DT;         // logits max-reduced per p.v MFMA of k-steps 2, 3
       bf16x8 a0 = ld_k(kn, 0, 0), a1 = ld_k(kn, 0, 1);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -453,17 +457,18 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
         s2[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], s2[0], 0, 0, 0);
-        exps(ks * EPK, EPK / 2);
+#pragma unroll
+        for (int x = 0; x < XA; ++x) expo((2 * ks) * XA + x);
         __builtin_amdgcn_sched_barrier(0);
         s2[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s2[1], 0, 0, 0);
-        exps(ks * EPK + EPK / 2, EPK / 2);
+#pragma unroll
+        for (int x = 0; x < XA; ++x) expo((2 * ks + 1) * XA + x);
         __builtin_amdgcn_sched_barrier(0);
         a0 = n0;
         a1 = n1;
       }
-      l_run += ls0 + ls1;
 
-      // (2) O^T += V^T(b) P^T(b), under the mask / cap / max of S(b+1)
+      // (2) O^T += V^T(b) P^T(b)
       const int k0n = (blk + 1) * BK;
       float m0 = -INFINITY, m1 = -INFINITY;
       bf16x8 va = ld_vt(vb, 0, 0);
@@ -478,18 +483,25 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
           else if (ks + 1 < 4) vn = ld_vt(vb, ks + 1, 0);
           __builtin_amdgcn_sched_barrier(0);
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[dt], 0, 0, 0);
+          const int m = ks * DT + dt;
+          if (ks < 2) {
 #pragma unroll
-          for (int q = 0; q < EPM; ++q) {
-            const int e = (ks * DT + dt) * EPM + q;
-            const float s = logit(mask_next, k0n, s2[e >> 4][e & 15], e);
-            s2[e >> 4][e & 15] = s;
-            if (q & 1) m1 = fmaxf(m1, s);
-            else m0 = fmaxf(m0, s);
+            for (int x = 0; x < XB; ++x) expo(16 + m * XB + x);
+          } else {
+#pragma unroll
+            for (int x = 0; x < MB; ++x) {
+              const int e = (m - 2 * DT) * MB + x;
+              const float sv = logit(mask_next, k0n, s2[e >> 4][e & 15], e);
+              s2[e >> 4][e & 15] = sv;
+              if (x & 1) m1 = fmaxf(m1, sv);
+              else m0 = fmaxf(m0, sv);
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
           va = vn;
         }
       }
+      l_run += ls0 + ls1;
       mx = fmaxf(m0, m1);
       mx = fmaxf(mx, __shfl_xor(mx, 32)) * c_eff;
       end_step(blk);
