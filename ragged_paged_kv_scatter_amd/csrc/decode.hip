@@ -453,53 +453,82 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
   }
 }
 
-// Merge of split partials by log-sum-exp, one wave per (row, q head):
-// M = max_j m_j (and the sink), L = sum_j 2^(m_j - M) l_j (+ 2^(sink - M)),
-// out = v_scale * sum_j 2^(m_j - M) acc_j / L.
-template <typename QT, int D>
+// Merge of split partials by log-sum-exp, one wave per (row, kv head) and its
+// G q heads: M = max_j m_j (and the sink), L = sum_j 2^(m_j - M) l_j
+// (+ 2^(sink - M)), out = v_scale * sum_j 2^(m_j - M) acc_j / L.  The lanes of
+// a head split its d range; the split loop is unrolled so that the loads of
+// several partials are in flight at once.
+template <int E>
+__device__ __forceinline__ void load_floats(const float* src, float* dst) {
+  if constexpr (E % 4 == 0) {
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(src + e);
+      dst[e] = v.x; dst[e + 1] = v.y; dst[e + 2] = v.z; dst[e + 3] = v.w;
+    }
+  } else if constexpr (E == 2) {
+    const float2 v = *reinterpret_cast<const float2*>(src);
+    dst[0] = v.x; dst[1] = v.y;
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) dst[e] = src[e];
+  }
+}
+
+template <typename QT, int D, int G>
 __global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
+  constexpr int LPH = 64 / G;           // lanes per head
+  constexpr int E = D / LPH;            // d elements per lane
+  static_assert(LPH * G == 64 && E * LPH == D, "merge lane split");
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(p.ws + p.lay.header);
   const RowDesc* rows = reinterpret_cast<const RowDesc*>(p.ws + p.lay.rows);
   const int32_t* merge_rows = reinterpret_cast<const int32_t*>(p.ws + p.lay.merge_rows);
   const float* part_ml = reinterpret_cast<const float*>(p.ws + p.lay.part_ml);
   const float* part_acc = reinterpret_cast<const float*>(p.ws + p.lay.part_acc);
-  constexpr int PER = (D + 63) / 64;
   const int lane = lane_id();
-  const long long total = (long long)hdr->n_merge_rows * p.Hq;
+  const int hi = lane / LPH, sub = lane % LPH;
+  const int Hq = p.Hq, Hkv = p.Hkv;
+  const long long total = (long long)hdr->n_merge_rows * Hkv;
   for (long long idx = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); idx < total;
        idx += (long long)gridDim.x * 4) {
-    const int mi = (int)(idx / p.Hq);
-    const int h = (int)(idx - (long long)mi * p.Hq);
+    const int mi = (int)(idx / Hkv);
+    const int g = (int)(idx - (long long)mi * Hkv);
+    const int h = g * G + hi;
     const RowDesc rd = rows[merge_rows[mi]];
     const int n = rd.n_split;
+    // M: the LPH lanes of a head take splits sub, sub + LPH, ...
     float M = -INFINITY;
-    for (int j = 0; j < n; ++j) M = fmaxf(M, part_ml[2 * ((long long)(rd.part_base + j) * p.Hq + h)]);
+    for (int j = sub; j < n; j += LPH)
+      M = fmaxf(M, part_ml[2 * ((long long)(rd.part_base + j) * Hq + h)]);
+#pragma unroll
+    for (int o = 1; o < LPH; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
     float sg = 0.f;
-    if (p.sink) { sg = p.sink[h] * kLog2e; M = fmaxf(M, sg); }
+    if (p.sink) {
+      sg = p.sink[h] * kLog2e;
+      M = fmaxf(M, sg);
+    }
     float L = p.sink ? __builtin_amdgcn_exp2f(sg - M) : 0.f;
-    float o[PER];
+    float o[E];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] = 0.f;
+    for (int e = 0; e < E; ++e) o[e] = 0.f;
+#pragma unroll 4
     for (int j = 0; j < n; ++j) {
-      const long long pb = (long long)(rd.part_base + j) * p.Hq + h;
-      const float w = __builtin_amdgcn_exp2f(part_ml[2 * pb] - M);
-      L += w * part_ml[2 * pb + 1];
+      const long long pb = (long long)(rd.part_base + j) * Hq + h;
+      const float2 ml = *reinterpret_cast<const float2*>(part_ml + 2 * pb);
+      float a[E];
+      load_floats<E>(part_acc + pb * D + sub * E, a);
+      const float w = __builtin_amdgcn_exp2f(ml.x - M);
+      L = fmaf(w, ml.y, L);
 #pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        const int d = lane + 64 * e;
-        if (d < D) o[e] = fmaf(w, part_acc[pb * D + d], o[e]);
-      }
+      for (int e = 0; e < E; ++e) o[e] = fmaf(w, a[e], o[e]);
     }
     const float sc = p.v_scale / L;
     QT* op = static_cast<QT*>(p.out);
+    const long long base = ((long long)rd.token * Hq + h) * D + sub * E;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int d = lane + 64 * e;
-      if (d < D) store_out<QT>(op, ((long long)rd.token * p.Hq + h) * D + d, o[e] * sc);
-    }
+    for (int e = 0; e < E; ++e) store_out<QT>(op, base + e, o[e] * sc);
   }
 }
-
 
 // Workgroups of `kernel` that fit on the device at once (occupancy x CUs).
 int resident_blocks(const void* kernel, int block_threads, size_t lds) {
@@ -555,19 +584,31 @@ hipError_t launch_rows(const AttnParams& p, rpa_dtype q_dt, rpa_dtype cache_dt, 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_merge(const AttnParams& p, rpa_dtype q_dt, hipStream_t s) {
-  const long long waves = (long long)p.lay.max_merge_rows * p.Hq;
-  if (waves <= 0) return hipSuccess;
-  long long wgs = (waves + 3) / 4;
-  dim3 grid((unsigned)(wgs < 4096 ? wgs : 4096));
-  if (q_dt == RPA_F32) {
-    if (p.D == 64) merge_kernel<float, 64><<<grid, 256, 0, s>>>(p);
-    else merge_kernel<float, 128><<<grid, 256, 0, s>>>(p);
-  } else {
-    if (p.D == 64) merge_kernel<uint16_t, 64><<<grid, 256, 0, s>>>(p);
-    else merge_kernel<uint16_t, 128><<<grid, 256, 0, s>>>(p);
+namespace {
+template <typename QT, int D>
+hipError_t launch_merge_d(const AttnParams& p, dim3 grid, hipStream_t s) {
+  switch (p.Hq / p.Hkv) {
+    case 1: merge_kernel<QT, D, 1><<<grid, 256, 0, s>>>(p); break;
+    case 2: merge_kernel<QT, D, 2><<<grid, 256, 0, s>>>(p); break;
+    case 4: merge_kernel<QT, D, 4><<<grid, 256, 0, s>>>(p); break;
+    case 8: merge_kernel<QT, D, 8><<<grid, 256, 0, s>>>(p); break;
+    case 16: merge_kernel<QT, D, 16><<<grid, 256, 0, s>>>(p); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_merge(const AttnParams& p, rpa_dtype q_dt, hipStream_t s) {
+  const long long waves = (long long)p.lay.max_merge_rows * p.Hkv;
+  if (waves <= 0) return hipSuccess;
+  const long long wgs = (waves + 3) / 4;
+  const dim3 grid((unsigned)(wgs < 4096 ? wgs : 4096));
+  if (q_dt == RPA_F32) {
+    return p.D == 64 ? launch_merge_d<float, 64>(p, grid, s) : launch_merge_d<float, 128>(p, grid, s);
+  }
+  return p.D == 64 ? launch_merge_d<uint16_t, 64>(p, grid, s)
+                   : launch_merge_d<uint16_t, 128>(p, grid, s);
 }
 
 }  // namespace rpa

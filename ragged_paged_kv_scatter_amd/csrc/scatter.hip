@@ -4,6 +4,8 @@
 // the cache shape).  A token's destination is one contiguous cache row of
 // 2 * Hkv * Dpad elements (K_0 V_0 K_1 V_1 ...), so every workgroup writes
 // whole rows with 16-byte stores; bf16 -> e4m3 quantisation is fused.
+#include <algorithm>
+
 #include "device_common.h"
 #include "rpa_internal.h"
 
@@ -11,7 +13,8 @@ namespace rpa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTokensPerWG = 8;
+constexpr int kTokensPerWG = 8;       // at most; fewer when the batch is small
+constexpr int kTargetWGs = 1024;      // spread small batches over the chip
 
 // Element sizes by type tag.
 template <typename T> struct Elem;
@@ -33,10 +36,10 @@ __device__ __forceinline__ int find_seq(const int32_t* qsl, int num_seqs, int to
 constexpr int kSeqsInLds = 1024;   // query_start_loc is searched in LDS up to this many seqs
 
 template <typename IN, typename C>
-__global__ __launch_bounds__(kThreads) void scatter_kernel(ScatterParams p) {
+__global__ __launch_bounds__(kThreads) void scatter_kernel(ScatterParams p, int tpw) {
   __shared__ long long s_row[kTokensPerWG];  // destination cache row (element index), -1 = skip
   __shared__ int32_t s_qsl[kSeqsInLds + 1];
-  const int tok0 = blockIdx.x * kTokensPerWG;
+  const int tok0 = blockIdx.x * tpw;
   const int num_seqs = min(max(p.dist[0] + p.dist[1] + p.dist[2], 0), p.max_num_seqs);
   const bool qsl_in_lds = num_seqs <= kSeqsInLds;
   if (qsl_in_lds) {
@@ -44,7 +47,7 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScatterParams p) {
     __syncthreads();
   }
   const int n_valid = num_seqs > 0 ? (qsl_in_lds ? s_qsl[num_seqs] : p.qsl[num_seqs]) : 0;
-  if (threadIdx.x < kTokensPerWG) {
+  if (threadIdx.x < tpw) {
     const int tok = tok0 + threadIdx.x;
     long long row = -1;
     if (tok < n_valid && tok < p.T) {
@@ -63,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScatterParams p) {
   constexpr int EPC = 16 / ESZ;                    // cache elements per 16-byte chunk
   const int chunks_per_head = p.Dpad / EPC;        // Dpad * ESZ % 16 == 0 (host-checked)
   const int chunks_per_row = 2 * p.Hkv * chunks_per_head;
-  const int total = kTokensPerWG * chunks_per_row;
+  const int total = tpw * chunks_per_row;
   const IN* keys = static_cast<const IN*>(p.keys);
   const IN* values = static_cast<const IN*>(p.values);
   C* cache = static_cast<C*>(p.cache);
@@ -112,15 +115,16 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScatterParams p) {
 hipError_t launch_scatter(const ScatterParams& p, rpa_dtype in_dt, rpa_dtype cache_dt,
                           hipStream_t s) {
   if (p.T <= 0) return hipSuccess;
-  dim3 grid((p.T + kTokensPerWG - 1) / kTokensPerWG), block(kThreads);
+  const int tpw = std::min(kTokensPerWG, std::max(1, (p.T + kTargetWGs - 1) / kTargetWGs));
+  dim3 grid((p.T + tpw - 1) / tpw), block(kThreads);
   if (in_dt == RPA_F32 && cache_dt == RPA_F32) {
-    scatter_kernel<float, float><<<grid, block, 0, s>>>(p);
+    scatter_kernel<float, float><<<grid, block, 0, s>>>(p, tpw);
   } else if (in_dt == RPA_BF16 && cache_dt == RPA_BF16) {
-    scatter_kernel<uint16_t, uint16_t><<<grid, block, 0, s>>>(p);
+    scatter_kernel<uint16_t, uint16_t><<<grid, block, 0, s>>>(p, tpw);
   } else if (in_dt == RPA_BF16 && cache_dt == RPA_FP8_E4M3) {
-    scatter_kernel<uint16_t, uint8_t><<<grid, block, 0, s>>>(p);
+    scatter_kernel<uint16_t, uint8_t><<<grid, block, 0, s>>>(p, tpw);
   } else if (in_dt == RPA_FP8_E4M3 && cache_dt == RPA_FP8_E4M3) {
-    scatter_kernel<uint8_t, uint8_t><<<grid, block, 0, s>>>(p);
+    scatter_kernel<uint8_t, uint8_t><<<grid, block, 0, s>>>(p, tpw);
   } else {
     return hipErrorInvalidValue;
   }
