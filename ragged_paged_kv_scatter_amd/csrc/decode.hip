@@ -35,11 +35,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-template <int BYTES> struct Vec;
-template <> struct Vec<16> { using T = uint4; };
-template <> struct Vec<8> { using T = uint2; };
-template <> struct Vec<4> { using T = uint32_t; };
-
 template <int CTRL>
 __device__ __forceinline__ float dppf(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
@@ -160,15 +155,16 @@ struct Chunk {
   static constexpr int NP = (sizeof(CT) == 4) ? EPL : EPL / 2;   // words after widening
 };
 
+// The cache is streamed once per call: loads are non-temporal (nt), which
+// keeps them from displacing reusable lines in L2.
 template <typename CT, int EPL>
 __device__ __forceinline__ void load_chunk(const CT* ptr, bool valid, uint32_t* w) {
-  using V = typename Vec<Chunk<CT, EPL>::BYTES>::T;
   constexpr int NW = Chunk<CT, EPL>::NW;
+  typedef uint32_t words __attribute__((ext_vector_type(NW)));
   if (valid) {
-    const V v = *reinterpret_cast<const V*>(ptr);
-    const uint32_t* vw = reinterpret_cast<const uint32_t*>(&v);
+    const words v = __builtin_nontemporal_load(reinterpret_cast<const words*>(ptr));
 #pragma unroll
-    for (int i = 0; i < NW; ++i) w[i] = vw[i];
+    for (int i = 0; i < NW; ++i) w[i] = v[i];
   } else {
 #pragma unroll
     for (int i = 0; i < NW; ++i) w[i] = 0u;
