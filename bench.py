@@ -105,8 +105,8 @@ def cpu_baseline(w, budget_s=15.0):
 
 
 KERNEL_SOURCES = {  # kernel -> sources whose hash identifies a counter summary
-    "decode": ["decode.hip", "device_common.h", "rpa_internal.h"],
-    "prefill": ["prefill.hip", "device_common.h", "rpa_internal.h"],
+    "decode": ["decode.hip", "merge.h", "device_common.h", "rpa_internal.h"],
+    "prefill": ["prefill.hip", "merge.h", "device_common.h", "rpa_internal.h"],
 }
 KERNEL_SYMBOL = {"decode": "row_kernel", "prefill": "prefill_kernel"}
 

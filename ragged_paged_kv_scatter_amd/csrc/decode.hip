@@ -26,6 +26,7 @@
 #include <utility>
 
 #include "device_common.h"
+#include "merge.h"
 #include "rpa_internal.h"
 
 namespace rpa {
@@ -136,15 +137,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
                                          __builtin_bit_cast(bf16x2, b), c, false);
-}
-
-template <typename QT>
-__device__ __forceinline__ void store_out(QT* o, long long idx, float v);
-template <>
-__device__ __forceinline__ void store_out<float>(float* o, long long idx, float v) { o[idx] = v; }
-template <>
-__device__ __forceinline__ void store_out<uint16_t>(uint16_t* o, long long idx, float v) {
-  o[idx] = (uint16_t)f32_to_bf16(v);
 }
 
 // Head-row chunk of EPL cache elements -> words: fp32 words, or bf16 pairs.
@@ -449,81 +441,15 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
   }
 }
 
-// Merge of split partials by log-sum-exp, one wave per (row, kv head) and its
-// G q heads: M = max_j m_j (and the sink), L = sum_j 2^(m_j - M) l_j
-// (+ 2^(sink - M)), out = v_scale * sum_j 2^(m_j - M) acc_j / L.  The lanes of
-// a head split its d range; the split loop is unrolled so that the loads of
-// several partials are in flight at once.
-template <int E>
-__device__ __forceinline__ void load_floats(const float* src, float* dst) {
-  if constexpr (E % 4 == 0) {
-#pragma unroll
-    for (int e = 0; e < E; e += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(src + e);
-      dst[e] = v.x; dst[e + 1] = v.y; dst[e + 2] = v.z; dst[e + 3] = v.w;
-    }
-  } else if constexpr (E == 2) {
-    const float2 v = *reinterpret_cast<const float2*>(src);
-    dst[0] = v.x; dst[1] = v.y;
-  } else {
-#pragma unroll
-    for (int e = 0; e < E; ++e) dst[e] = src[e];
-  }
-}
-
+// Stand-alone merge of the split partials (when no prefill kernel runs after
+// the row kernel to do it): four merge items per workgroup.
 template <typename QT, int D, int G>
 __global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
-  constexpr int LPH = 64 / G;           // lanes per head
-  constexpr int E = D / LPH;            // d elements per lane
-  static_assert(LPH * G == 64 && E * LPH == D, "merge lane split");
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(p.ws + p.lay.header);
-  const RowDesc* rows = reinterpret_cast<const RowDesc*>(p.ws + p.lay.rows);
-  const int32_t* merge_rows = reinterpret_cast<const int32_t*>(p.ws + p.lay.merge_rows);
-  const float* part_ml = reinterpret_cast<const float*>(p.ws + p.lay.part_ml);
-  const float* part_acc = reinterpret_cast<const float*>(p.ws + p.lay.part_acc);
-  const int lane = lane_id();
-  const int hi = lane / LPH, sub = lane % LPH;
-  const int Hq = p.Hq, Hkv = p.Hkv;
-  const long long total = (long long)hdr->n_merge_rows * Hkv;
+  const long long total = (long long)hdr->n_merge_rows * p.Hkv;
   for (long long idx = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); idx < total;
-       idx += (long long)gridDim.x * 4) {
-    const int mi = (int)(idx / Hkv);
-    const int g = (int)(idx - (long long)mi * Hkv);
-    const int h = g * G + hi;
-    const RowDesc rd = rows[merge_rows[mi]];
-    const int n = rd.n_split;
-    // M: the LPH lanes of a head take splits sub, sub + LPH, ...
-    float M = -INFINITY;
-    for (int j = sub; j < n; j += LPH)
-      M = fmaxf(M, part_ml[2 * ((long long)(rd.part_base + j) * Hq + h)]);
-#pragma unroll
-    for (int o = 1; o < LPH; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
-    float sg = 0.f;
-    if (p.sink) {
-      sg = p.sink[h] * kLog2e;
-      M = fmaxf(M, sg);
-    }
-    float L = p.sink ? __builtin_amdgcn_exp2f(sg - M) : 0.f;
-    float o[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = 0.f;
-#pragma unroll 4
-    for (int j = 0; j < n; ++j) {
-      const long long pb = (long long)(rd.part_base + j) * Hq + h;
-      const float2 ml = *reinterpret_cast<const float2*>(part_ml + 2 * pb);
-      float a[E];
-      load_floats<E>(part_acc + pb * D + sub * E, a);
-      const float w = __builtin_amdgcn_exp2f(ml.x - M);
-      L = fmaf(w, ml.y, L);
-#pragma unroll
-      for (int e = 0; e < E; ++e) o[e] = fmaf(w, a[e], o[e]);
-    }
-    const float sc = p.v_scale / L;
-    QT* op = static_cast<QT*>(p.out);
-    const long long base = ((long long)rd.token * Hq + h) * D + sub * E;
-#pragma unroll
-    for (int e = 0; e < E; ++e) store_out<QT>(op, base + e, o[e] * sc);
-  }
+       idx += (long long)gridDim.x * 4)
+    merge_one<QT, D, G>(p, idx);
 }
 
 // Workgroups of `kernel` that fit on the device at once (occupancy x CUs).

@@ -27,9 +27,12 @@
 // way.  k_scale is folded into the logit scale and v_scale into 1/l.
 #include <math.h>
 
+#include <algorithm>
+
 #include <type_traits>
 
 #include "device_common.h"
+#include "merge.h"
 #include "rpa_internal.h"
 
 namespace rpa {
@@ -210,6 +213,15 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
     const i16x8 av = {x1[0], x1[1], x1[2], x1[3], x2[0], x2[1], x2[2], x2[3]};
     return __builtin_bit_cast(bf16x8, av);
   };
+
+  // Split-KV partials of the row kernel (launched before this one): one wave
+  // per (row, kv head).  They touch rows this kernel does not write.
+  if (p.fuse_merge) {
+    const long long n_merge = (long long)hdr->n_merge_rows * Hkv;
+    for (long long mi = (long long)blockIdx.x * 4 + wave; mi < n_merge;
+         mi += (long long)gridDim.x * 4)
+      merge_one_g<uint16_t, D>(p, mi);
+  }
 
   // Persistent grid (a multiple of 8 blocks): block b takes units b, b + grid,
   // ...  Consecutive units sit on different XCDs; the head slot -> (kv head =
@@ -623,7 +635,9 @@ hipError_t launch_d(const AttnParams& p, long long blocks, hipStream_t s) {
 
 template <typename CT>
 hipError_t launch_t(const AttnParams& p, hipStream_t s) {
-  const long long blocks = (long long)p.lay.max_pf_items * p.Hq;
+  const long long merge_blocks =
+      p.fuse_merge ? ((long long)p.lay.max_merge_rows * p.Hkv + 3) / 4 : 0;
+  const long long blocks = std::max((long long)p.lay.max_pf_items * p.Hq, merge_blocks);
   if (blocks <= 0) return hipSuccess;
   const bool cap = p.cap > 0.f;
   if (p.D == 64) return cap ? launch_d<CT, 64, true>(p, blocks, s) : launch_d<CT, 64, false>(p, blocks, s);

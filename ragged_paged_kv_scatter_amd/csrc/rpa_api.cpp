@@ -281,18 +281,20 @@ int rpa_forward(const rpa_desc* desc, const rpa_options* opts, const void* queri
   ap.cap = opts->logits_soft_cap;
   const rpa_dtype qd = (rpa_dtype)desc->q_dtype, cd = (rpa_dtype)desc->cache_dtype;
 
-  if (prefill_supported(*desc)) {
-    prof_begin("prefill", s);
-    e = launch_prefill(ap, qd, cd, s);
-    prof_end(s);
-    if (e != hipSuccess) return hip_fail(e);
-  }
+  // rows, then either the prefill kernel (which first merges the rows'
+  // split partials) or the stand-alone merge
   prof_begin("decode", s);
   e = launch_rows(ap, qd, cd, s);
   prof_end(s);
   if (e != hipSuccess) return hip_fail(e);
-  prof_begin("merge", s);
-  e = launch_merge(ap, qd, s);
+  if (prefill_supported(*desc)) {
+    ap.fuse_merge = 1;
+    prof_begin("prefill", s);
+    e = launch_prefill(ap, qd, cd, s);
+  } else {
+    prof_begin("merge", s);
+    e = launch_merge(ap, qd, s);
+  }
   prof_end(s);
   if (e != hipSuccess) return hip_fail(e);
   return RPA_OK;

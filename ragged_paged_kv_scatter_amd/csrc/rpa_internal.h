@@ -113,6 +113,7 @@ struct AttnParams {
   float qk_scale;      // softmax_scale * q_scale * k_scale
   float v_scale;       // 1 when none
   float cap;           // 0 when none
+  int32_t fuse_merge;  // prefill kernel: first merge the row kernel's split partials
 };
 
 // Launchers (return hipSuccess or the launch error).
