@@ -1,0 +1,223 @@
+// Device-side planner: reads the ragged metadata (query_start_loc, kv_lens,
+// distribution) on the GPU, so no host synchronisation is needed, and writes
+// the work lists of the attention kernels into the workspace:
+//   * row items: (query row, KV split) for rows served by the row kernel;
+//   * prefill items: (sequence, query tile) for the MFMA prefill kernel.
+// One workgroup of 1024 threads; per-sequence tables live in LDS.
+#pragma once
+
+#include "device_common.h"
+#include "rpa_internal.h"
+
+namespace rpa {
+namespace plan_detail {
+
+constexpr int kT = kPlanThreads;
+constexpr int kWaves = kT / 64;
+
+// Exclusive prefix sum over the workgroup; returns the prefix of this thread
+// and writes the total to *total.  All threads must call it.
+template <typename V>
+__device__ V block_exclusive_scan(V v, V* total, V* s_waves) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  V x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    V y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_waves[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    V acc = 0;
+    for (int w = 0; w < kWaves; ++w) { V t = s_waves[w]; s_waves[w] = acc; acc += t; }
+    s_waves[kWaves] = acc;
+  }
+  __syncthreads();
+  V res = x - v + s_waves[wave];
+  *total = s_waves[kWaves];
+  __syncthreads();
+  return res;
+}
+
+__device__ __forceinline__ long long visible_sum(int ctx, int q_len, int window) {
+  // sum over t < q_len of the visible length of query t (position ctx + t):
+  // min(ctx + t + 1, W) with a window, ctx + t + 1 without.
+  long long q = q_len, c = ctx;
+  if (window <= 0) return q * (c + 1) + q * (q - 1) / 2;
+  long long n1 = min(max((long long)window - c, 0LL), q);
+  return n1 * (c + 1) + n1 * (n1 - 1) / 2 + (q - n1) * (long long)window;
+}
+
+// The planner, run by one workgroup of kPlanThreads threads; s_seq_rows is
+// dynamic LDS of max_num_seqs + 1 entries.
+__device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_rows) {
+  __shared__ long long s_w64[kWaves + 1];
+  __shared__ int32_t s_w32[kWaves + 1];
+  __shared__ int32_t s_w32b[kWaves + 1];
+  __shared__ int32_t s_w32c[kWaves + 1];
+
+  char* ws = p.ws;
+  PlanHeader* hdr = reinterpret_cast<PlanHeader*>(ws + p.lay.header);
+  RowDesc* rows = reinterpret_cast<RowDesc*>(ws + p.lay.rows);
+  ItemDesc* items = reinterpret_cast<ItemDesc*>(ws + p.lay.items);
+  int32_t* merge_rows = reinterpret_cast<int32_t*>(ws + p.lay.merge_rows);
+  PrefillItem* pf = reinterpret_cast<PrefillItem*>(ws + p.lay.pf_items);
+
+  const int num_seqs = min(max(p.dist[0] + p.dist[1] + p.dist[2], 0), p.max_num_seqs);
+  const int W = p.window;
+  // zero row the prefill kernel reads for keys outside a tile's visible range
+  for (int i = threadIdx.x; i < kZeroBytes / 4; i += kT)
+    reinterpret_cast<int32_t*>(ws + p.lay.zeros)[i] = 0;
+
+  // ---- pass 1: per-sequence row counts, prefill tiles, visible-key totals ----
+  int row_base = 0, pf_base = 0;
+  long long vis_total = 0;
+  for (int base = 0; base < num_seqs; base += kT) {
+    const int s = base + threadIdx.x;
+    int n_rows = 0, n_pf = 0;
+    long long vis = 0;
+    int q0 = 0, q_len = 0, ctx = 0;
+    if (s < num_seqs) {
+      q0 = p.qsl[s];
+      q_len = p.qsl[s + 1] - q0;
+      ctx = p.kv_lens[s] - q_len;
+      if (q_len > 0) {
+        if (q_len >= p.prefill_min_q) {
+          n_pf = (q_len + kPrefillBQ - 1) / kPrefillBQ;
+        } else {
+          n_rows = q_len;
+          vis = visible_sum(ctx, q_len, W);
+        }
+      }
+    }
+    int tot_rows, tot_pf;
+    long long tot_vis;
+    const int my_row = block_exclusive_scan(n_rows, &tot_rows, s_w32) + row_base;
+    const int my_pf = block_exclusive_scan(n_pf, &tot_pf, s_w32b) + pf_base;
+    block_exclusive_scan(vis, &tot_vis, s_w64);
+    if (s < num_seqs) {
+      s_seq_rows[s] = my_row;
+      // heaviest tiles first within a sequence (causal: later tiles see more keys)
+      for (int i = 0; i < n_pf; ++i) {
+        const int tile = n_pf - 1 - i;
+        PrefillItem it;
+        it.seq = s;
+        it.q_begin = tile * kPrefillBQ;
+        it.q_end = min(q_len, (tile + 1) * kPrefillBQ);
+        it.pad = 0;
+        if (my_pf + i < p.lay.max_pf_items) pf[my_pf + i] = it;
+      }
+    }
+    row_base += tot_rows;
+    pf_base += tot_pf;
+    vis_total += tot_vis;
+  }
+  if (threadIdx.x == 0) s_seq_rows[num_seqs] = row_base;
+  __syncthreads();
+  const int n_rows = min(row_base, p.lay.max_rows);
+
+  // ---- split size: about kTargetWaves waves of work over all kv heads ----
+  const long long target_items = max(1, min(kTargetItems, kTargetWaves / max(p.Hkv, 1)));
+  long long S = (vis_total + target_items - 1) / target_items;
+  S = (S + 15) / 16 * 16;
+  if (S < kMinSplit) S = kMinSplit;
+  const int split = (int)min(S, (long long)0x40000000);
+
+  // row r -> (seq, token, visible range [lo, hi))
+  auto row_info = [&](int r, int& seq, int& token, int& lo, int& hi) {
+    int a = 0, b = num_seqs - 1;                    // largest s with s_seq_rows[s] <= r
+    while (a < b) {
+      const int mid = (a + b + 1) >> 1;
+      if (s_seq_rows[mid] <= r) a = mid; else b = mid - 1;
+    }
+    seq = a;
+    const int t = r - s_seq_rows[seq];
+    const int q0 = p.qsl[seq];
+    const int q_len = p.qsl[seq + 1] - q0;
+    const int pos = p.kv_lens[seq] - q_len + t;
+    token = q0 + t;
+    hi = pos + 1;
+    lo = (W > 0) ? max(0, pos - W + 1) : 0;
+  };
+
+  // ---- pass 2a: number of full-size splits (they are scheduled first) ----
+  int n_full_total = 0;
+  for (int base = 0; base < n_rows; base += kT) {
+    const int r = base + threadIdx.x;
+    int n_full = 0;
+    if (r < n_rows) {
+      int seq, token, lo, hi;
+      row_info(r, seq, token, lo, hi);
+      n_full = (hi - lo) / split;
+    }
+    int tot;
+    block_exclusive_scan(n_full, &tot, s_w32);
+    n_full_total += tot;
+  }
+
+  // ---- pass 2b: rows, their items (full splits first, then the remainders) ----
+  int full_base = 0, rem_base = n_full_total, part_base = 0, merge_base = 0;
+  for (int base = 0; base < n_rows; base += kT) {
+    const int r = base + threadIdx.x;
+    int n_split = 0, n_full = 0, seq = 0, lo = 0, hi = 0, token = 0;
+    if (r < n_rows) {
+      row_info(r, seq, token, lo, hi);
+      n_full = (hi - lo) / split;
+      n_split = (hi - lo + split - 1) / split;
+    }
+    const int has_rem = n_split - n_full;
+    int tot_full, tot_rem, tot_parts, tot_merge;
+    const int my_full = block_exclusive_scan(n_full, &tot_full, s_w32) + full_base;
+    const int my_rem = block_exclusive_scan(has_rem, &tot_rem, s_w32b) + rem_base;
+    const int my_part =
+        block_exclusive_scan(n_split > 1 ? n_split : 0, &tot_parts, s_w32c) + part_base;
+    const int my_merge = block_exclusive_scan(n_split > 1 ? 1 : 0, &tot_merge, s_w32) +
+                         merge_base;
+    if (r < n_rows) {
+      RowDesc rd;
+      rd.token = token;
+      rd.seq = seq;
+      rd.lo = lo;
+      rd.hi = hi;
+      rd.n_split = n_split;
+      rd.part_base = n_split > 1 ? my_part : -1;
+      rd.pad[0] = rd.pad[1] = 0;
+      rows[r] = rd;
+      for (int j = 0; j < n_split; ++j) {
+        const int slot = (j < n_full) ? my_full + j : my_rem;
+        if (slot >= p.lay.max_items) break;
+        ItemDesc it;
+        it.row = r;
+        it.lo = lo + j * split;
+        it.hi = min(hi, lo + (j + 1) * split);
+        it.part = n_split > 1 ? my_part + j : -1;
+        items[slot] = it;
+      }
+      if (n_split > 1 && my_merge < p.lay.max_merge_rows) merge_rows[my_merge] = r;
+    }
+    full_base += tot_full;
+    rem_base += tot_rem;
+    part_base += tot_parts;
+    merge_base += tot_merge;
+  }
+  const int item_base = rem_base;
+  if (threadIdx.x == 0) {
+    PlanHeader h = {};
+    h.num_seqs = num_seqs;
+    h.n_rows = n_rows;
+    h.n_items = min(item_base, p.lay.max_items);
+    h.split = split;
+    h.n_merge_rows = min(merge_base, p.lay.max_merge_rows);
+    h.n_pf_items = min(pf_base, p.lay.max_pf_items);
+    h.row_next = 0;
+    h.pf_next = 0;
+    *hdr = h;
+  }
+}
+
+}  // namespace plan_detail
+
+using plan_detail::plan_body;
+
+}  // namespace rpa

@@ -171,6 +171,32 @@ using namespace rpa;
 
 extern "C" {
 
+namespace {
+ScatterParams scatter_params(const rpa_desc& d, const void* keys, const void* values,
+                             void* kv_cache, const int32_t* kv_lens, const int32_t* block_tables,
+                             const int32_t* qsl, const int32_t* dist, float k_scale,
+                             float v_scale) {
+  ScatterParams p = {};
+  p.keys = keys;
+  p.values = values;
+  p.cache = kv_cache;
+  p.kv_lens = kv_lens;
+  p.block_tables = block_tables;
+  p.qsl = qsl;
+  p.dist = dist;
+  p.T = d.total_tokens;
+  p.max_num_seqs = d.max_num_seqs;
+  p.pps = d.pages_per_seq;
+  p.page_size = d.page_size;
+  p.Hkv = d.num_kv_heads;
+  p.D = d.head_dim;
+  p.Dpad = d.head_dim_padded;
+  p.inv_k_scale_src = k_scale > 0.f ? k_scale : 1.f;
+  p.inv_v_scale_src = v_scale > 0.f ? v_scale : 1.f;
+  return p;
+}
+}  // namespace
+
 int rpa_update_kv_cache(const rpa_desc* desc, const void* keys, const void* values,
                         void* kv_cache, const int32_t* kv_lens, const int32_t* block_tables,
                         const int32_t* query_start_loc, const int32_t* distribution,
@@ -182,23 +208,8 @@ int rpa_update_kv_cache(const rpa_desc* desc, const void* keys, const void* valu
   if (!finite_nonneg(k_scale) || !finite_nonneg(v_scale)) return RPA_ERR_INVALID_OPTION;
   if (!aligned16(keys) || !aligned16(values) || !aligned16(kv_cache)) return RPA_ERR_INVALID_SHAPE;
   if (desc->total_tokens == 0 || desc->max_num_seqs == 0) return RPA_OK;
-  ScatterParams p = {};
-  p.keys = keys;
-  p.values = values;
-  p.cache = kv_cache;
-  p.kv_lens = kv_lens;
-  p.block_tables = block_tables;
-  p.qsl = query_start_loc;
-  p.dist = distribution;
-  p.T = desc->total_tokens;
-  p.max_num_seqs = desc->max_num_seqs;
-  p.pps = desc->pages_per_seq;
-  p.page_size = desc->page_size;
-  p.Hkv = desc->num_kv_heads;
-  p.D = desc->head_dim;
-  p.Dpad = desc->head_dim_padded;
-  p.inv_k_scale_src = k_scale > 0.f ? k_scale : 1.f;
-  p.inv_v_scale_src = v_scale > 0.f ? v_scale : 1.f;
+  const ScatterParams p = scatter_params(*desc, keys, values, kv_cache, kv_lens, block_tables,
+                                         query_start_loc, distribution, k_scale, v_scale);
   hipStream_t s = static_cast<hipStream_t>(stream);
   prof_begin("scatter", s);
   hipError_t e = launch_scatter(p, (rpa_dtype)desc->kv_in_dtype, (rpa_dtype)desc->cache_dtype, s);
@@ -234,11 +245,6 @@ int rpa_forward(const rpa_desc* desc, const rpa_options* opts, const void* queri
   if (desc->total_tokens == 0 || desc->max_num_seqs == 0) return RPA_OK;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (keys) {
-    st = rpa_update_kv_cache(desc, keys, values, kv_cache, kv_lens, block_tables,
-                             query_start_loc, distribution, opts->k_scale, opts->v_scale, stream);
-    if (st) return st;
-  }
   char* ws = static_cast<char*>(workspace);
   PlanParams pp = {};
   pp.kv_lens = kv_lens;
@@ -251,8 +257,14 @@ int rpa_forward(const rpa_desc* desc, const rpa_options* opts, const void* queri
   pp.window = opts->sliding_window;
   pp.prefill_min_q = prefill_min_q(*desc);
   pp.Hkv = desc->num_kv_heads;
-  prof_begin("plan", s);
-  hipError_t e = launch_plan(pp, s);
+  // one launch: the planner, and the cache update when new tokens come along
+  ScatterParams sp = {};
+  if (keys)
+    sp = scatter_params(*desc, keys, values, kv_cache, kv_lens, block_tables, query_start_loc,
+                        distribution, opts->k_scale, opts->v_scale);
+  prof_begin(keys ? "plan+scatter" : "plan", s);
+  hipError_t e = launch_prep(pp, keys ? &sp : nullptr, (rpa_dtype)desc->kv_in_dtype,
+                             (rpa_dtype)desc->cache_dtype, s);
   prof_end(s);
   if (e != hipSuccess) return hip_fail(e);
 

@@ -119,7 +119,9 @@ struct AttnParams {
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_scatter(const ScatterParams& p, rpa_dtype in_dt, rpa_dtype cache_dt,
                           hipStream_t s);
-hipError_t launch_plan(const PlanParams& p, hipStream_t s);
+// planner, plus the cache update when sp is non-NULL (one launch)
+hipError_t launch_prep(const PlanParams& pp, const ScatterParams* sp, rpa_dtype in_dt,
+                       rpa_dtype cache_dt, hipStream_t s);
 hipError_t launch_rows(const AttnParams& p, rpa_dtype q_dt, rpa_dtype cache_dt, hipStream_t s);
 hipError_t launch_merge(const AttnParams& p, rpa_dtype q_dt, hipStream_t s);
 hipError_t launch_prefill(const AttnParams& p, rpa_dtype q_dt, rpa_dtype cache_dt,
