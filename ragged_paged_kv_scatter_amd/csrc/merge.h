@@ -1,10 +1,12 @@
 // Merge of the split-KV partials written by the row kernel, by log-sum-exp:
-// for a row and q head, M = max_j m_j (and the sink), L = sum_j 2^(m_j - M) l_j
-// (+ 2^(sink - M)), out = v_scale * sum_j 2^(m_j - M) acc_j / L (m in log2
-// units).  One wave merges one (row, kv head) with its G q heads: the lanes of
-// a head split its d range, and the split loop is unrolled so that the loads
-// of several partials are in flight at once.  Used by the stand-alone merge
-// kernel and by the prefill kernel, which merges before its own work.
+// for a row and q head, out = v_scale * sum_j 2^(m_j - M) acc_j / L with
+// M = max_j m_j (and the sink) and L = sum_j 2^(m_j - M) l_j (+ 2^(sink - M)),
+// m in log2 units.  One wave merges one (row, kv head) with its G q heads: the
+// lanes of a head split its d range.  The running form (M, L, acc rescaled as
+// M grows) takes one pass over the partials, and the split loop is unrolled
+// so that the loads of several partials are in flight at once.  Used by the
+// stand-alone merge kernel and by the prefill kernel, which merges before its
+// own work.
 #pragma once
 
 #include "device_common.h"
@@ -49,8 +51,7 @@ __device__ __forceinline__ void merge_one(const AttnParams& p, long long idx) {
   constexpr int E = D / LPH;            // d elements per lane
   constexpr float kLog2eM = 1.4426950408889634f;
   static_assert(LPH * G == 64 && E * LPH == D, "merge lane split");
-  const RowDesc* rows = reinterpret_cast<const RowDesc*>(p.ws + p.lay.rows);
-  const int32_t* merge_rows = reinterpret_cast<const int32_t*>(p.ws + p.lay.merge_rows);
+  const MergeDesc* merge_rows = reinterpret_cast<const MergeDesc*>(p.ws + p.lay.merge_rows);
   const float* part_ml = reinterpret_cast<const float*>(p.ws + p.lay.part_ml);
   const float* part_acc = reinterpret_cast<const float*>(p.ws + p.lay.part_acc);
   const int lane = lane_id();
@@ -59,37 +60,34 @@ __device__ __forceinline__ void merge_one(const AttnParams& p, long long idx) {
   const int mi = (int)(idx / Hkv);
   const int g = (int)(idx - (long long)mi * Hkv);
   const int h = g * G + hi;
-  const RowDesc rd = rows[merge_rows[mi]];
-  const int n = rd.n_split;
-  // M: the LPH lanes of a head take splits sub, sub + LPH, ...
-  float M = -INFINITY;
-  for (int j = sub; j < n; j += LPH)
-    M = fmaxf(M, part_ml[2 * ((long long)(rd.part_base + j) * Hq + h)]);
-#pragma unroll
-  for (int o = 1; o < LPH; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
-  float sg = 0.f;
+  const MergeDesc md = merge_rows[mi];
+  // running state; the sink enters as a partial with l = 1 and acc = 0
+  float M = -INFINITY, L = 0.f;
   if (p.sink) {
-    sg = p.sink[h] * kLog2eM;
-    M = fmaxf(M, sg);
+    M = p.sink[h] * kLog2eM;
+    L = 1.f;
   }
-  float L = p.sink ? __builtin_amdgcn_exp2f(sg - M) : 0.f;
   float o[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = 0.f;
 #pragma unroll 4
-  for (int j = 0; j < n; ++j) {
-    const long long pb = (long long)(rd.part_base + j) * Hq + h;
+  for (int j = 0; j < md.n_split; ++j) {
+    const long long pb = (long long)(md.part_base + j) * Hq + h;
     const float2 ml = *reinterpret_cast<const float2*>(part_ml + 2 * pb);
     float a[E];
     load_floats<E>(part_acc + pb * D + sub * E, a);
-    const float w = __builtin_amdgcn_exp2f(ml.x - M);
-    L = fmaf(w, ml.y, L);
+    const float m_new = fmaxf(M, ml.x);
+    const bool none = m_new == -INFINITY;           // nothing seen yet
+    const float r = none ? 1.f : __builtin_amdgcn_exp2f(M - m_new);
+    const float w = none ? 0.f : __builtin_amdgcn_exp2f(ml.x - m_new);
+    M = m_new;
+    L = fmaf(w, ml.y, L * r);
 #pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = fmaf(w, a[e], o[e]);
+    for (int e = 0; e < E; ++e) o[e] = fmaf(w, a[e], o[e] * r);
   }
   const float sc = p.v_scale / L;
   QT* op = static_cast<QT*>(p.out);
-  const long long base = ((long long)rd.token * Hq + h) * D + sub * E;
+  const long long base = ((long long)md.token * Hq + h) * D + sub * E;
 #pragma unroll
   for (int e = 0; e < E; ++e) store_out<QT>(op, base + e, o[e] * sc);
 }

@@ -50,8 +50,13 @@ __device__ __forceinline__ long long visible_sum(int ctx, int q_len, int window)
 }
 
 // The planner, run by one workgroup of kPlanThreads threads; s_seq_rows is
-// dynamic LDS of max_num_seqs + 1 entries.
+// dynamic LDS of plan_lds_words(max_num_seqs) words: the first row of each
+// sequence and, when max_num_seqs <= kPlanCacheSeqs, the sequences' first
+// query token and context length, so later passes need no global reads.
 __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_rows) {
+  const bool cached = p.max_num_seqs <= kPlanCacheSeqs;
+  int32_t* s_q0 = s_seq_rows + (p.max_num_seqs + 1);   // qsl[s], s <= num_seqs (cached)
+  int32_t* s_ctx = s_q0 + (p.max_num_seqs + 1);        // kv_len - q_len (cached)
   __shared__ long long s_w64[kWaves + 1];
   __shared__ int32_t s_w32[kWaves + 1];
   __shared__ int32_t s_w32b[kWaves + 1];
@@ -61,7 +66,7 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
   PlanHeader* hdr = reinterpret_cast<PlanHeader*>(ws + p.lay.header);
   RowDesc* rows = reinterpret_cast<RowDesc*>(ws + p.lay.rows);
   ItemDesc* items = reinterpret_cast<ItemDesc*>(ws + p.lay.items);
-  int32_t* merge_rows = reinterpret_cast<int32_t*>(ws + p.lay.merge_rows);
+  MergeDesc* merge_rows = reinterpret_cast<MergeDesc*>(ws + p.lay.merge_rows);
   PrefillItem* pf = reinterpret_cast<PrefillItem*>(ws + p.lay.pf_items);
 
   const int num_seqs = min(max(p.dist[0] + p.dist[1] + p.dist[2], 0), p.max_num_seqs);
@@ -82,6 +87,11 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
       q0 = p.qsl[s];
       q_len = p.qsl[s + 1] - q0;
       ctx = p.kv_lens[s] - q_len;
+      if (cached) {
+        s_q0[s] = q0;
+        s_ctx[s] = ctx;
+        if (s == num_seqs - 1) s_q0[num_seqs] = q0 + q_len;
+      }
       if (q_len > 0) {
         if (q_len >= p.prefill_min_q) {
           n_pf = (q_len + kPrefillBQ - 1) / kPrefillBQ;
@@ -133,9 +143,15 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
     }
     seq = a;
     const int t = r - s_seq_rows[seq];
-    const int q0 = p.qsl[seq];
-    const int q_len = p.qsl[seq + 1] - q0;
-    const int pos = p.kv_lens[seq] - q_len + t;
+    int q0, pos;
+    if (cached) {
+      q0 = s_q0[seq];
+      pos = s_ctx[seq] + t;
+    } else {
+      q0 = p.qsl[seq];
+      const int q_len = p.qsl[seq + 1] - q0;
+      pos = p.kv_lens[seq] - q_len + t;
+    }
     token = q0 + t;
     hi = pos + 1;
     lo = (W > 0) ? max(0, pos - W + 1) : 0;
@@ -194,7 +210,14 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
         it.part = n_split > 1 ? my_part + j : -1;
         items[slot] = it;
       }
-      if (n_split > 1 && my_merge < p.lay.max_merge_rows) merge_rows[my_merge] = r;
+      if (n_split > 1 && my_merge < p.lay.max_merge_rows) {
+        MergeDesc md;
+        md.token = token;
+        md.part_base = my_part;
+        md.n_split = n_split;
+        md.pad = 0;
+        merge_rows[my_merge] = md;
+      }
     }
     full_base += tot_full;
     rem_base += tot_rem;

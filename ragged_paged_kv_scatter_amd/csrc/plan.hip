@@ -13,7 +13,7 @@ namespace {
 template <typename IN, typename C>
 __global__ __launch_bounds__(kPlanThreads) void prep_kernel(PlanParams pp, ScatterParams sp,
                                                             int tpw) {
-  extern __shared__ int32_t s_seq_rows[];           // [max_num_seqs + 1], planner only
+  extern __shared__ int32_t s_seq_rows[];           // planner tables (plan_lds_words)
   if (blockIdx.x == 0) plan_body(pp, s_seq_rows);
   else scatter_body<IN, C, kPlanThreads>(sp, tpw, blockIdx.x - 1);
 }
@@ -24,7 +24,7 @@ constexpr int kTargetScatterWGs = 256;
 
 hipError_t launch_prep(const PlanParams& pp, const ScatterParams* sp, rpa_dtype in_dt,
                        rpa_dtype cache_dt, hipStream_t s) {
-  const size_t lds = (size_t)(pp.max_num_seqs + 1) * sizeof(int32_t);
+  const size_t lds = (size_t)plan_lds_words(pp.max_num_seqs) * sizeof(int32_t);
   ScatterParams p = {};
   int tpw = 1;
   unsigned grid = 1;

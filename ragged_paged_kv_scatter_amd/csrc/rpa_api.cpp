@@ -154,7 +154,7 @@ Workspace workspace_layout(const rpa_desc& d) {
   w.items = off;
   off = align256(off + (size_t)w.max_items * sizeof(ItemDesc));
   w.merge_rows = off;
-  off = align256(off + (size_t)w.max_merge_rows * sizeof(int32_t));
+  off = align256(off + (size_t)w.max_merge_rows * sizeof(MergeDesc));
   w.pf_items = off;
   off = align256(off + (size_t)w.max_pf_items * sizeof(PrefillItem));
   w.part_ml = off;

@@ -22,6 +22,11 @@ constexpr int kTargetWaves = 16384;
 constexpr int kTargetItems = 2048;    // upper bound of kTargetWaves / Hkv used for sizing
 constexpr int kMinSplit = 128;        // never cut a row's KV range finer than this
 constexpr int kPlanThreads = 1024;    // the planner is one workgroup
+constexpr int kPlanCacheSeqs = 4000;  // planner keeps per-sequence data in LDS up to this (48 KB)
+// dynamic LDS words of the planner for max_num_seqs sequences
+inline int plan_lds_words(int max_num_seqs) {
+  return (max_num_seqs + 1) * (max_num_seqs <= kPlanCacheSeqs ? 3 : 1);
+}
 constexpr int kWavesPerWG = 4;        // row kernel: one item per wave
 constexpr int kPrefillBQ = 128;       // query tokens per prefill tile (4 waves x 32)
 
@@ -53,6 +58,13 @@ struct ItemDesc {        // a split of one row: keys [lo, hi)
   int32_t row;
   int32_t lo, hi;
   int32_t part;          // partial slot, or -1 when the row has a single split
+};
+
+struct MergeDesc {       // a row with more than one split, for the merge
+  int32_t token;         // row index into queries / out
+  int32_t part_base;     // its first partial slot
+  int32_t n_split;       // its number of partials
+  int32_t pad;
 };
 
 struct PrefillItem {     // a query tile of one prefill sequence
