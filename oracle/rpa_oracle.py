@@ -330,3 +330,56 @@ def written_slots(kv_lens, block_tables, query_start_loc, distribution, *, page_
         page, off = slot_of(block_tables, pages_per_seq, page_size, s, np.arange(ctx, kv_len))
         w[page, off] = True
     return w
+
+
+# ---------------------------------------------------------------------------
+# Slot-mapping form of the update, into split K / V caches
+# (vLLM differential_flash_attn.py: the metadata builder's "Compute slot
+# mapping" step, cuda-graph padding with PAD_SLOT_ID, and populate_kv_cache's
+# reshape_and_cache_flash call on kv_cache[0], kv_cache[1] with the flattened
+# slot mapping, the cache dtype and the k/v scales).  The pages show the calls
+# only; the readings taken (listed in the design doc): a slot is
+# block * block_size + offset of the token's position, rows past the last
+# sequence carry PAD_SLOT, and a store skips PAD_SLOT (and, as a guard, any
+# slot outside the pool).
+# ---------------------------------------------------------------------------
+
+PAD_SLOT = -1
+
+
+def slot_mapping(kv_lens, block_tables, query_start_loc, distribution, *, page_size,
+                 pages_per_seq, total_tokens):
+    """int64 [total_tokens]: flat cache slot of every new token row, the same
+    (page, offset) the combined-layout update writes; PAD_SLOT for rows past
+    the last valid sequence."""
+    out = np.full(total_tokens, PAD_SLOT, dtype=np.int64)
+    for s in range(num_seqs_of(distribution)):
+        q0, q_len, ctx, _ = seq_bounds(query_start_loc, kv_lens, s)
+        if q_len == 0:
+            continue
+        page, off = slot_of(block_tables, pages_per_seq, page_size, s, ctx + np.arange(q_len))
+        out[q0:q0 + q_len] = page.astype(np.int64) * page_size + off
+    return out
+
+
+def reshape_and_cache(key_cache_bits, value_cache_bits, keys_bits, values_bits, slots, *,
+                      kv_in_dtype, cache_dtype, k_scale=0.0, v_scale=0.0):
+    """Copies of the split caches ([num_blocks, block_size, Hkv, Dpad] each)
+    with token i's K row (all heads) stored at flat slot slots[i] of the key
+    cache and its V row in the value cache, lanes [D, Dpad) zero.  Tokens whose
+    slot is negative or past the pool are skipped; nothing else changes."""
+    kc = np.array(key_cache_bits, copy=True)
+    vc = np.array(value_cache_bits, copy=True)
+    nb, bs, _, _ = kc.shape
+    D = keys_bits.shape[2]
+    k = encode_for_cache(keys_bits, kv_in_dtype, cache_dtype, k_scale)
+    v = encode_for_cache(values_bits, kv_in_dtype, cache_dtype, v_scale)
+    for i, sl in enumerate(np.asarray(slots, dtype=np.int64)):
+        if sl < 0 or sl >= nb * bs:
+            continue
+        b, o = divmod(int(sl), bs)
+        kc[b, o] = 0
+        kc[b, o, :, :D] = k[i]
+        vc[b, o] = 0
+        vc[b, o, :, :D] = v[i]
+    return kc, vc

@@ -5,7 +5,7 @@ import types
 
 import pytest
 
-from tests import helpers, test_fp8_codec, test_oracle
+from tests import helpers, test_fp8_codec, test_oracle, test_oracle_slots
 
 SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle", "rpa_oracle.py")
 SRC = open(SRC_PATH).read()
@@ -43,6 +43,13 @@ MUTANTS = [
     ("subnormal_scale", "return s * (m / 8.0) * 2.0 ** -6", "return s * (m / 8.0) * 2.0 ** -7"),
     ("bf16_shift", "(bits.astype(np.uint32) << np.uint32(16))",
      "(bits.astype(np.uint32) << np.uint32(15))"),
+    ("slot_offset_dropped", "out[q0:q0 + q_len] = page.astype(np.int64) * page_size + off",
+     "out[q0:q0 + q_len] = page.astype(np.int64) * page_size"),
+    ("padding_rows_get_slot_0", "out = np.full(total_tokens, PAD_SLOT, dtype=np.int64)",
+     "out = np.zeros(total_tokens, dtype=np.int64)"),
+    ("split_v_gets_k", "vc[b, o, :, :D] = v[i]", "vc[b, o, :, :D] = k[i]"),
+    ("pad_slot_stored", "if sl < 0 or sl >= nb * bs:", "if sl >= nb * bs:"),
+    ("split_pad_lanes_kept", "        kc[b, o] = 0\n", ""),
 ]
 
 T = test_oracle
@@ -69,6 +76,9 @@ PINS = [
     test_fp8_codec.test_decode_all_codes_match_torch,
     test_fp8_codec.test_closed_forms,
     test_fp8_codec.test_encode_every_bf16_pattern_matches_torch,
+    test_oracle_slots.test_slot_mapping_matches_hand_derived_slots,
+    lambda: test_oracle_slots.test_split_update_equals_combined_update("mixed_bf16"),
+    test_oracle_slots.test_pad_and_out_of_pool_slots_are_skipped,
 ]
 
 
@@ -82,7 +92,7 @@ def load(old, new):
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_mutant_is_caught(name, old, new, monkeypatch):
     mod = load(old, new)
-    for m in (helpers, test_oracle, test_fp8_codec):
+    for m in (helpers, test_oracle, test_fp8_codec, test_oracle_slots):
         monkeypatch.setattr(m, "O", mod)
     caught = 0
     for pin in PINS:
@@ -95,7 +105,7 @@ def test_mutant_is_caught(name, old, new, monkeypatch):
 
 def test_unmutated_source_passes_all_pins(monkeypatch):
     mod = load("import math\n", "import math\n")
-    for m in (helpers, test_oracle, test_fp8_codec):
+    for m in (helpers, test_oracle, test_fp8_codec, test_oracle_slots):
         monkeypatch.setattr(m, "O", mod)
     for pin in PINS:
         pin()
