@@ -164,12 +164,90 @@ def summarize_counters(workload, kernel, fetch_csv, write_csv, copy_bytes):
     print(json.dumps(out, indent=1))
 
 
+def bench_reshape_and_cache(args, w, dev):
+    """One step = rpa_slot_mapping + rpa_reshape_and_cache of the workload's new
+    tokens into split K / V caches ([num_pages, page_size, Hkv, Dpad] each).
+    Algorithmic bytes: the new K and V rows read once and stored once."""
+    import torch
+
+    import ragged_paged_kv_scatter_amd as rpa
+    from oracle import rpa_oracle as O
+    from tests.helpers import bits
+
+    meta = {k: torch.from_numpy(np.ascontiguousarray(getattr(w, k))).to(dev)
+            for k in ("kv_lens", "block_tables", "query_start_loc", "distribution")}
+    kc = w.kv_cache[:, :, 0::2, :].contiguous()
+    vc = w.kv_cache[:, :, 1::2, :].contiguous()
+    slots = torch.empty(w.total_tokens, dtype=torch.int64, device=dev)
+
+    def step():
+        rpa.rpa_slot_mapping(meta["kv_lens"], meta["block_tables"], meta["query_start_loc"],
+                             meta["distribution"], page_size=w.page_size,
+                             total_tokens=w.total_tokens, out=slots)
+        rpa.rpa_reshape_and_cache(w.keys, w.values, kc, vc, slots, k_scale=w.k_scale,
+                                  v_scale=w.v_scale)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    rpa.profile_enable(True)
+    rpa.profile_read()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    rpa.profile_enable(False)
+    kstats = rpa.profile_read()
+    ms = (t1 - t0) * 1e3 / args.steps
+    n_valid = int(w.query_start_loc[w.num_seqs])
+    in_b = 2 * n_valid * w.num_kv_heads * w.head_dim * ELEM[w.kv_in_dtype]
+    out_b = 2 * n_valid * w.num_kv_heads * w.head_dim_padded * ELEM[w.cache_dtype]
+    nbytes = in_b + out_b
+    n, kms = kstats.get("reshape_and_cache", (1, 0.0))
+    kavg = kms / max(n, 1)
+    achieved = nbytes / (kavg * 1e-3) / 1e9
+    line = {
+        "metric": "slot-mapping KV store GB/s (new K/V read + split-cache rows written)",
+        "value": nbytes / (ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.cache_dtype, "data": "synthetic",
+        "config": {"workload": w.name, "op": "reshape_and_cache", "token_rows": n_valid,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "kv_in_dtype": w.kv_in_dtype, "cache_dtype": w.cache_dtype,
+                   "bytes": nbytes, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "reshape_and_cache", "kernel_avg_ms": kavg},
+        "kernels_ms": {k: v[1] / max(v[0], 1) for k, v in kstats.items()},
+    }
+    if not args.no_cpu_baseline:
+        kb, vb = bits(w.keys, w.kv_in_dtype), bits(w.values, w.kv_in_dtype)
+        kcb, vcb = bits(kc, w.cache_dtype), bits(vc, w.cache_dtype)
+        sl = O.slot_mapping(w.kv_lens, w.block_tables, w.query_start_loc, w.distribution,
+                            page_size=w.page_size, pages_per_seq=w.pages_per_seq,
+                            total_tokens=w.total_tokens)
+        rows = min(n_valid, 4096)
+        t0 = time.perf_counter()
+        O.reshape_and_cache(kcb, vcb, kb[:rows], vb[:rows], sl[:rows], kv_in_dtype=w.kv_in_dtype,
+                            cache_dtype=w.cache_dtype, k_scale=w.k_scale, v_scale=w.v_scale)
+        secs = time.perf_counter() - t0
+        line["cpu_baseline"] = dict(value=nbytes * rows / n_valid / secs / 1e9, unit="GB/s",
+                                    cores=1, kind="oracle",
+                                    sample=f"{rows} of {n_valid} token rows, {secs:.1f} s on "
+                                           "the host (cache copies included)")
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_bf16")
+    ap.add_argument("--op", default="forward", choices=["forward", "reshape_and_cache"],
+                    help="forward: the whole step (default); reshape_and_cache: the update's "
+                         "slot-mapping form into split K/V caches, at the workload's token count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -194,6 +272,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = W.make(args.workload, device=dev)
+    if args.op == "reshape_and_cache":
+        bench_reshape_and_cache(args, w, dev)
+        return
     meta = {k: torch.from_numpy(np.ascontiguousarray(getattr(w, k))).to(dev)
             for k in ("kv_lens", "block_tables", "query_start_loc", "distribution")}
     out = torch.empty(w.queries.shape, dtype=w.queries.dtype, device=dev)

@@ -132,6 +132,41 @@ int rpa_update_kv_cache(const rpa_desc* desc, const void* keys, const void* valu
                         const int32_t* query_start_loc, const int32_t* distribution,
                         float k_scale, float v_scale, void* stream);
 
+/* Flat cache slot of every new token row: the slot mapping of the update's
+ * split-cache form (vLLM differential_flash_attn.py, the metadata builder's
+ * "Compute slot mapping" step and its PAD_SLOT_ID padding).  For every valid
+ * sequence s and t < q_len, with pos = kv_len - q_len + t:
+ *   slot_mapping[qsl[s] + t] = block_tables[s*pages_per_seq + pos/page_size] * page_size
+ *                              + pos % page_size,
+ * the same (page, offset) rpa_update_kv_cache writes.  Rows qsl[num_seqs] ..
+ * total_tokens-1 get -1 (padding).  slot_mapping is int64[total_tokens] in
+ * device memory.  Uses total_tokens, max_num_seqs, pages_per_seq and
+ * page_size of desc; the other fields are checked as for the other calls.
+ * Returns RPA_OK or an error code. */
+int rpa_slot_mapping(const rpa_desc* desc, const int32_t* kv_lens, const int32_t* block_tables,
+                     const int32_t* query_start_loc, const int32_t* distribution,
+                     int64_t* slot_mapping, void* stream);
+
+/* The update in its slot-mapping form, into split K and V caches (vLLM
+ * differential_flash_attn.py, populate_kv_cache: reshape_and_cache_flash on
+ * kv_cache[0] and kv_cache[1] with the flattened slot mapping, the cache dtype
+ * and the k/v scales).
+ *   key_cache, value_cache  [num_pages, page_size, num_kv_heads, head_dim_padded]
+ *                           in cache_dtype (num_pages = blocks, page_size = block size)
+ *   keys, values            [total_tokens, num_kv_heads, head_dim] in kv_in_dtype
+ *   slot_mapping            int64[total_tokens]
+ * For every row i with 0 <= slot = slot_mapping[i] < num_pages*page_size and
+ * every kv head h:
+ *   key_cache  [slot/page_size][slot%page_size][h][0:head_dim] = encode(keys  [i][h][:], k_scale)
+ *   value_cache[slot/page_size][slot%page_size][h][0:head_dim] = encode(values[i][h][:], v_scale)
+ *   lanes [head_dim, head_dim_padded) of both rows = 0.
+ * Rows with any other slot (-1 padding, or past the pool) are skipped, and no
+ * other byte changes.  encode() is the one of rpa_update_kv_cache.  Slots of
+ * one call must be distinct.  Returns RPA_OK or an error code. */
+int rpa_reshape_and_cache(const rpa_desc* desc, const void* keys, const void* values,
+                          void* key_cache, void* value_cache, const int64_t* slot_mapping,
+                          float k_scale, float v_scale, void* stream);
+
 /* Bytes of device workspace rpa_forward needs for these sizes and options
  * (plan, work lists and split-KV partial results).  Writes *bytes; returns a
  * status code (the same host checks rpa_forward makes). */

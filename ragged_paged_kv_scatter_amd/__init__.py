@@ -17,8 +17,8 @@ import torch
 from . import _lib
 from ._lib import RpaDesc, RpaError, RpaKernelStat, RpaOptions
 
-__all__ = ["rpa_update_kv_cache", "rpa_forward", "rpa_workspace_bytes", "profile_enable",
-           "profile_read", "RpaError"]
+__all__ = ["rpa_update_kv_cache", "rpa_forward", "rpa_workspace_bytes", "rpa_slot_mapping",
+           "rpa_reshape_and_cache", "profile_enable", "profile_read", "RpaError"]
 
 _DT = {torch.float32: _lib.RPA_F32, torch.bfloat16: _lib.RPA_BF16, torch.uint8: _lib.RPA_FP8_E4M3,
        torch.float8_e4m3fn: _lib.RPA_FP8_E4M3}
@@ -122,6 +122,69 @@ def rpa_update_kv_cache(keys, values, kv_cache, kv_lens, block_tables, query_sta
         _ptr(block_tables), _ptr(query_start_loc), _ptr(distribution),
         float(k_scale or 0.0), float(v_scale or 0.0), _stream(dev)))
     return kv_cache
+
+
+def _flat_desc(total_tokens, max_num_seqs, pages_per_seq, num_pages, page_size, num_kv_heads,
+               head_dim, head_dim_padded, kv_in_dtype, cache_dtype):
+    d = RpaDesc()
+    d.total_tokens, d.max_num_seqs, d.pages_per_seq, d.num_pages, d.page_size = \
+        total_tokens, max_num_seqs, pages_per_seq, num_pages, page_size
+    d.num_q_heads, d.num_kv_heads, d.head_dim, d.head_dim_padded = \
+        num_kv_heads, num_kv_heads, head_dim, head_dim_padded
+    d.q_dtype = _lib.RPA_F32 if kv_in_dtype == _lib.RPA_F32 else _lib.RPA_BF16
+    d.kv_in_dtype, d.cache_dtype = kv_in_dtype, cache_dtype
+    return d
+
+
+def rpa_slot_mapping(kv_lens, block_tables, query_start_loc, distribution, *, page_size,
+                     total_tokens, out=None):
+    """Flat cache slot (int64 [total_tokens]) of every new token row; -1 for rows
+    past the last sequence."""
+    dev = _check_dev(kv_lens, block_tables, query_start_loc, distribution, out)
+    for t, n in ((kv_lens, "kv_lens"), (block_tables, "block_tables"),
+                 (query_start_loc, "query_start_loc"), (distribution, "distribution")):
+        _meta(t, n)
+    max_num_seqs = kv_lens.shape[0]
+    if block_tables.numel() % max(max_num_seqs, 1):
+        raise ValueError("block_tables must hold max_num_seqs * pages_per_seq entries")
+    pps = block_tables.numel() // max(max_num_seqs, 1)
+    if out is None:
+        out = torch.empty(total_tokens, dtype=torch.int64, device=dev)
+    if out.dtype != torch.int64 or out.numel() != total_tokens or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int64 tensor of total_tokens entries")
+    # only the sequence geometry is used; the head geometry is a valid placeholder
+    d = _flat_desc(total_tokens, max_num_seqs, pps, 1, page_size, 1, 64, 64,
+                   _lib.RPA_F32, _lib.RPA_F32)
+    _lib.check(_lib.load().rpa_slot_mapping(
+        ctypes.byref(d), _ptr(kv_lens), _ptr(block_tables), _ptr(query_start_loc),
+        _ptr(distribution), _ptr(out), _stream(dev)))
+    return out
+
+
+def rpa_reshape_and_cache(keys, values, key_cache, value_cache, slot_mapping, *, k_scale=None,
+                          v_scale=None):
+    """Store new K / V rows ([T, Hkv, D]) into split caches ([num_blocks, block_size,
+    Hkv, Dpad]) at their flat slots, in place; slots outside the pool (-1
+    padding) are skipped.  Returns ``(key_cache, value_cache)``."""
+    dev = _check_dev(keys, values, key_cache, value_cache, slot_mapping)
+    T, Hkv, D = keys.shape
+    if tuple(values.shape) != (T, Hkv, D):
+        raise ValueError("values must have the shape of keys")
+    if key_cache.dim() != 4 or tuple(value_cache.shape) != tuple(key_cache.shape):
+        raise ValueError("key_cache / value_cache must both be [num_blocks, block_size, Hkv, Dpad]")
+    nb, bs, hc, dp = key_cache.shape
+    if hc != Hkv or key_cache.dtype != value_cache.dtype:
+        raise ValueError("cache head count or dtype does not match")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must be int64 with one entry per token row")
+    for t in (keys, values, key_cache, value_cache, slot_mapping):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    d = _flat_desc(T, 1, 1, nb, bs, Hkv, D, dp, _dtype(keys), _dtype(key_cache))
+    _lib.check(_lib.load().rpa_reshape_and_cache(
+        ctypes.byref(d), _ptr(keys), _ptr(values), _ptr(key_cache), _ptr(value_cache),
+        _ptr(slot_mapping), float(k_scale or 0.0), float(v_scale or 0.0), _stream(dev)))
+    return key_cache, value_cache
 
 
 def rpa_workspace_bytes(desc: RpaDesc, opts: RpaOptions) -> int:

@@ -13,7 +13,8 @@ STATUS = {0: "RPA_OK", 1: "RPA_ERR_NULL_POINTER", 2: "RPA_ERR_INVALID_SHAPE",
           3: "RPA_ERR_UNSUPPORTED", 4: "RPA_ERR_INVALID_OPTION", 5: "RPA_ERR_WORKSPACE",
           6: "RPA_ERR_HIP"}
 EXPORTS = ("rpa_update_kv_cache", "rpa_workspace_bytes", "rpa_forward", "rpa_error_string",
-           "rpa_profile_enable", "rpa_profile_read")
+           "rpa_profile_enable", "rpa_profile_read", "rpa_slot_mapping",
+           "rpa_reshape_and_cache")
 
 
 class RpaDesc(ctypes.Structure):
@@ -77,6 +78,11 @@ def load():
     lib.rpa_profile_enable.restype = ctypes.c_int
     lib.rpa_profile_read.argtypes = [ctypes.POINTER(RpaKernelStat), ctypes.c_int]
     lib.rpa_profile_read.restype = ctypes.c_int
+    lib.rpa_slot_mapping.argtypes = [ctypes.POINTER(RpaDesc), P, P, P, P, P, P]
+    lib.rpa_slot_mapping.restype = ctypes.c_int
+    lib.rpa_reshape_and_cache.argtypes = [ctypes.POINTER(RpaDesc), P, P, P, P, P,
+                                          ctypes.c_float, ctypes.c_float, P]
+    lib.rpa_reshape_and_cache.restype = ctypes.c_int
     del I32P
     _lib = lib
     return lib

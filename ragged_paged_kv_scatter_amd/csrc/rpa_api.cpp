@@ -217,6 +217,63 @@ int rpa_update_kv_cache(const rpa_desc* desc, const void* keys, const void* valu
   return e == hipSuccess ? RPA_OK : hip_fail(e);
 }
 
+int rpa_slot_mapping(const rpa_desc* desc, const int32_t* kv_lens, const int32_t* block_tables,
+                     const int32_t* query_start_loc, const int32_t* distribution,
+                     int64_t* slot_mapping, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (!slot_mapping) return RPA_ERR_NULL_POINTER;
+  if ((st = check_meta(kv_lens, block_tables, query_start_loc, distribution))) return st;
+  if (desc->total_tokens == 0) return RPA_OK;
+  SlotMapParams p = {};
+  p.kv_lens = kv_lens;
+  p.block_tables = block_tables;
+  p.qsl = query_start_loc;
+  p.dist = distribution;
+  p.slots = slot_mapping;
+  p.T = desc->total_tokens;
+  p.max_num_seqs = desc->max_num_seqs;
+  p.pps = desc->pages_per_seq;
+  p.page_size = desc->page_size;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  prof_begin("slot_mapping", s);
+  hipError_t e = launch_slot_mapping(p, s);
+  prof_end(s);
+  return e == hipSuccess ? RPA_OK : hip_fail(e);
+}
+
+int rpa_reshape_and_cache(const rpa_desc* desc, const void* keys, const void* values,
+                          void* key_cache, void* value_cache, const int64_t* slot_mapping,
+                          float k_scale, float v_scale, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (!keys || !values || !key_cache || !value_cache || !slot_mapping)
+    return RPA_ERR_NULL_POINTER;
+  if (!finite_nonneg(k_scale) || !finite_nonneg(v_scale)) return RPA_ERR_INVALID_OPTION;
+  if (!aligned16(keys) || !aligned16(values) || !aligned16(key_cache) || !aligned16(value_cache))
+    return RPA_ERR_INVALID_SHAPE;
+  if (desc->total_tokens == 0) return RPA_OK;
+  ReshapeParams p = {};
+  p.keys = keys;
+  p.values = values;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.slots = slot_mapping;
+  p.num_slots = (int64_t)desc->num_pages * desc->page_size;
+  p.T = desc->total_tokens;
+  p.Hkv = desc->num_kv_heads;
+  p.D = desc->head_dim;
+  p.Dpad = desc->head_dim_padded;
+  p.k_scale = k_scale > 0.f ? k_scale : 1.f;
+  p.v_scale = v_scale > 0.f ? v_scale : 1.f;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  prof_begin("reshape_and_cache", s);
+  hipError_t e = launch_reshape_and_cache(p, (rpa_dtype)desc->kv_in_dtype,
+                                          (rpa_dtype)desc->cache_dtype, s);
+  prof_end(s);
+  return e == hipSuccess ? RPA_OK : hip_fail(e);
+}
+
 int rpa_workspace_bytes(const rpa_desc* desc, const rpa_options* opts, size_t* bytes) {
   int st = check_desc(desc);
   if (st) return st;

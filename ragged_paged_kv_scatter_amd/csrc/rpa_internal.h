@@ -101,6 +101,26 @@ struct ScatterParams {
   float inv_k_scale_src, inv_v_scale_src;  // the scales themselves (division done in-kernel)
 };
 
+struct SlotMapParams {    // flat slot of each new token row
+  const int32_t* kv_lens;
+  const int32_t* block_tables;
+  const int32_t* qsl;
+  const int32_t* dist;
+  int64_t* slots;
+  int32_t T, max_num_seqs, pps, page_size;
+};
+
+struct ReshapeParams {    // new K / V rows into split caches by flat slot
+  const void* keys;
+  const void* values;
+  void* key_cache;
+  void* value_cache;
+  const int64_t* slots;
+  int64_t num_slots;      // num_blocks * block_size; slots outside [0, num_slots) are skipped
+  int32_t T, Hkv, D, Dpad;
+  float k_scale, v_scale;  // 1 when none
+};
+
 struct PlanParams {
   const int32_t* kv_lens;
   const int32_t* qsl;
@@ -139,6 +159,9 @@ hipError_t launch_merge(const AttnParams& p, rpa_dtype q_dt, hipStream_t s);
 hipError_t launch_prefill(const AttnParams& p, rpa_dtype q_dt, rpa_dtype cache_dt,
                           hipStream_t s);
 bool prefill_supported(const rpa_desc& d);
+hipError_t launch_slot_mapping(const SlotMapParams& p, hipStream_t s);
+hipError_t launch_reshape_and_cache(const ReshapeParams& p, rpa_dtype in_dt, rpa_dtype cache_dt,
+                                    hipStream_t s);
 
 // Profiling hooks used by the launchers' caller.
 void prof_begin(const char* name, hipStream_t s);

@@ -30,6 +30,32 @@ __device__ __forceinline__ int find_seq(const int32_t* qsl, int num_seqs, int to
   return lo;
 }
 
+// 16 bytes of cache elements from new K or V elements at src: a bit copy, or
+// for an e4m3 cache fed with bf16, x / scale in float32 (IEEE RNE) encoded to
+// the nearest e4m3fn code (clamped to +-448, ties to even).
+template <typename IN, typename C>
+__device__ __forceinline__ uint4 encode_chunk(const IN* src, float scale) {
+  if constexpr (sizeof(IN) == sizeof(C)) {
+    return *reinterpret_cast<const uint4*>(src);
+  } else {
+    // bf16 -> e4m3: 16 inputs (32 bytes) -> 16 codes
+    static_assert(sizeof(IN) == 2 && sizeof(C) == 1, "only bf16 -> e4m3 converts");
+    const uint4 a = reinterpret_cast<const uint4*>(src)[0];
+    const uint4 b = reinterpret_cast<const uint4*>(src)[1];
+    const uint32_t wds[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t packed[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t c0 = f32_to_e4m3(__fdiv_rn(bf16lo(wds[2 * k]), scale));
+      const uint32_t c1 = f32_to_e4m3(__fdiv_rn(bf16hi(wds[2 * k]), scale));
+      const uint32_t c2 = f32_to_e4m3(__fdiv_rn(bf16lo(wds[2 * k + 1]), scale));
+      const uint32_t c3 = f32_to_e4m3(__fdiv_rn(bf16hi(wds[2 * k + 1]), scale));
+      packed[k] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    }
+    return make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  }
+}
+
 // IN: element type of keys/values; C: element type of the cache.
 constexpr int kSeqsInLds = 1024;   // query_start_loc is searched in LDS up to this many seqs
 
@@ -83,26 +109,7 @@ __device__ __forceinline__ void scatter_body(const ScatterParams& p, int tpw, in
     uint4 outv = make_uint4(0, 0, 0, 0);
     if (d0 < p.D) {                                // D * ESZ % 16 == 0: chunk all in or all pad
       const IN* src = ((ch & 1) ? values : keys) + (tok * p.Hkv + h) * p.D + d0;
-      if constexpr (sizeof(IN) == sizeof(C)) {
-        outv = *reinterpret_cast<const uint4*>(src);
-      } else {
-        // bf16 -> e4m3: 16 inputs (32 bytes) -> 16 codes
-        static_assert(sizeof(IN) == 2 && sizeof(C) == 1, "only bf16 -> e4m3 converts");
-        const float scale = (ch & 1) ? p.inv_v_scale_src : p.inv_k_scale_src;
-        const uint4 a = reinterpret_cast<const uint4*>(src)[0];
-        const uint4 b = reinterpret_cast<const uint4*>(src)[1];
-        const uint32_t wds[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        uint32_t packed[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t c0 = f32_to_e4m3(__fdiv_rn(bf16lo(wds[2 * k]), scale));
-          const uint32_t c1 = f32_to_e4m3(__fdiv_rn(bf16hi(wds[2 * k]), scale));
-          const uint32_t c2 = f32_to_e4m3(__fdiv_rn(bf16lo(wds[2 * k + 1]), scale));
-          const uint32_t c3 = f32_to_e4m3(__fdiv_rn(bf16hi(wds[2 * k + 1]), scale));
-          packed[k] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
-        }
-        outv = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-      }
+      outv = encode_chunk<IN, C>(src, (ch & 1) ? p.inv_v_scale_src : p.inv_k_scale_src);
     }
     C* dst = cache + (row * (2 * p.Hkv) + ch) * p.Dpad + d0;
     *reinterpret_cast<uint4*>(dst) = outv;
@@ -111,6 +118,9 @@ __device__ __forceinline__ void scatter_body(const ScatterParams& p, int tpw, in
 
 }  // namespace scatter_detail
 
+using scatter_detail::Elem;
+using scatter_detail::encode_chunk;
+using scatter_detail::find_seq;
 using scatter_detail::kScatterRowsMax;
 using scatter_detail::scatter_body;
 

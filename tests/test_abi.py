@@ -26,7 +26,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"rpa_update_kv_cache", "rpa_forward", "rpa_workspace_bytes",
-                          "rpa_error_string"}
+                          "rpa_error_string", "rpa_slot_mapping", "rpa_reshape_and_cache"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -111,6 +111,26 @@ def test_null_and_workspace_errors_do_not_launch(lib):
                                    float("nan"), 1.0, None) == 4
     assert lib.rpa_update_kv_cache(None, fake, fake, fake, fake, fake, fake, fake, 1.0, 1.0,
                                    None) == 1
+
+
+def test_split_cache_calls_check_before_launch(lib):
+    d = good_desc()
+    fake = ctypes.c_void_p(4096)   # never dereferenced: every call below fails host checks
+    # slot mapping: NULL output, NULL metadata, bad page size
+    assert lib.rpa_slot_mapping(ctypes.byref(d), fake, fake, fake, fake, None, None) == 1
+    assert lib.rpa_slot_mapping(ctypes.byref(d), None, fake, fake, fake, fake, None) == 1
+    assert lib.rpa_slot_mapping(ctypes.byref(good_desc(page_size=24)), fake, fake, fake, fake,
+                                fake, None) == 3
+    # reshape_and_cache: NULL cache, bad scale, misaligned keys, unsupported dtype pair
+    assert lib.rpa_reshape_and_cache(ctypes.byref(d), fake, fake, None, fake, fake, 1.0, 1.0,
+                                     None) == 1
+    assert lib.rpa_reshape_and_cache(ctypes.byref(d), fake, fake, fake, fake, fake, -1.0, 1.0,
+                                     None) == 4
+    assert lib.rpa_reshape_and_cache(ctypes.byref(d), ctypes.c_void_p(4096 + 4), fake, fake, fake,
+                                     fake, 1.0, 1.0, None) == 2
+    bad = good_desc(kv_in_dtype=_lib.RPA_F32, cache_dtype=_lib.RPA_FP8_E4M3)
+    assert lib.rpa_reshape_and_cache(ctypes.byref(bad), fake, fake, fake, fake, fake, 1.0, 1.0,
+                                     None) == 3
 
 
 def test_error_strings(lib):
