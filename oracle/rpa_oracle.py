@@ -383,3 +383,34 @@ def reshape_and_cache(key_cache_bits, value_cache_bits, keys_bits, values_bits, 
         vc[b, o] = 0
         vc[b, o, :, :D] = v[i]
     return kc, vc
+
+
+# ---------------------------------------------------------------------------
+# Block copies of the split caches (vLLM differential_flash_attn.py:
+# swap_blocks applies ops.swap_blocks to the K plane kv_cache[0] and the V
+# plane kv_cache[1] with one src_to_dst table; copy_blocks applies
+# ops.copy_blocks to the K and V planes of every layer's cache with one
+# src_to_dists table).  The pages show the calls only; the reading taken
+# (listed in the design doc): a table is int64 [n, 2] of (source block,
+# destination block) pairs and each pair copies one whole block, all of its
+# bytes; destinations are distinct and no destination is also a source.
+# ---------------------------------------------------------------------------
+
+def swap_blocks(src_cache, dst_cache, src_to_dst):
+    """Copy of dst_cache ([num_blocks, ...]) with block d replaced by block s of
+    src_cache for every (s, d) pair."""
+    out = np.array(dst_cache, copy=True)
+    for s, d in np.asarray(src_to_dst, dtype=np.int64).reshape(-1, 2):
+        out[d] = src_cache[s]
+    return out
+
+
+def copy_blocks(caches, src_to_dists):
+    """Copies of every cache in `caches` (each [num_blocks, ...]) with block d
+    replaced by block s of the same cache, for every (s, d) pair."""
+    out = [np.array(c, copy=True) for c in caches]
+    pairs = np.asarray(src_to_dists, dtype=np.int64).reshape(-1, 2)
+    for c, o in zip(caches, out):
+        for s, d in pairs:
+            o[d] = c[s]
+    return out

@@ -5,7 +5,8 @@ import types
 
 import pytest
 
-from tests import helpers, test_fp8_codec, test_oracle, test_oracle_slots
+from tests import (helpers, test_fp8_codec, test_oracle, test_oracle_blocks,
+                   test_oracle_slots)
 
 SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle", "rpa_oracle.py")
 SRC = open(SRC_PATH).read()
@@ -50,6 +51,8 @@ MUTANTS = [
     ("split_v_gets_k", "vc[b, o, :, :D] = v[i]", "vc[b, o, :, :D] = k[i]"),
     ("pad_slot_stored", "if sl < 0 or sl >= nb * bs:", "if sl >= nb * bs:"),
     ("split_pad_lanes_kept", "        kc[b, o] = 0\n", ""),
+    ("swap_direction", "out[d] = src_cache[s]", "out[s] = src_cache[d]"),
+    ("copy_reads_destination", "o[d] = c[s]", "o[d] = c[d]"),
 ]
 
 T = test_oracle
@@ -79,6 +82,8 @@ PINS = [
     test_oracle_slots.test_slot_mapping_matches_hand_derived_slots,
     lambda: test_oracle_slots.test_split_update_equals_combined_update("mixed_bf16"),
     test_oracle_slots.test_pad_and_out_of_pool_slots_are_skipped,
+    test_oracle_blocks.test_swap_blocks_hand_example,
+    test_oracle_blocks.test_copy_blocks_every_layer_same_pairs,
 ]
 
 
@@ -92,7 +97,7 @@ def load(old, new):
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_mutant_is_caught(name, old, new, monkeypatch):
     mod = load(old, new)
-    for m in (helpers, test_oracle, test_fp8_codec, test_oracle_slots):
+    for m in (helpers, test_oracle, test_fp8_codec, test_oracle_slots, test_oracle_blocks):
         monkeypatch.setattr(m, "O", mod)
     caught = 0
     for pin in PINS:
@@ -105,7 +110,7 @@ def test_mutant_is_caught(name, old, new, monkeypatch):
 
 def test_unmutated_source_passes_all_pins(monkeypatch):
     mod = load("import math\n", "import math\n")
-    for m in (helpers, test_oracle, test_fp8_codec, test_oracle_slots):
+    for m in (helpers, test_oracle, test_fp8_codec, test_oracle_slots, test_oracle_blocks):
         monkeypatch.setattr(m, "O", mod)
     for pin in PINS:
         pin()
