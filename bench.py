@@ -239,15 +239,83 @@ def bench_reshape_and_cache(args, w, dev):
     print(json.dumps(line), flush=True)
 
 
+def bench_copy_blocks(args, w, dev, num_blocks=8192, num_pairs=2048):
+    """One step = rpa_copy_blocks of num_pairs (source, destination) block pairs
+    in one layer's K and V caches of num_blocks blocks [page_size, Hkv, Dpad].
+    Algorithmic bytes: every copied block read once and written once."""
+    import torch
+
+    import ragged_paged_kv_scatter_amd as rpa
+    from oracle import rpa_oracle as O
+
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[w.cache_dtype]
+    shape = (num_blocks, w.page_size, w.num_kv_heads, w.head_dim_padded)
+    kc = torch.zeros(shape, dtype=dt, device=dev)
+    vc = torch.zeros(shape, dtype=dt, device=dev)
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(num_blocks)
+    pairs_np = np.stack([perm[:num_pairs], perm[num_pairs:2 * num_pairs]], 1).astype(np.int64)
+    pairs = torch.from_numpy(pairs_np).to(dev)
+
+    def step():
+        rpa.rpa_copy_blocks([kc], [vc], pairs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    rpa.profile_enable(True)
+    rpa.profile_read()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    rpa.profile_enable(False)
+    kstats = rpa.profile_read()
+    ms = (t1 - t0) * 1e3 / args.steps
+    block = kc[0].numel() * kc.element_size()
+    nbytes = 2 * 2 * num_pairs * block            # K and V planes, read + write
+    n, kms = kstats.get("copy_blocks", (1, 0.0))
+    kavg = kms / max(n, 1)
+    achieved = nbytes / (kavg * 1e-3) / 1e9
+    line = {
+        "metric": "block copy GB/s (copied K/V blocks read + written)",
+        "value": nbytes / (ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.cache_dtype, "data": "synthetic",
+        "config": {"workload": w.name, "op": "copy_blocks", "num_blocks": num_blocks,
+                   "pairs": num_pairs, "block_bytes": block, "bytes": nbytes,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "copy_blocks",
+                     "kernel_avg_ms": kavg},
+        "kernels_ms": {k: v[1] / max(v[0], 1) for k, v in kstats.items()},
+    }
+    if not args.no_cpu_baseline:
+        host = np.zeros((num_blocks,) + shape[1:], dtype=np.uint8 if dt == torch.uint8 else
+                        (np.uint16 if dt == torch.bfloat16 else np.uint32))
+        t0 = time.perf_counter()
+        O.copy_blocks([host, host], pairs_np)
+        secs = time.perf_counter() - t0
+        line["cpu_baseline"] = dict(value=nbytes / secs / 1e9, unit="GB/s", cores=1,
+                                    kind="oracle",
+                                    sample=f"all {num_pairs} pairs of both planes, {secs:.1f} s "
+                                           "on the host (whole-cache copies included)")
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_bf16")
-    ap.add_argument("--op", default="forward", choices=["forward", "reshape_and_cache"],
+    ap.add_argument("--op", default="forward",
+                    choices=["forward", "reshape_and_cache", "copy_blocks"],
                     help="forward: the whole step (default); reshape_and_cache: the update's "
-                         "slot-mapping form into split K/V caches, at the workload's token count")
+                         "slot-mapping form into split K/V caches, at the workload's token "
+                         "count; copy_blocks: 2048 block copies in 8192-block split caches of "
+                         "the workload's block shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -274,6 +342,9 @@ def main():
     w = W.make(args.workload, device=dev)
     if args.op == "reshape_and_cache":
         bench_reshape_and_cache(args, w, dev)
+        return
+    if args.op == "copy_blocks":
+        bench_copy_blocks(args, w, dev)
         return
     meta = {k: torch.from_numpy(np.ascontiguousarray(getattr(w, k))).to(dev)
             for k in ("kv_lens", "block_tables", "query_start_loc", "distribution")}

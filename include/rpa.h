@@ -167,6 +167,39 @@ int rpa_reshape_and_cache(const rpa_desc* desc, const void* keys, const void* va
                           void* key_cache, void* value_cache, const int64_t* slot_mapping,
                           float k_scale, float v_scale, void* stream);
 
+/* Block copies within split caches, for every layer (vLLM
+ * differential_flash_attn.py, copy_blocks: ops.copy_blocks on the K plane
+ * kv_cache[0] and the V plane kv_cache[1] of every layer's cache with one
+ * pair table).  For every layer l < num_layers and pair i < num_pairs with
+ * (s, d) = (src_to_dst[2i], src_to_dst[2i+1]):
+ *   key_caches[l] block d   = key_caches[l] block s
+ *   value_caches[l] block d = value_caches[l] block s
+ * A block is block_bytes bytes; a cache holds num_blocks of them.
+ *   key_caches, value_caches  HOST arrays of num_layers DEVICE pointers
+ *                             (16-byte aligned; num_layers <= 64)
+ *   src_to_dst                DEVICE int64[2 * num_pairs]
+ * Destinations must be distinct and none may also be a source (copies run
+ * in parallel).  Pairs with an index outside [0, num_blocks) are skipped.
+ * block_bytes must be a positive multiple of 16.  Returns RPA_OK or an
+ * error code. */
+int rpa_copy_blocks(void* const* key_caches, void* const* value_caches, int32_t num_layers,
+                    int64_t num_blocks, int64_t block_bytes, const int64_t* src_to_dst,
+                    int32_t num_pairs, void* stream);
+
+/* Block moves between two caches, e.g. device and pinned host memory for
+ * swapping (vLLM differential_flash_attn.py, swap_blocks: ops.swap_blocks on
+ * the K plane and the V plane with one src_to_dst table; call once per
+ * plane).  For every pair i: dst block src_to_dst[2i+1] = src block
+ * src_to_dst[2i], block_bytes bytes each, one async copy per pair on
+ * `stream`.  src_to_dst is a HOST int64[2 * num_pairs] (it drives the copies
+ * from the host).  Host memory must be pinned (hipHostMalloc) for the copies
+ * to be asynchronous.  Pairs outside [0, src_blocks) x [0, dst_blocks) are
+ * rejected with RPA_ERR_INVALID_SHAPE before any copy is enqueued.  Returns
+ * RPA_OK or an error code. */
+int rpa_swap_blocks(const void* src_cache, void* dst_cache, int64_t src_blocks,
+                    int64_t dst_blocks, int64_t block_bytes, const int64_t* src_to_dst,
+                    int32_t num_pairs, void* stream);
+
 /* Bytes of device workspace rpa_forward needs for these sizes and options
  * (plan, work lists and split-KV partial results).  Writes *bytes; returns a
  * status code (the same host checks rpa_forward makes). */

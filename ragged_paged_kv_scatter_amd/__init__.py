@@ -18,7 +18,8 @@ from . import _lib
 from ._lib import RpaDesc, RpaError, RpaKernelStat, RpaOptions
 
 __all__ = ["rpa_update_kv_cache", "rpa_forward", "rpa_workspace_bytes", "rpa_slot_mapping",
-           "rpa_reshape_and_cache", "profile_enable", "profile_read", "RpaError"]
+           "rpa_reshape_and_cache", "rpa_copy_blocks", "rpa_swap_blocks", "profile_enable",
+           "profile_read", "RpaError"]
 
 _DT = {torch.float32: _lib.RPA_F32, torch.bfloat16: _lib.RPA_BF16, torch.uint8: _lib.RPA_FP8_E4M3,
        torch.float8_e4m3fn: _lib.RPA_FP8_E4M3}
@@ -185,6 +186,54 @@ def rpa_reshape_and_cache(keys, values, key_cache, value_cache, slot_mapping, *,
         ctypes.byref(d), _ptr(keys), _ptr(values), _ptr(key_cache), _ptr(value_cache),
         _ptr(slot_mapping), float(k_scale or 0.0), float(v_scale or 0.0), _stream(dev)))
     return key_cache, value_cache
+
+
+def _block_bytes(cache):
+    if cache.dim() < 2 or not cache.is_contiguous():
+        raise ValueError("a cache must be a contiguous [num_blocks, ...] tensor")
+    return cache[0].numel() * cache.element_size()
+
+
+def rpa_copy_blocks(key_caches, value_caches, src_to_dst):
+    """For every layer's K and V cache ([num_blocks, ...] device tensors), copy
+    block d = block s for every (s, d) row of the device int64 table
+    ``src_to_dst`` ([n, 2]), in place."""
+    if len(key_caches) != len(value_caches) or not key_caches:
+        raise ValueError("one key cache and one value cache per layer")
+    dev = _check_dev(src_to_dst, *key_caches, *value_caches)
+    shape, bb = tuple(key_caches[0].shape), _block_bytes(key_caches[0])
+    for c in list(key_caches) + list(value_caches):
+        if tuple(c.shape) != shape or _block_bytes(c) != bb:
+            raise ValueError("all caches must share one shape and block size")
+    if src_to_dst.dtype != torch.int64 or src_to_dst.dim() != 2 or src_to_dst.shape[1] != 2:
+        raise ValueError("src_to_dst must be int64 [n, 2]")
+    pairs = src_to_dst.contiguous()
+    n = len(key_caches)
+    ks = (ctypes.c_void_p * n)(*[c.data_ptr() for c in key_caches])
+    vs = (ctypes.c_void_p * n)(*[c.data_ptr() for c in value_caches])
+    _lib.check(_lib.load().rpa_copy_blocks(ks, vs, n, shape[0], bb, _ptr(pairs), pairs.shape[0],
+                                           _stream(dev)))
+    return key_caches, value_caches
+
+
+def rpa_swap_blocks(src_cache, dst_cache, src_to_dst):
+    """dst block d = src block s for every (s, d) row of the host int64 table
+    ``src_to_dst`` ([n, 2]); either cache may live in pinned host memory.  One
+    plane per call (the K and the V plane are swapped by two calls)."""
+    if src_to_dst.is_cuda or src_to_dst.dtype != torch.int64 or src_to_dst.dim() != 2 \
+            or src_to_dst.shape[1] != 2:
+        raise ValueError("src_to_dst must be a host int64 [n, 2] tensor")
+    bb = _block_bytes(src_cache)
+    if _block_bytes(dst_cache) != bb:
+        raise ValueError("caches must share one block size")
+    dev = src_cache.device if src_cache.is_cuda else dst_cache.device
+    if not dev.type == "cuda":
+        raise ValueError("one of the caches must be on the GPU")
+    pairs = src_to_dst.contiguous()
+    _lib.check(_lib.load().rpa_swap_blocks(
+        _ptr(src_cache), _ptr(dst_cache), src_cache.shape[0], dst_cache.shape[0], bb,
+        ctypes.c_void_p(pairs.data_ptr()), pairs.shape[0], _stream(dev)))
+    return dst_cache
 
 
 def rpa_workspace_bytes(desc: RpaDesc, opts: RpaOptions) -> int:

@@ -274,6 +274,55 @@ int rpa_reshape_and_cache(const rpa_desc* desc, const void* keys, const void* va
   return e == hipSuccess ? RPA_OK : hip_fail(e);
 }
 
+int rpa_copy_blocks(void* const* key_caches, void* const* value_caches, int32_t num_layers,
+                    int64_t num_blocks, int64_t block_bytes, const int64_t* src_to_dst,
+                    int32_t num_pairs, void* stream) {
+  if (!key_caches || !value_caches || !src_to_dst) return RPA_ERR_NULL_POINTER;
+  if (num_layers < 0 || num_layers > kMaxCopyLayers || num_pairs < 0 || num_blocks <= 0 ||
+      block_bytes <= 0 || block_bytes % 16 != 0 || num_pairs > 65535)
+    return RPA_ERR_INVALID_SHAPE;
+  CopyBlocksParams p = {};
+  for (int l = 0; l < num_layers; ++l) {
+    if (!key_caches[l] || !value_caches[l]) return RPA_ERR_NULL_POINTER;
+    if (!aligned16(key_caches[l]) || !aligned16(value_caches[l])) return RPA_ERR_INVALID_SHAPE;
+    p.k[l] = key_caches[l];
+    p.v[l] = value_caches[l];
+  }
+  if (num_layers == 0 || num_pairs == 0) return RPA_OK;
+  p.pairs = src_to_dst;
+  p.num_blocks = num_blocks;
+  p.block_bytes = block_bytes;
+  p.num_layers = num_layers;
+  p.num_pairs = num_pairs;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  prof_begin("copy_blocks", s);
+  hipError_t e = launch_copy_blocks(p, s);
+  prof_end(s);
+  return e == hipSuccess ? RPA_OK : hip_fail(e);
+}
+
+int rpa_swap_blocks(const void* src_cache, void* dst_cache, int64_t src_blocks,
+                    int64_t dst_blocks, int64_t block_bytes, const int64_t* src_to_dst,
+                    int32_t num_pairs, void* stream) {
+  if (!src_cache || !dst_cache || (!src_to_dst && num_pairs > 0)) return RPA_ERR_NULL_POINTER;
+  if (num_pairs < 0 || src_blocks <= 0 || dst_blocks <= 0 || block_bytes <= 0)
+    return RPA_ERR_INVALID_SHAPE;
+  for (int32_t i = 0; i < num_pairs; ++i) {
+    const int64_t sb = src_to_dst[2 * i], db = src_to_dst[2 * i + 1];
+    if (sb < 0 || sb >= src_blocks || db < 0 || db >= dst_blocks) return RPA_ERR_INVALID_SHAPE;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const char* from = static_cast<const char*>(src_cache);
+  char* to = static_cast<char*>(dst_cache);
+  for (int32_t i = 0; i < num_pairs; ++i) {
+    const hipError_t e = hipMemcpyAsync(to + src_to_dst[2 * i + 1] * block_bytes,
+                                        from + src_to_dst[2 * i] * block_bytes,
+                                        (size_t)block_bytes, hipMemcpyDefault, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return RPA_OK;
+}
+
 int rpa_workspace_bytes(const rpa_desc* desc, const rpa_options* opts, size_t* bytes) {
   int st = check_desc(desc);
   if (st) return st;

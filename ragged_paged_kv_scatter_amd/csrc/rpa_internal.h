@@ -121,6 +121,16 @@ struct ReshapeParams {    // new K / V rows into split caches by flat slot
   float k_scale, v_scale;  // 1 when none
 };
 
+constexpr int kMaxCopyLayers = 64;
+
+struct CopyBlocksParams {   // block copies within the split caches of every layer
+  void* k[kMaxCopyLayers];
+  void* v[kMaxCopyLayers];
+  const int64_t* pairs;     // [num_pairs][2] = (source, destination)
+  int64_t num_blocks, block_bytes;
+  int32_t num_layers, num_pairs;
+};
+
 struct PlanParams {
   const int32_t* kv_lens;
   const int32_t* qsl;
@@ -160,6 +170,7 @@ hipError_t launch_prefill(const AttnParams& p, rpa_dtype q_dt, rpa_dtype cache_d
                           hipStream_t s);
 bool prefill_supported(const rpa_desc& d);
 hipError_t launch_slot_mapping(const SlotMapParams& p, hipStream_t s);
+hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t s);
 hipError_t launch_reshape_and_cache(const ReshapeParams& p, rpa_dtype in_dt, rpa_dtype cache_dt,
                                     hipStream_t s);
 

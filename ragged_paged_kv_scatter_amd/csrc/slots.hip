@@ -72,7 +72,26 @@ __global__ __launch_bounds__(kSlotThreads) void reshape_cache_kernel(ReshapePara
 
 constexpr int kTargetWGs = 1024;
 
+// One workgroup per (pair, layer, plane): 16-byte chunks of the block.
+__global__ __launch_bounds__(kSlotThreads) void copy_blocks_kernel(CopyBlocksParams p) {
+  const int pair = blockIdx.x;
+  const int layer = blockIdx.y >> 1, plane = blockIdx.y & 1;
+  const long long src = p.pairs[2 * pair], dst = p.pairs[2 * pair + 1];
+  if (src < 0 || src >= p.num_blocks || dst < 0 || dst >= p.num_blocks) return;
+  char* base = static_cast<char*>(plane ? p.v[layer] : p.k[layer]);
+  const uint4* from = reinterpret_cast<const uint4*>(base + src * p.block_bytes);
+  uint4* to = reinterpret_cast<uint4*>(base + dst * p.block_bytes);
+  const long long n = p.block_bytes / 16;
+  for (long long i = threadIdx.x; i < n; i += kSlotThreads) to[i] = from[i];
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t s) {
+  if (p.num_pairs <= 0 || p.num_layers <= 0) return hipSuccess;
+  copy_blocks_kernel<<<dim3(p.num_pairs, 2 * p.num_layers), kSlotThreads, 0, s>>>(p);
+  return hipGetLastError();
+}
 
 hipError_t launch_slot_mapping(const SlotMapParams& p, hipStream_t s) {
   if (p.T <= 0) return hipSuccess;

@@ -26,7 +26,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"rpa_update_kv_cache", "rpa_forward", "rpa_workspace_bytes",
-                          "rpa_error_string", "rpa_slot_mapping", "rpa_reshape_and_cache"}
+                          "rpa_error_string", "rpa_slot_mapping", "rpa_reshape_and_cache",
+                          "rpa_copy_blocks", "rpa_swap_blocks"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -131,6 +132,22 @@ def test_split_cache_calls_check_before_launch(lib):
     bad = good_desc(kv_in_dtype=_lib.RPA_F32, cache_dtype=_lib.RPA_FP8_E4M3)
     assert lib.rpa_reshape_and_cache(ctypes.byref(bad), fake, fake, fake, fake, fake, 1.0, 1.0,
                                      None) == 3
+
+
+def test_block_copy_calls_check_before_launch(lib):
+    fake = ctypes.c_void_p(4096)
+    arr = (ctypes.c_void_p * 2)(4096, 8192)
+    bad = (ctypes.c_void_p * 2)(4096, 4096 + 8)
+    PP = ctypes.POINTER(ctypes.c_void_p)
+    cast = lambda a: ctypes.cast(a, PP)
+    assert lib.rpa_copy_blocks(None, cast(arr), 2, 4, 64, fake, 1, None) == 1
+    assert lib.rpa_copy_blocks(cast(arr), cast(arr), 65, 4, 64, fake, 1, None) == 2
+    assert lib.rpa_copy_blocks(cast(arr), cast(arr), 2, 4, 60, fake, 1, None) == 2
+    assert lib.rpa_copy_blocks(cast(bad), cast(arr), 2, 4, 64, fake, 1, None) == 2
+    assert lib.rpa_copy_blocks(cast(arr), cast(arr), 2, 4, 64, fake, 0, None) == 0
+    pairs = (ctypes.c_int64 * 4)(0, 1, 3, 5)      # second pair: destination 5 >= 4 blocks
+    assert lib.rpa_swap_blocks(fake, fake, 4, 4, 64, pairs, 2, None) == 2
+    assert lib.rpa_swap_blocks(None, fake, 4, 4, 64, pairs, 1, None) == 1
 
 
 def test_error_strings(lib):
