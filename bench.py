@@ -239,6 +239,33 @@ def bench_reshape_and_cache(args, w, dev):
     print(json.dumps(line), flush=True)
 
 
+def graph_timing(args, step, dev, work, decode_like, unit):
+    """The same step captured once in a HIP graph and replayed: the launches
+    without the host's per-call work (rpa_forward's checks and its three
+    launch calls)."""
+    import torch
+
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    value = work / (ms * 1e-3) / (1e9 if decode_like else 1e12)
+    return dict(ms_per_step=ms, value=value, unit=unit)
+
+
 def bench_copy_blocks(args, w, dev, num_blocks=8192, num_pairs=2048):
     """One step = rpa_copy_blocks of num_pairs (source, destination) block pairs
     in one layer's K and V caches of num_blocks blocks [page_size, Hkv, Dpad].
@@ -317,6 +344,8 @@ def main():
                          "count; copy_blocks: 2048 block copies in 8192-block split caches of "
                          "the workload's block shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the step replayed from a captured HIP graph")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this size first (counter calibration)")
@@ -425,6 +454,12 @@ def main():
         "roofline": roof,
         "kernels_ms": {k: v[1] / max(v[0], 1) for k, v in kstats.items()},
     }
+    if not args.no_graph:
+        try:
+            line["graph"] = graph_timing(args, step, dev, kvb if decode_like else flops,
+                                         decode_like, unit)
+        except Exception as e:  # reported, never fatal: `value` is the eager step
+            line["graph"] = dict(error=str(e)[:200])
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, args.cpu_budget)
         if unit == "GB/s":
