@@ -1,0 +1,76 @@
+"""GPU parity over a sweep of shapes and options the named workloads do not
+reach: every supported dtype triple, head_dim 64 / 128 (with and without lane
+padding), group sizes 1 to 16, page sizes 16 to 128, sliding window, soft cap,
+sink and q / k / v scales, on batches mixing decode rows, prefill chunks of
+awkward lengths, a zero-length query and long contexts that split.  Each case
+compares rpa_forward with the oracle on NaN-poisoned caches, to the dtype's
+tolerance, and the updated cache bit for bit."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from ragged_paged_kv_scatter_amd import workloads as W
+from tests.helpers import bits, gpu_forward, oracle_forward, poison_unused, tolerance
+
+pytestmark = pytest.mark.gpu
+
+# label: (q, kv_in, cache, D, Dpad, Hq, Hkv, page_size, window, cap, sink, (q, k, v) scales)
+CASES = {
+    "f32_g1_d64_ps16": ("f32", "f32", "f32", 64, 64, 2, 2, 16, 0, 0.0, False, (0, 0, 0)),
+    "f32_g16_d128_ps32_window_sink": ("f32", "f32", "f32", 128, 128, 16, 1, 32, 40, 0.0, True,
+                                      (0, 0, 0)),
+    "bf16_g1_d128_ps64": ("bf16", "bf16", "bf16", 128, 128, 4, 4, 64, 0, 0.0, False, (0, 0, 0)),
+    "bf16_g2_d64_ps128_cap": ("bf16", "bf16", "bf16", 64, 64, 4, 2, 128, 0, 5.0, False,
+                              (0, 0, 0)),
+    "bf16_g8_d128_ps16_all": ("bf16", "bf16", "bf16", 128, 128, 16, 2, 16, 64, 8.0, True,
+                              (0, 0, 0)),
+    "bf16_g16_d64_ps32_padded": ("bf16", "bf16", "bf16", 64, 96, 16, 1, 32, 0, 0.0, True,
+                                 (0, 0, 0)),
+    "bf16_g4_d128_qscale": ("bf16", "bf16", "bf16", 128, 128, 8, 2, 16, 0, 0.0, False,
+                            (0.5, 0, 0)),
+    "fp8_g4_d128_ps16_scales": ("bf16", "bf16", "fp8", 128, 128, 8, 2, 16, 0, 0.0, False,
+                                (0, 0.07, 0.03)),
+    "fp8_g8_d64_ps64_window_cap": ("bf16", "bf16", "fp8", 64, 64, 16, 2, 64, 50, 10.0, True,
+                                   (0, 0.05, 0.05)),
+    "fp8in_g2_d128_ps32": ("bf16", "fp8", "fp8", 128, 128, 4, 2, 32, 0, 0.0, False,
+                           (0, 0.1, 0.2)),
+}
+
+
+def make_case(label, seed, device="cuda"):
+    (qd, kd, cd, D, dp, hq, hkv, ps, win, cap, sink, (qs, ks, vs)) = CASES[label]
+    rng = np.random.default_rng(seed)
+    # decode rows (one with a long context, split into several KV ranges), a
+    # zero-length query, then prefill chunks of awkward lengths over contexts
+    dec_kv = [int(rng.integers(1, 300)), 1400, int(rng.integers(300, 700))]
+    q_lens = [1, 1, 1, 0]
+    kv_lens = dec_kv + [int(rng.integers(1, 60))]
+    for q in (2, 17, 130, 257):
+        q_lens.append(q)
+        kv_lens.append(q + int(rng.integers(0, 300)))
+    return W.build(label, q_lens=q_lens, kv_lens=kv_lens, distribution=(3, 5, 0),
+                   num_q_heads=hq, num_kv_heads=hkv, head_dim=D, head_dim_padded=dp,
+                   page_size=ps, q_dtype=qd, kv_in_dtype=kd, cache_dtype=cd,
+                   softmax_scale=1 / math.sqrt(D), seed=seed, sliding_window=win,
+                   logits_soft_cap=cap, q_scale=qs, k_scale=ks, v_scale=vs, with_sink=sink,
+                   extra_seqs=1, extra_tokens=2, device=device, rng=rng)
+
+
+@pytest.mark.parametrize("label", list(CASES))
+def test_sweep_case_matches_oracle(label):
+    print(f"\n[case] sweep {label}", flush=True)
+    w = make_case(label, seed=7000 + list(CASES).index(label))
+    poison_unused(w)
+    before = bits(w.kv_cache, w.cache_dtype)
+    ref, ref_cache = oracle_forward(w, cache_bits=before)
+    out = gpu_forward(w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(w.kv_cache, w.cache_dtype), ref_cache)
+    n_valid = int(w.query_start_loc[w.num_seqs])
+    o = out[:n_valid].double().cpu().numpy()
+    err = np.abs(o - ref[:n_valid]).max()
+    print(f"[{label}] max_abs={err:.3e} tol={tolerance(w):.0e}", flush=True)
+    assert err <= tolerance(w)
+    assert torch.isnan(out[n_valid:].float()).all()
