@@ -45,6 +45,31 @@ __device__ __forceinline__ float swz(float v) {
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), PATTERN));
 }
 
+// v and its partner across lane bit K (4: 16-lane rows, 5: 32-lane halves)
+// from a permlane swap of v with itself, without a trip through LDS.  Lane by
+// lane the two outputs are {v, partner}: (v, partner) where bit K of the lane
+// is clear, (partner, v) where it is set.
+template <int K>
+__device__ __forceinline__ void swap_pair(float v, float& a, float& b) {
+  static_assert(K == 4 || K == 5, "rows or halves");
+  const uint32_t u = __float_as_uint(v);
+  if constexpr (K == 4) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  }
+}
+template <int K>
+__device__ __forceinline__ float partner_of(float v) {
+  float a, b;
+  swap_pair<K>(v, a, b);
+  return ((__lane_id() >> K) & 1) ? a : b;
+}
+
 // Partner value for a reduction step over lane bit K: any partner whose lane
 // id differs in bit K (and possibly lower bits) keeps a reduction complete, so
 // the cheap DPP mirrors serve bits 2 and 3 (lane ^ 7, lane ^ 15).
@@ -54,8 +79,7 @@ __device__ __forceinline__ float red_x(float v) {
   else if constexpr (K == 1) return dppf<0x4E>(v);   // quad_perm [2,3,0,1]
   else if constexpr (K == 2) return dppf<0x141>(v);  // row_half_mirror
   else if constexpr (K == 3) return dppf<0x140>(v);  // row_mirror
-  else if constexpr (K == 4) return swz<0x401F>(v);  // lane ^ 16
-  else return __shfl_xor(v, 32);
+  else return partner_of<K>(v);                       // lane ^ 16, lane ^ 32
 }
 // Exact partner lane ^ (1 << K) (values differ across the lower bits).
 template <int K>
@@ -64,8 +88,7 @@ __device__ __forceinline__ float xor_x(float v) {
   else if constexpr (K == 1) return dppf<0x4E>(v);
   else if constexpr (K == 2) return swz<0x101F>(v);  // lane ^ 4
   else if constexpr (K == 3) return dppf<0x128>(v);  // row_ror:8 == lane ^ 8 in a row
-  else if constexpr (K == 4) return swz<0x401F>(v);
-  else return __shfl_xor(v, 32);
+  else return partner_of<K>(v);
 }
 
 // Value of lane REP of this lane's aligned group of LPT lanes.
@@ -109,9 +132,15 @@ __device__ __forceinline__ void reduce_scatter(float* v, int lane) {
 }
 
 // max / sum over the token slots (lane bits B..5), exact partners
+// (over bits 4 and 5 the two swap outputs are {v, partner}: the op of the
+// two is v op partner in every lane, as the ops commute)
 template <int B>
 __device__ __forceinline__ float slots_max(float v) {
-  if constexpr (B <= 5) {
+  if constexpr (B >= 4 && B <= 5) {
+    float a, b;
+    swap_pair<B>(v, a, b);
+    return slots_max<B + 1>(fmaxf(a, b));
+  } else if constexpr (B <= 5) {
     v = fmaxf(v, xor_x<B>(v));
     return slots_max<B + 1>(v);
   }
@@ -119,7 +148,11 @@ __device__ __forceinline__ float slots_max(float v) {
 }
 template <int B>
 __device__ __forceinline__ float slots_sum(float v) {
-  if constexpr (B <= 5) {
+  if constexpr (B >= 4 && B <= 5) {
+    float a, b;
+    swap_pair<B>(v, a, b);
+    return slots_sum<B + 1>(a + b);
+  } else if constexpr (B <= 5) {
     v += xor_x<B>(v);
     return slots_sum<B + 1>(v);
   }
@@ -177,6 +210,38 @@ __device__ __forceinline__ void widen_fp8(const uint32_t* w, uint32_t* out) {
   }
 }
 
+// A lane's EPL consecutive output elements v * scale as bf16 (round to
+// nearest even) or fp32, with 16- or 8-byte stores (o and the slice offset
+// are multiples of the store width).
+template <typename QT, int EPL>
+__device__ __forceinline__ void store_slice(QT* o, long long base, const float* v, float scale) {
+  constexpr int BYTES = EPL * (int)sizeof(QT);
+  if constexpr (sizeof(QT) == 2 && BYTES % 8 == 0) {
+    constexpr int NWD = EPL / 2;
+    uint32_t w[NWD];
+#pragma unroll
+    for (int k = 0; k < NWD; ++k)
+      w[k] = f32_to_bf16(v[2 * k] * scale) | (f32_to_bf16(v[2 * k + 1] * scale) << 16);
+    if constexpr (NWD % 4 == 0) {
+#pragma unroll
+      for (int k = 0; k < NWD; k += 4)
+        *reinterpret_cast<uint4*>(o + base + 2 * k) = make_uint4(w[k], w[k + 1], w[k + 2], w[k + 3]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < NWD; k += 2)
+        *reinterpret_cast<uint2*>(o + base + 2 * k) = make_uint2(w[k], w[k + 1]);
+    }
+  } else if constexpr (sizeof(QT) == 4 && EPL % 4 == 0) {
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4)
+      *reinterpret_cast<float4*>(o + base + e) =
+          make_float4(v[e] * scale, v[e + 1] * scale, v[e + 2] * scale, v[e + 3] * scale);
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) store_out<QT>(o, base + e, v[e] * scale);
+  }
+}
+
 template <typename QT, typename CT, int D, int G, int EPL, int NR>
 __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
   constexpr bool F32 = sizeof(CT) == 4;
@@ -189,9 +254,11 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
   constexpr int NP = Chunk<CT, EPL>::NP;
   static_assert((1 << B) == LPT && (1 << LG) == G && G <= LPT, "lane split");
   static_assert(NR % 2 == 0, "p.v pairs two load rows");
+  // Where registers allow (two waves per SIMD kept), the next item's q and
+  // first K/V loads are issued before this item's epilogue.
+  constexpr bool kLean = G * NP <= 16;
 
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(p.ws + p.lay.header);
-  const RowDesc* rows = reinterpret_cast<const RowDesc*>(p.ws + p.lay.rows);
   const ItemDesc* items = reinterpret_cast<const ItemDesc*>(p.ws + p.lay.items);
   float* part_ml = reinterpret_cast<float*>(p.ws + p.lay.part_ml);
   float* part_acc = reinterpret_cast<float*>(p.ws + p.lay.part_acc);
@@ -201,7 +268,9 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
   const int dl = lane % LPT;            // d-slice
   const int my_head = dl >> (B - LG);   // head whose logit this lane holds after the scatter
   const int Hkv = p.Hkv;
-  const long long total = (long long)hdr->n_items * Hkv;
+  const int n_items = hdr->n_items;
+  const int32_t* chunk_first = reinterpret_cast<const int32_t*>(p.ws + p.lay.chunks);
+  const long long total = (long long)hdr->n_chunks * Hkv;  // (chunk, kv head) pairs
   const int sh = p.ps_shift;                        // page_size = 1 << sh
   const int pmask = (1 << sh) - 1;
   const uint32_t row_bytes = 2u * Hkv * p.Dpad * (uint32_t)sizeof(CT);  // one cache token row
@@ -210,35 +279,106 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
   const bool use_cap = p.cap > 0.f;
   const float c_log2 = p.qk_scale * kLog2e;
 
-  // The grid is the number of resident waves; wave w walks items w, w + grid,
-  // ...  The planner lists full-size splits first, so every wave ends on the
-  // short remainder splits and the launch has no long tail.
-  const int wave = threadIdx.x >> 6;
-  for (long long idx = (long long)blockIdx.x * kWavesPerWG + wave; idx < total;
-       idx += (long long)gridDim.x * kWavesPerWG) {
-    const int item_i = (int)(idx / Hkv);
-    const int g = (int)(idx - (long long)item_i * Hkv);
-    const ItemDesc it = items[item_i];
-    const RowDesc rd = rows[it.row];
-    const int* bt = p.block_tables + (long long)rd.seq * p.pps;
-
-    // q of the G heads, this lane's d-slice: fp32 values or raw bf16 pairs
-    uint32_t qw[G][NP];
-    {
-      const QT* qp = static_cast<const QT*>(p.q) + ((long long)rd.token * p.Hq + g * G) * D +
-                     dl * EPL;
+  // Wave-uniform view of a work item: (row, KV split, kv head g).
+  struct Item {
+    int token, seq, lo, hi, part, g;
+  };
+  int g = 0, i_last = 0;  // kv head and item end of the wave's current chunk
+  auto desc_at = [&](int i) __attribute__((always_inline)) {
+    return items[i < i_last ? i : i_last - 1];
+  };
+  auto make_item = [&](const ItemDesc& d) __attribute__((always_inline)) {
+    Item r;
+    r.token = __builtin_amdgcn_readfirstlane(d.token);
+    r.seq = __builtin_amdgcn_readfirstlane(d.seq);
+    r.lo = __builtin_amdgcn_readfirstlane(d.lo);
+    r.hi = __builtin_amdgcn_readfirstlane(d.hi);
+    r.part = __builtin_amdgcn_readfirstlane(d.part);
+    r.g = g;
+    return r;
+  };
+  // q of the G heads of item `it`, this lane's d-slice: fp32 values or raw bf16 pairs
+  auto load_q = [&](const Item& it, uint32_t (*qw)[NP]) __attribute__((always_inline)) {
+    const QT* qp =
+        static_cast<const QT*>(p.q) + ((long long)it.token * p.Hq + it.g * G) * D + dl * EPL;
 #pragma unroll
-      for (int i = 0; i < G; ++i) {
-        if constexpr (sizeof(QT) == 4) {
+    for (int i = 0; i < G; ++i) {
+      if constexpr (sizeof(QT) == 4) {
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) qw[i][e] = __float_as_uint(qp[i * D + e]);
-        } else {
+        for (int e = 0; e < EPL; ++e) qw[i][e] = __float_as_uint(qp[i * D + e]);
+      } else {
 #pragma unroll
-          for (int e = 0; e < NP; ++e)
-            qw[i][e] = reinterpret_cast<const uint32_t*>(qp + i * D)[e];
-        }
+        for (int e = 0; e < NP; ++e) qw[i][e] = reinterpret_cast<const uint32_t*>(qp + i * D)[e];
       }
     }
+  };
+  // Page ids of a 64-page window from page k0 >> sh on: lane i holds the i-th.
+  auto load_window = [&](const Item& it, int k0, int& pw0, int& page_reg)
+      __attribute__((always_inline)) {
+    pw0 = k0 >> sh;
+    const int pi = pw0 + lane;
+    const int* bt = p.block_tables + (long long)it.seq * p.pps;
+    page_reg = (pi <= ((it.hi - 1) >> sh)) ? bt[pi] : 0;
+  };
+  // Loads of one step of item `it`, whose tokens below `lim` lie in the page
+  // window held in page_reg.  Tokens from `lim` on are clamped to lim - 1
+  // (valid memory, masked out of the softmax), so every load is
+  // unconditional.  No page id is loaded here: a global load inside the step
+  // loop would make every step wait for all loads in flight (the wait counter
+  // is in order), so windows are switched between chunks of an item instead.
+  auto load_step = [&](const Item& it, int lim, int pw0, int page_reg, int k0,
+                       uint32_t (*kw)[NW], uint32_t (*vw)[NW]) __attribute__((always_inline)) {
+    const char* kv_head = reinterpret_cast<const char*>(cache + 2LL * it.g * p.Dpad + dl * EPL);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int tok = min(k0 + r * TPR + slot, lim - 1);
+      const int page = __builtin_amdgcn_ds_bpermute(((tok >> sh) - pw0) << 2, page_reg);
+      const uint32_t row = ((uint32_t)page << sh) | (uint32_t)(tok & pmask);
+      const char* kp = kv_head + (uint64_t)row * row_bytes;
+      load_chunk<CT, EPL>(reinterpret_cast<const CT*>(kp), true, kw[r]);
+      load_chunk<CT, EPL>(reinterpret_cast<const CT*>(kp + head_bytes), true, vw[r]);
+    }
+  };
+  // end of the chunk of `it` that starts at token c: the tokens whose pages
+  // lie in the 64-page window from page c >> sh on
+  auto chunk_end = [&](const Item& it, int c) __attribute__((always_inline)) {
+    const long long e = ((long long)(c >> sh) + 64) << sh;
+    return e < it.hi ? (int)e : it.hi;
+  };
+
+  // Wave w takes (chunk, kv head) pair w: the grid has a wave for every pair
+  // (the planner makes at most row_chunks_max(resident waves, Hkv) chunks and
+  // the launch has that many waves per kv head), and the chunks hold equal
+  // numbers of keys, so the waves end together.  The wave walks the chunk's
+  // items; they overlap: while the wave works on one, the descriptor of the
+  // item after next and the first page window of the next are in flight.
+  const long long ch = (long long)blockIdx.x * kWavesPerWG + (threadIdx.x >> 6);
+  if (ch >= total) return;
+  const int c = (int)(ch / Hkv);
+  g = (int)(ch - (long long)c * Hkv);
+  const int i_first = min(max(__builtin_amdgcn_readfirstlane(chunk_first[c]), 0), n_items);
+  i_last = min(max(__builtin_amdgcn_readfirstlane(chunk_first[c + 1]), i_first), n_items);
+  if (i_first >= i_last) return;
+
+  Item cur = make_item(desc_at(i_first));
+  uint32_t qw[G][NP];
+  load_q(cur, qw);
+  int pw0 = 0, page_reg = 0;
+  load_window(cur, cur.lo, pw0, page_reg);
+  int idx_n = i_first + 1;
+  ItemDesc desc_n = desc_at(idx_n);
+  uint32_t kA[NR][NW], vA[NR][NW], kB[NR][NW], vB[NR][NW];
+  load_step(cur, chunk_end(cur, cur.lo), pw0, page_reg, cur.lo, kA, vA);
+
+  while (true) {
+    const bool has_next = idx_n < i_last;
+    const Item nxt = make_item(desc_n);  // a clamped, valid item when !has_next
+    uint32_t qw_n[G][NP];
+    if constexpr (kLean) load_q(nxt, qw_n);
+    int pw0_n = 0, page_reg_n = 0;
+    load_window(nxt, nxt.lo, pw0_n, page_reg_n);
+    const int idx_nn = idx_n + 1;
+    desc_n = desc_at(idx_nn);
 
     float acc[G][EPL];
 #pragma unroll
@@ -247,35 +387,8 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
       for (int e = 0; e < EPL; ++e) acc[i][e] = 0.f;
     float m_own = -INFINITY, l_own = 0.f;  // softmax state of head my_head
 
-    const int last_page = (it.hi - 1) >> sh;
-    int pw0 = -(1 << 30);
-    int page_reg = 0;
-    const char* kv_head =
-        reinterpret_cast<const char*>(cache + 2LL * g * p.Dpad + dl * EPL);
-
-    uint32_t kA[NR][NW], vA[NR][NW], kB[NR][NW], vB[NR][NW];
-
-    // Loads of one step.  Tokens past the item are clamped to its last token
-    // (valid memory, masked out of the softmax), so every load is unconditional.
-    auto load_step = [&](int k0, uint32_t (*kw)[NW], uint32_t (*vw)[NW]) {
-      const int need_hi = min(k0 + STEP, it.hi) - 1;
-      if ((need_hi >> sh) >= pw0 + 64 || (k0 >> sh) < pw0) {
-        pw0 = k0 >> sh;
-        const int pi = pw0 + lane;
-        page_reg = (pi <= last_page) ? bt[pi] : 0;
-      }
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const int tok = min(k0 + r * TPR + slot, it.hi - 1);
-        const int page = __builtin_amdgcn_ds_bpermute(((tok >> sh) - pw0) << 2, page_reg);
-        const uint32_t row = ((uint32_t)page << sh) | (uint32_t)(tok & pmask);
-        const char* kp = kv_head + (uint64_t)row * row_bytes;
-        load_chunk<CT, EPL>(reinterpret_cast<const CT*>(kp), true, kw[r]);
-        load_chunk<CT, EPL>(reinterpret_cast<const CT*>(kp + head_bytes), true, vw[r]);
-      }
-    };
-
-    auto compute_step = [&](int k0, uint32_t (*kw)[NW], uint32_t (*vw)[NW]) {
+    auto compute_step = [&](int k0, int lim, uint32_t (*kw)[NW], uint32_t (*vw)[NW])
+        __attribute__((always_inline)) {
       // ---- step 1: logits of this lane's head for the NR load rows ----
       float s2[NR];
 #pragma unroll
@@ -307,7 +420,7 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
         reduce_scatter<B, G>(part, lane);
         float s = part[0];
         s = use_cap ? p.cap * tanhf(s * p.qk_scale / p.cap) * kLog2e : s * c_log2;
-        const bool valid = k0 + r * TPR + slot < it.hi;
+        const bool valid = k0 + r * TPR + slot < lim;
         s2[r] = valid ? s : -INFINITY;
       }
       float bm = s2[0];
@@ -386,12 +499,26 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
     };
 
     // software pipeline: the next step's loads are issued before this step's math
-    load_step(it.lo, kA, vA);
-    for (int k0 = it.lo; k0 < it.hi; k0 += 2 * STEP) {
-      if (k0 + STEP < it.hi) load_step(k0 + STEP, kB, vB);
-      compute_step(k0, kA, vA);
-      if (k0 + 2 * STEP < it.hi) load_step(k0 + 2 * STEP, kA, vA);
-      if (k0 + STEP < it.hi) compute_step(k0 + STEP, kB, vB);
+    for (int c_lo = cur.lo;;) {
+      const int c_hi = chunk_end(cur, c_lo);
+      // The loads are unconditional (past the chunk they re-read its last
+      // token, masked): a load issued on one path only would make the
+      // following waits drain every load in flight.  A fully masked step
+      // adds exactly nothing (p = 0), and the chunk's first step is never
+      // empty, so the running max is finite from then on.
+      for (int k0 = c_lo; k0 < c_hi; k0 += 2 * STEP) {
+        load_step(cur, c_hi, pw0, page_reg, k0 + STEP, kB, vB);
+        compute_step(k0, c_hi, kA, vA);
+        load_step(cur, c_hi, pw0, page_reg, k0 + 2 * STEP, kA, vA);
+        compute_step(k0 + STEP, c_hi, kB, vB);
+      }
+      if (c_hi >= cur.hi) break;
+      c_lo = c_hi;
+      load_window(cur, c_lo, pw0, page_reg);
+      load_step(cur, chunk_end(cur, c_lo), pw0, page_reg, c_lo, kA, vA);
+    }
+    if constexpr (kLean) {
+      if (has_next) load_step(nxt, chunk_end(nxt, nxt.lo), pw0_n, page_reg_n, nxt.lo, kA, vA);
     }
 
     // ---- combine the token slots; broadcast l, m of every head ----
@@ -407,11 +534,11 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
     }(std::make_integer_sequence<int, G>{});
     if (slot == 0) {
       const float vs = p.v_scale;
-      if (it.part < 0) {
+      if (cur.part < 0) {
         QT* op = static_cast<QT*>(p.out);
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-          const int h = g * G + i;
+          const int h = cur.g * G + i;
           float ll = lh[i], f = 1.f;
           if (p.sink) {
             const float sg = p.sink[h] * kLog2e;
@@ -420,24 +547,36 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
             ll = ll * f + __builtin_amdgcn_exp2f(sg - mx);
           }
           const float scale = f * vs / ll;
-          const long long base = ((long long)rd.token * p.Hq + h) * D + dl * EPL;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) store_out<QT>(op, base + e, acc[i][e] * scale);
+          const long long base = ((long long)cur.token * p.Hq + h) * D + dl * EPL;
+          store_slice<QT, EPL>(op, base, acc[i], scale);
         }
-      } else if (it.part < p.lay.max_parts) {
+      } else if (cur.part < p.lay.max_parts) {
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-          const long long pb = (long long)it.part * p.Hq + g * G + i;
+          const long long pb = (long long)cur.part * p.Hq + cur.g * G + i;
           if (dl == 0) {
             part_ml[2 * pb] = mh[i];
             part_ml[2 * pb + 1] = lh[i];
           }
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) part_acc[pb * D + dl * EPL + e] = acc[i][e];
+          store_slice<float, EPL>(part_acc, pb * D + dl * EPL, acc[i], 1.f);
         }
       }
     }
     (void)my_head;
+    if (!has_next) break;
+    cur = nxt;
+    if constexpr (kLean) {
+#pragma unroll
+      for (int i = 0; i < G; ++i)
+#pragma unroll
+        for (int e = 0; e < NP; ++e) qw[i][e] = qw_n[i][e];
+    } else {
+      load_q(cur, qw);
+    }
+    pw0 = pw0_n;
+    page_reg = page_reg_n;
+    idx_n = idx_nn;
+    if constexpr (!kLean) load_step(cur, chunk_end(cur, cur.lo), pw0, page_reg, cur.lo, kA, vA);
   }
 }
 
@@ -463,19 +602,50 @@ int resident_blocks(const void* kernel, int block_threads, size_t lds) {
   return per_cu * cus > 0 ? per_cu * cus : 1024;
 }
 
+// Row kernel configuration for these types and sizes.
+template <typename QT, typename CT, int D, int G>
+struct RowCfg {
+  // elements per lane: one 16-byte load, at most 64 accumulators per lane
+  static constexpr int E16 = 16 / (int)sizeof(CT);
+  static constexpr int EPL = (E16 * G > 64) ? (64 / G) : E16;
+  // load rows per step: 4, or 2 where G x EPL = 64 accumulators leave no room
+  // for two 4-row buffers at two waves per SIMD
+  static constexpr int NR = (G * EPL >= 64 && (sizeof(CT) >= 2 || G >= 16)) ? 2 : 4;
+  static int resident() {
+    static const int cap = resident_blocks(
+        reinterpret_cast<const void*>(&row_kernel<QT, CT, D, G, EPL, NR>), 64 * kWavesPerWG, 0);
+    return cap;
+  }
+};
+
 template <typename QT, typename CT, int D, int G>
 hipError_t launch_rows_t(const AttnParams& p, hipStream_t s) {
-  // elements per lane: one 16-byte load, at most 64 accumulators per lane
-  constexpr int E16 = 16 / (int)sizeof(CT);
-  constexpr int EPL = (E16 * G > 64) ? (64 / G) : E16;
-  constexpr int NR = 4;
-  static const int cap = resident_blocks(
-      reinterpret_cast<const void*>(&row_kernel<QT, CT, D, G, EPL, NR>), 64 * kWavesPerWG, 0);
-  const long long waves = (long long)p.lay.max_items * p.Hkv;
-  const long long wgs = (waves + kWavesPerWG - 1) / kWavesPerWG;
-  dim3 grid((unsigned)(wgs < cap ? (wgs > 0 ? wgs : 1) : cap));
-  row_kernel<QT, CT, D, G, EPL, NR><<<grid, 64 * kWavesPerWG, 0, s>>>(p);
+  using Cfg = RowCfg<QT, CT, D, G>;
+  // one wave per (chunk, kv head) for as many chunks as the planner may make
+  const long long waves =
+      (long long)row_chunks_max(Cfg::resident() * kWavesPerWG, p.Hkv) * p.Hkv;
+  dim3 grid((unsigned)((waves + kWavesPerWG - 1) / kWavesPerWG));
+  row_kernel<QT, CT, D, G, Cfg::EPL, Cfg::NR><<<grid, 64 * kWavesPerWG, 0, s>>>(p);
   return hipGetLastError();
+}
+
+template <typename QT, typename CT, int D>
+int row_waves_g(int G) {
+  switch (G) {
+    case 1: return RowCfg<QT, CT, D, 1>::resident() * kWavesPerWG;
+    case 2: return RowCfg<QT, CT, D, 2>::resident() * kWavesPerWG;
+    case 4: return RowCfg<QT, CT, D, 4>::resident() * kWavesPerWG;
+    case 8: return RowCfg<QT, CT, D, 8>::resident() * kWavesPerWG;
+    case 16: return RowCfg<QT, CT, D, 16>::resident() * kWavesPerWG;
+    default: return 0;
+  }
+}
+
+template <typename QT, typename CT>
+int row_waves_d(int D, int G) {
+  if (D == 64) return row_waves_g<QT, CT, 64>(G);
+  if (D == 128) return row_waves_g<QT, CT, 128>(G);
+  return 0;
 }
 
 template <typename QT, typename CT, int D>
@@ -498,6 +668,13 @@ hipError_t launch_rows_d(const AttnParams& p, hipStream_t s) {
 }
 
 }  // namespace
+
+int row_waves(rpa_dtype q_dt, rpa_dtype cache_dt, int D, int G) {
+  if (q_dt == RPA_F32 && cache_dt == RPA_F32) return row_waves_d<float, float>(D, G);
+  if (q_dt == RPA_BF16 && cache_dt == RPA_BF16) return row_waves_d<uint16_t, uint16_t>(D, G);
+  if (q_dt == RPA_BF16 && cache_dt == RPA_FP8_E4M3) return row_waves_d<uint16_t, uint8_t>(D, G);
+  return 0;
+}
 
 hipError_t launch_rows(const AttnParams& p, rpa_dtype q_dt, rpa_dtype cache_dt, hipStream_t s) {
   if (q_dt == RPA_F32 && cache_dt == RPA_F32) return launch_rows_d<float, float>(p, s);

@@ -1,7 +1,8 @@
 // Device-side planner: reads the ragged metadata (query_start_loc, kv_lens,
 // distribution) on the GPU, so no host synchronisation is needed, and writes
 // the work lists of the attention kernels into the workspace:
-//   * row items: (query row, KV split) for rows served by the row kernel;
+//   * row items: pieces (query row, key range) for rows served by the row
+//     kernel, grouped in equal chunks of keys, one chunk per wave and kv head;
 //   * prefill items: (sequence, query tile) for the MFMA prefill kernel.
 // One workgroup of 1024 threads; per-sequence tables live in LDS.
 #pragma once
@@ -127,12 +128,16 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
   __syncthreads();
   const int n_rows = min(row_base, p.lay.max_rows);
 
-  // ---- split size: about kTargetWaves waves of work over all kv heads ----
-  const long long target_items = max(1, min(kTargetItems, kTargetWaves / max(p.Hkv, 1)));
-  long long S = (vis_total + target_items - 1) / target_items;
-  S = (S + 15) / 16 * 16;
-  if (S < kMinSplit) S = kMinSplit;
-  const int split = (int)min(S, (long long)0x40000000);
+  // ---- chunks: the visible key ranges of all rows, in row order, form one
+  // stream of vis_total keys, cut into n_chunks chunks of C keys (the last one
+  // shorter); a chunk is the work of one wave per kv head, so the waves of the
+  // row kernel get equal work, and only rows cut by a chunk boundary leave
+  // split partials to merge. ----
+  const long long want = row_chunks_max(p.row_waves, p.Hkv);
+  long long C = (vis_total + want - 1) / want;
+  if (C < kMinSplit) C = kMinSplit;
+  const int n_chunks = (int)min((vis_total + C - 1) / C, (long long)kTargetItems);
+  int32_t* chunk_first = reinterpret_cast<int32_t*>(ws + p.lay.chunks);
 
   // row r -> (seq, token, visible range [lo, hi))
   auto row_info = [&](int r, int& seq, int& token, int& lo, int& hi) {
@@ -157,38 +162,25 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
     lo = (W > 0) ? max(0, pos - W + 1) : 0;
   };
 
-  // ---- pass 2a: number of full-size splits (they are scheduled first) ----
-  int n_full_total = 0;
+  // ---- pass 2: rows and their pieces (the parts of a row in different chunks) ----
+  long long stream_base = 0;
+  int item_base = 0, part_base = 0, merge_base = 0;
   for (int base = 0; base < n_rows; base += kT) {
     const int r = base + threadIdx.x;
-    int n_full = 0;
-    if (r < n_rows) {
-      int seq, token, lo, hi;
-      row_info(r, seq, token, lo, hi);
-      n_full = (hi - lo) / split;
-    }
-    int tot;
-    block_exclusive_scan(n_full, &tot, s_w32);
-    n_full_total += tot;
-  }
-
-  // ---- pass 2b: rows, their items (full splits first, then the remainders) ----
-  int full_base = 0, rem_base = n_full_total, part_base = 0, merge_base = 0;
-  for (int base = 0; base < n_rows; base += kT) {
-    const int r = base + threadIdx.x;
-    int n_split = 0, n_full = 0, seq = 0, lo = 0, hi = 0, token = 0;
+    int seq = 0, token = 0, lo = 0, hi = 0;
+    long long len = 0;
     if (r < n_rows) {
       row_info(r, seq, token, lo, hi);
-      n_full = (hi - lo) / split;
-      n_split = (hi - lo + split - 1) / split;
+      len = hi - lo;                                  // >= 1: a row sees its own key
     }
-    const int has_rem = n_split - n_full;
-    int tot_full, tot_rem, tot_parts, tot_merge;
-    const int my_full = block_exclusive_scan(n_full, &tot_full, s_w32) + full_base;
-    const int my_rem = block_exclusive_scan(has_rem, &tot_rem, s_w32b) + rem_base;
+    long long tot_len;
+    const long long off = block_exclusive_scan(len, &tot_len, s_w64) + stream_base;
+    const int n_split = (r < n_rows) ? (int)((off + len - 1) / C - off / C + 1) : 0;
+    int tot_items, tot_parts, tot_merge;
+    const int my_item = block_exclusive_scan(n_split, &tot_items, s_w32) + item_base;
     const int my_part =
-        block_exclusive_scan(n_split > 1 ? n_split : 0, &tot_parts, s_w32c) + part_base;
-    const int my_merge = block_exclusive_scan(n_split > 1 ? 1 : 0, &tot_merge, s_w32) +
+        block_exclusive_scan(n_split > 1 ? n_split : 0, &tot_parts, s_w32b) + part_base;
+    const int my_merge = block_exclusive_scan(n_split > 1 ? 1 : 0, &tot_merge, s_w32c) +
                          merge_base;
     if (r < n_rows) {
       RowDesc rd;
@@ -200,15 +192,23 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
       rd.part_base = n_split > 1 ? my_part : -1;
       rd.pad[0] = rd.pad[1] = 0;
       rows[r] = rd;
+      const long long c0 = off / C;
       for (int j = 0; j < n_split; ++j) {
-        const int slot = (j < n_full) ? my_full + j : my_rem;
+        const int slot = my_item + j;
         if (slot >= p.lay.max_items) break;
+        const long long s0 = max(off, (c0 + j) * C);
+        const long long s1 = min(off + len, (c0 + j + 1) * C);
         ItemDesc it;
-        it.row = r;
-        it.lo = lo + j * split;
-        it.hi = min(hi, lo + (j + 1) * split);
+        it.token = token;
+        it.seq = seq;
+        it.lo = lo + (int)(s0 - off);
+        it.hi = lo + (int)(s1 - off);
         it.part = n_split > 1 ? my_part + j : -1;
+        it.row = r;
+        it.pad[0] = it.pad[1] = 0;
         items[slot] = it;
+        // every chunk has exactly one piece that starts at its first key
+        if (s0 == (c0 + j) * C && c0 + j < n_chunks) chunk_first[c0 + j] = slot;
       }
       if (n_split > 1 && my_merge < p.lay.max_merge_rows) {
         MergeDesc md;
@@ -219,18 +219,21 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
         merge_rows[my_merge] = md;
       }
     }
-    full_base += tot_full;
-    rem_base += tot_rem;
+    stream_base += tot_len;
+    item_base += tot_items;
     part_base += tot_parts;
     merge_base += tot_merge;
   }
-  const int item_base = rem_base;
+  // chunks that hold keys (all of them unless rows were cut off at max_rows)
+  const int n_chunks_laid = (int)min((long long)n_chunks, (stream_base + C - 1) / C);
   if (threadIdx.x == 0) {
+    chunk_first[n_chunks_laid] = min(item_base, p.lay.max_items);
     PlanHeader h = {};
     h.num_seqs = num_seqs;
     h.n_rows = n_rows;
     h.n_items = min(item_base, p.lay.max_items);
-    h.split = split;
+    h.split = (int)min(C, (long long)0x7fffffff);
+    h.n_chunks = n_chunks_laid;
     h.n_merge_rows = min(merge_base, p.lay.max_merge_rows);
     h.n_pf_items = min(pf_base, p.lay.max_pf_items);
     h.row_next = 0;

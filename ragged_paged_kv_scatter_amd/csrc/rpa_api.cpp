@@ -153,6 +153,8 @@ Workspace workspace_layout(const rpa_desc& d) {
   off = align256(off + (size_t)w.max_rows * sizeof(RowDesc));
   w.items = off;
   off = align256(off + (size_t)w.max_items * sizeof(ItemDesc));
+  w.chunks = off;
+  off = align256(off + (size_t)(kTargetItems + 1) * sizeof(int32_t));
   w.merge_rows = off;
   off = align256(off + (size_t)w.max_merge_rows * sizeof(MergeDesc));
   w.pf_items = off;
@@ -363,6 +365,8 @@ int rpa_forward(const rpa_desc* desc, const rpa_options* opts, const void* queri
   pp.window = opts->sliding_window;
   pp.prefill_min_q = prefill_min_q(*desc);
   pp.Hkv = desc->num_kv_heads;
+  pp.row_waves = row_waves((rpa_dtype)desc->q_dtype, (rpa_dtype)desc->cache_dtype,
+                           desc->head_dim, desc->num_q_heads / desc->num_kv_heads);
   // one launch: the planner, and the cache update when new tokens come along
   ScatterParams sp = {};
   if (keys)

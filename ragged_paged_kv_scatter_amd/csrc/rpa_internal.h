@@ -13,14 +13,20 @@ namespace rpa {
 // ---------------------------------------------------------------------------
 // Tunables of the plan.
 // ---------------------------------------------------------------------------
-// Row-kernel work items aimed for: the KV range of a query row is cut into
-// splits of S tokens with S >= (sum of visible lengths) / (kTargetWaves / Hkv)
-// (each item is one wave per kv head), so there are at most
-// kTargetItems + rows items and at most 2 * kTargetItems split partials
-// (every split row has length > S).
-constexpr int kTargetWaves = 16384;
-constexpr int kTargetItems = 2048;    // upper bound of kTargetWaves / Hkv used for sizing
+// Row-kernel work: the visible key ranges of the rows, in row order, form one
+// stream cut into at most kTargetItems chunks (one per resident wave and kv
+// head) of at least kMinSplit keys; a chunk's pieces of rows are the items, so
+// there are at most kTargetItems + rows items, fewer than 2 * kTargetItems
+// split partials (the rows cut by a chunk boundary) and fewer than
+// kTargetItems split rows.
+constexpr int kTargetItems = 2048;    // chunks at most
 constexpr int kMinSplit = 128;        // never cut a row's KV range finer than this
+// Chunks the planner may make for a row kernel with this many resident waves;
+// the row kernel is launched with this many waves per kv head.
+__host__ __device__ inline int row_chunks_max(int row_waves, int Hkv) {
+  const int c = row_waves / (Hkv > 0 ? Hkv : 1);
+  return c < 1 ? 1 : (c > kTargetItems ? kTargetItems : c);
+}
 constexpr int kPlanThreads = 1024;    // the planner is one workgroup
 constexpr int kPlanCacheSeqs = 4000;  // planner keeps per-sequence data in LDS up to this (48 KB)
 // dynamic LDS words of the planner for max_num_seqs sequences
@@ -37,12 +43,13 @@ struct PlanHeader {
   int32_t num_seqs;      // min(sum(distribution), max_num_seqs)
   int32_t n_rows;        // query rows handled by the row kernel
   int32_t n_items;       // (row, split) items of the row kernel
-  int32_t split;         // S, tokens per split
+  int32_t split;         // C, keys per chunk
   int32_t n_merge_rows;  // rows with more than one split
   int32_t n_pf_items;    // (sequence, query tile) items of the prefill kernel
   int32_t row_next;      // work counter of the row kernel (zeroed by the planner)
   int32_t pf_next;       // work counter of the prefill kernel (zeroed by the planner)
-  int32_t pad[8];
+  int32_t n_chunks;      // chunks of the row kernel (chunk c = items [first[c], first[c+1]))
+  int32_t pad[7];
 };
 
 struct RowDesc {         // one query row of the row (decode) kernel
@@ -55,9 +62,12 @@ struct RowDesc {         // one query row of the row (decode) kernel
 };
 
 struct ItemDesc {        // a split of one row: keys [lo, hi)
-  int32_t row;
+  int32_t token;         // row index into queries / out
+  int32_t seq;
   int32_t lo, hi;
   int32_t part;          // partial slot, or -1 when the row has a single split
+  int32_t row;
+  int32_t pad[2];
 };
 
 struct MergeDesc {       // a row with more than one split, for the merge
@@ -76,7 +86,7 @@ struct PrefillItem {     // a query tile of one prefill sequence
 constexpr int kZeroBytes = 1024;      // zero-filled source row for masked key loads
 
 struct Workspace {       // byte offsets into the caller's workspace
-  size_t header, zeros, rows, items, merge_rows, pf_items, part_ml, part_acc, total;
+  size_t header, zeros, rows, items, chunks, merge_rows, pf_items, part_ml, part_acc, total;
   int32_t max_rows, max_items, max_parts, max_pf_items, max_merge_rows;
 };
 
@@ -138,6 +148,7 @@ struct PlanParams {
   char* ws;
   Workspace lay;
   int32_t max_num_seqs, T, window, prefill_min_q, Hkv;
+  int32_t row_waves;     // resident waves of the row kernel (chunks = row_waves / Hkv)
 };
 
 struct AttnParams {
@@ -165,6 +176,8 @@ hipError_t launch_scatter(const ScatterParams& p, rpa_dtype in_dt, rpa_dtype cac
 hipError_t launch_prep(const PlanParams& pp, const ScatterParams* sp, rpa_dtype in_dt,
                        rpa_dtype cache_dt, hipStream_t s);
 hipError_t launch_rows(const AttnParams& p, rpa_dtype q_dt, rpa_dtype cache_dt, hipStream_t s);
+// waves of the row kernel for these types and sizes that fit on the device at once
+int row_waves(rpa_dtype q_dt, rpa_dtype cache_dt, int D, int G);
 hipError_t launch_merge(const AttnParams& p, rpa_dtype q_dt, hipStream_t s);
 hipError_t launch_prefill(const AttnParams& p, rpa_dtype q_dt, rpa_dtype cache_dt,
                           hipStream_t s);
