@@ -223,10 +223,21 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
       merge_one_g<uint16_t, D>(p, mi);
   }
 
-  // Persistent grid (a multiple of 8 blocks): block b takes units b, b + grid,
-  // ...  Consecutive units sit on different XCDs; the head slot -> (kv head =
-  // slot mod Hkv) mapping keeps the q heads of one kv head on one XCD and L2.
-  for (long long u = blockIdx.x; u < n_units; u += gridDim.x) {
+  // Persistent grid: in round k block b takes unit k * grid + b, except that
+  // odd rounds reverse the order of the groups of 8 blocks (when the grid is
+  // a multiple of 8).  Units come heavy first (causal tiles late in a
+  // sequence see more keys), so the reversal evens out the blocks' sums of
+  // work; units keep u mod 8 = b mod 8, so consecutive units sit on different
+  // XCDs and the head slot -> (kv head = slot mod Hkv) mapping keeps the q
+  // heads of one kv head on one XCD and L2.  Once a round's unit is past the
+  // end, every later round's is too.
+  const bool snake = (gridDim.x & 7) == 0;
+  for (long long k = 0;; ++k) {
+    const long long b = (snake && (k & 1)) ? (long long)(gridDim.x / 8 - 1 - blockIdx.x / 8) * 8 +
+                                                 (blockIdx.x & 7)
+                                           : (long long)blockIdx.x;
+    const long long u = k * gridDim.x + b;
+    if (u >= n_units) break;
     const int item_i = (int)(u / Hq);
     const int hh = (int)(u - (long long)item_i * Hq);
     const int g = hh % Hkv;
