@@ -470,6 +470,10 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
       constexpr int XA = 8 / KS;          // logits exponentiated per q.k MFMA
       constexpr int XB = 8 / DT;          // per p.v MFMA of k-steps 0, 1
       constexpr int MB = 16 / DT;         // logits max-reduced per p.v MFMA of k-steps 2, 3
+      // The two waves of a SIMD take turns: a wave in its compute part
+      // outranks one at its barrier / copy part, which keeps the MFMA pipe
+      // fed while the other wave catches up (measured 2-3% on long prefill).
+      __builtin_amdgcn_s_setprio(1);
       bf16x8 a0 = ld_k(kn, 0, 0), a1 = ld_k(kn, 0, 1);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -524,6 +528,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
           va = vn;
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       l_run += ls0 + ls1;
       mx = fmaxf(m0, m1);
       mx = fmaxf(mx, __shfl_xor(mx, 32)) * c_eff;
