@@ -91,20 +91,39 @@ __device__ __forceinline__ float xor_x(float v) {
   else return partner_of<K>(v);
 }
 
-// Value of lane REP of this lane's aligned group of LPT lanes.
+// Value of lane REP of this lane's aligned group of LPT lanes, by DPP and
+// permlane moves (no trip through LDS).
 template <int LPT, int REP>
 __device__ __forceinline__ float bcast(float v) {
+  const int x = __float_as_int(v);
   if constexpr (LPT == 1) {
     return v;
+  } else if constexpr (LPT == 2) {
+    // quad_perm [REP, REP, 2 + REP, 2 + REP]
+    constexpr int c = REP | (REP << 2) | ((2 + REP) << 4) | ((2 + REP) << 6);
+    return __int_as_float(__builtin_amdgcn_mov_dpp(x, c, 0xF, 0xF, false));
+  } else if constexpr (LPT == 4) {
+    constexpr int c = REP * 0x55;  // quad_perm [REP, REP, REP, REP]
+    return __int_as_float(__builtin_amdgcn_mov_dpp(x, c, 0xF, 0xF, false));
+  } else if constexpr (LPT == 8) {
+    // lane REP % 4 of every quad, then row_half_mirror (lane 4 + j <- 3 - j
+    // within each 8 lanes) written only into the quads (banks) not holding REP
+    const int t = __builtin_amdgcn_mov_dpp(x, (REP & 3) * 0x55, 0xF, 0xF, false);
+    constexpr int banks = (REP < 4) ? 0xA : 0x5;
+    return __int_as_float(__builtin_amdgcn_update_dpp(t, t, 0x141, 0xF, banks, false));
   } else if constexpr (LPT == 16) {
-    return __int_as_float(
-        __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + REP, 0xF, 0xF, false));
-  } else if constexpr (LPT < 16) {
-    return swz<((0x1F & ~(LPT - 1)) | (REP << 5))>(v);
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x150 + REP, 0xF, 0xF, false));
   } else if constexpr (LPT == 32) {
-    return swz<(REP << 5)>(v);
+    // lane REP % 16 of every row, then the row of REP within the 32-lane half
+    const float t =
+        __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x150 + (REP & 15), 0xF, 0xF, false));
+    float a, b;
+    swap_pair<4>(t, a, b);           // lane by lane {t, t of the partner row}
+    const bool own = ((__lane_id() >> 4) & 1) == (REP >> 4);
+    const bool hi = (__lane_id() >> 4) & 1;
+    return own ? t : (hi ? a : b);
   } else {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), REP));
+    return __int_as_float(__builtin_amdgcn_readlane(x, REP));
   }
 }
 
@@ -278,6 +297,8 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
   const CT* cache = static_cast<const CT*>(p.cache);
   const bool use_cap = p.cap > 0.f;
   const float c_log2 = p.qk_scale * kLog2e;
+  const float cap_k = use_cap ? p.qk_scale * 2.f * kLog2e / p.cap : 0.f;  // x -> 2x log2 e
+  const float cap_l2 = p.cap * kLog2e;
 
   // Wave-uniform view of a work item: (row, KV split, kv head g).
   struct Item {
@@ -419,7 +440,16 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
         }
         reduce_scatter<B, G>(part, lane);
         float s = part[0];
-        s = use_cap ? p.cap * tanhf(s * p.qk_scale / p.cap) * kLog2e : s * c_log2;
+        if constexpr (F32) {
+          s = use_cap ? p.cap * tanhf(s * p.qk_scale / p.cap) * kLog2e : s * c_log2;
+        } else if (use_cap) {
+          // cap * tanh(x) in log2 units with tanh(x) = 1 - 2 / (e^{2x} + 1):
+          // one exp2 and one reciprocal (well inside the bf16 / e4m3 bounds)
+          const float e2 = __builtin_amdgcn_exp2f(s * cap_k);
+          s = cap_l2 * (1.f - 2.f * __builtin_amdgcn_rcpf(e2 + 1.f));
+        } else {
+          s *= c_log2;
+        }
         const bool valid = k0 + r * TPR + slot < lim;
         s2[r] = valid ? s : -INFINITY;
       }
