@@ -215,17 +215,15 @@ __device__ __forceinline__ void load_chunk(const CT* ptr, bool valid, uint32_t* 
   }
 }
 
-// e4m3 codes -> bf16 pairs of consecutive elements (exact widening)
+// e4m3 codes -> bf16 pairs of consecutive elements (exact widening: the
+// scaled convert with scale 1 matched cvt_pk_f32_fp8 + bf16 truncation on all
+// 65536 code pairs on the MI355X)
 template <int NW>
 __device__ __forceinline__ void widen_fp8(const uint32_t* w, uint32_t* out) {
-  typedef float f2 __attribute__((ext_vector_type(2)));
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
-    const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
-    const f2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
-    out[2 * i] = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
-    out[2 * i + 1] =
-        __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
+    out[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[i], 1.f, false));
+    out[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[i], 1.f, true));
   }
 }
 

@@ -29,10 +29,17 @@ __device__ V block_exclusive_scan(V v, V* total, V* s_waves) {
   }
   if (lane == 63) s_waves[wave] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    V acc = 0;
-    for (int w = 0; w < kWaves; ++w) { V t = s_waves[w]; s_waves[w] = acc; acc += t; }
-    s_waves[kWaves] = acc;
+  if (wave == 0) {
+    // the kWaves wave totals, scanned by wave 0's lanes (no serial LDS chain)
+    const V t = lane < kWaves ? s_waves[lane] : V(0);
+    V inc = t;
+#pragma unroll
+    for (int o = 1; o < kWaves; o <<= 1) {
+      V y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    if (lane < kWaves) s_waves[lane] = inc - t;
+    if (lane == kWaves - 1) s_waves[kWaves] = inc;
   }
   __syncthreads();
   V res = x - v + s_waves[wave];

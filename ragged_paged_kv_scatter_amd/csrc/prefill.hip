@@ -64,12 +64,11 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// two e4m3 codes (bytes 0/1, or 2/3 with HI) -> two bf16 packed in one word (exact)
+// two e4m3 codes (bytes 0/1, or 2/3 with HI) -> two bf16 packed in one word
+// (exact: the scaled convert with scale 1 widens every code pair exactly)
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-  typedef float f2 __attribute__((ext_vector_type(2)));
-  const f2 f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
-  return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.f, HI));
 }
 
 // Physical 16-byte chunk of logical chunk c in LDS row r.
