@@ -608,6 +608,296 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Row kernel for large GQA groups (G = 8 or 16 q heads per kv head, bf16
+// queries, bf16 or e4m3 cache) on v_mfma_f32_16x16x32_bf16.  With G >= 8 the
+// dot products of the VALU kernel above outweigh the HBM time; here they run
+// on the matrix cores and the wave keeps up with its loads.  Same plan, work
+// items, split partials and output as the VALU kernel.
+//
+// A step covers 32 tokens, two groups of 16.  Lane l: c16 = l % 16, g4 = l / 16.
+//   S = K Q^T per group (16 tokens x 16 heads): A = K, lane (token c16,
+//     d-slot block g4) straight from its 16-byte load; B = Q^T, lane (head c16,
+//     the same d slots).  The d order inside an MFMA is permuted identically
+//     in both operands.  S lands as lane (head c16, tokens 4 g4 .. 4 g4 + 3).
+//   O += P V (16 heads x 16 d per MFMA, k = 32 tokens): A = P, lane (head c16,
+//     token slots 8 g4 + j = tokens 4 g4 + j of group 0 and of group 1), i.e.
+//     exactly the p of the lane's own S values; B = V, lane (d c16, the same
+//     tokens), read transposed (ds_read_b64_tr_b16) from the wave's copy of
+//     the step's V rows in LDS (bf16, rows padded to spread the banks).
+//     O lands as lane (d c16 of the block, heads 4 g4 .. 4 g4 + 3).
+// Heads past G (G = 8) have zero q and are never stored.
+// ---------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef i16x4 __attribute__((address_space(3)))* lds_i16x4_ptr;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename CT, int D>
+struct MfCfg {
+  static constexpr int ESZ = (int)sizeof(CT);
+  static constexpr int E = 16 / ESZ;         // elements per 16-byte load
+  static constexpr int NLD = D / (4 * E);    // 16-byte K (or V) loads per lane per 16 tokens
+  static constexpr int H = E / 8;            // q.k MFMAs fed by one load
+  static constexpr int NMQ = D / 32;         // q.k MFMAs per 16 tokens
+  static constexpr int NMP = D / 16;         // p.v MFMAs per step
+  static constexpr int LROW = 2 * D + 32;    // LDS bytes per staged V row
+  static constexpr int LWAVE = 32 * LROW;    // LDS bytes per wave
+};
+
+__device__ __forceinline__ u32x4 nt_load16(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+template <typename CT, int D, int G>
+__global__ __launch_bounds__(64 * kWavesPerWG) void mfma_row_kernel(AttnParams p) {
+  using Cfg = MfCfg<CT, D>;
+  constexpr int ESZ = Cfg::ESZ, E = Cfg::E, NLD = Cfg::NLD, H = Cfg::H, NMQ = Cfg::NMQ,
+                NMP = Cfg::NMP, LROW = Cfg::LROW;
+  constexpr bool FP8 = sizeof(CT) == 1;
+  static_assert(G == 8 || G == 16, "16-head MFMA columns");
+  static_assert(NLD >= 1 && H >= 1, "load split");
+  __shared__ __attribute__((aligned(16))) char s_v[kWavesPerWG * Cfg::LWAVE];
+
+  const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(p.ws + p.lay.header);
+  const ItemDesc* items = reinterpret_cast<const ItemDesc*>(p.ws + p.lay.items);
+  float* part_ml = reinterpret_cast<float*>(p.ws + p.lay.part_ml);
+  float* part_acc = reinterpret_cast<float*>(p.ws + p.lay.part_acc);
+  const int32_t* chunk_first = reinterpret_cast<const int32_t*>(p.ws + p.lay.chunks);
+
+  const int lane = lane_id();
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int wave = threadIdx.x >> 6;
+  char* vt = s_v + wave * Cfg::LWAVE;
+  const int Hkv = p.Hkv;
+  const int n_items = hdr->n_items;
+  const long long total = (long long)hdr->n_chunks * Hkv;
+  const int sh = p.ps_shift;
+  const int pmask = (1 << sh) - 1;
+  const uint32_t row_bytes = 2u * Hkv * p.Dpad * (uint32_t)ESZ;
+  const uint32_t head_bytes = p.Dpad * (uint32_t)ESZ;
+  const bool use_cap = p.cap > 0.f;
+  const float c_log2 = p.qk_scale * kLog2e;
+  const float cap_k = use_cap ? p.qk_scale * 2.f * kLog2e / p.cap : 0.f;
+  const float cap_l2 = p.cap * kLog2e;
+
+  const long long ch = (long long)blockIdx.x * kWavesPerWG + wave;
+  if (ch >= total) return;
+  const int c = (int)(ch / Hkv);
+  const int g = (int)(ch - (long long)c * Hkv);
+  const int i_first = min(max(__builtin_amdgcn_readfirstlane(chunk_first[c]), 0), n_items);
+  const int i_last = min(max(__builtin_amdgcn_readfirstlane(chunk_first[c + 1]), i_first), n_items);
+  const char* kv_head = reinterpret_cast<const char*>(p.cache) + 2LL * g * p.Dpad * ESZ;
+
+  // this lane's d offset (elements) of load ld: 4 E ld + E g4
+  auto d_of = [&](int ld) { return 4 * E * ld + E * g4; };
+
+  for (int ii = i_first; ii < i_last; ++ii) {
+    const ItemDesc dsc = items[ii];
+    const int token = __builtin_amdgcn_readfirstlane(dsc.token);
+    const int seq = __builtin_amdgcn_readfirstlane(dsc.seq);
+    const int lo = __builtin_amdgcn_readfirstlane(dsc.lo);
+    const int hi = __builtin_amdgcn_readfirstlane(dsc.hi);
+    const int part = __builtin_amdgcn_readfirstlane(dsc.part);
+    const int* bt = p.block_tables + (long long)seq * p.pps;
+
+    // q^T operands: lane (head c16, d slots of g4) per MFMA
+    bf16x8 qb[NMQ];
+    {
+      const uint16_t* qp = static_cast<const uint16_t*>(p.q) +
+                           ((long long)token * p.Hq + g * G + (c16 < G ? c16 : 0)) * D;
+#pragma unroll
+      for (int m = 0; m < NMQ; ++m) {
+        const int d0 = d_of(m / H) + 8 * (m % H);
+        const uint4 v = (c16 < G) ? *reinterpret_cast<const uint4*>(qp + d0) : make_uint4(0, 0, 0, 0);
+        qb[m] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+
+    int pw0 = 0, page_reg = 0;
+    auto load_window = [&](int k0) __attribute__((always_inline)) {
+      pw0 = k0 >> sh;
+      const int pi = pw0 + lane;
+      page_reg = (pi <= ((hi - 1) >> sh)) ? bt[pi] : 0;
+    };
+    auto chunk_end = [&](int k) __attribute__((always_inline)) {
+      const long long e = ((long long)(k >> sh) + 64) << sh;
+      return e < hi ? (int)e : hi;
+    };
+    // K and V pieces of the 32 tokens from k0 (tokens from lim on re-read lim - 1)
+    auto load_step = [&](int lim, int k0, u32x4 (*kw)[NLD], u32x4 (*vw)[NLD])
+        __attribute__((always_inline)) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int tok = min(k0 + 16 * t + c16, lim - 1);
+        const int page = __builtin_amdgcn_ds_bpermute(((tok >> sh) - pw0) << 2, page_reg);
+        const uint32_t row = ((uint32_t)page << sh) | (uint32_t)(tok & pmask);
+        const char* kp = kv_head + (uint64_t)row * row_bytes;
+#pragma unroll
+        for (int ld = 0; ld < NLD; ++ld) {
+          const uint32_t off = (uint32_t)(ESZ * d_of(ld));
+          kw[t][ld] = nt_load16(kp + off);
+          vw[t][ld] = nt_load16(kp + head_bytes + off);
+        }
+      }
+    };
+
+    f32x4 o[NMP];
+#pragma unroll
+    for (int b = 0; b < NMP; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;   // head c16
+
+    auto compute_step = [&](int k0, int lim, u32x4 (*kw)[NLD], u32x4 (*vw)[NLD])
+        __attribute__((always_inline)) {
+      // ---- S = K Q^T for the two groups ----
+      f32x4 sg[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        sg[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < NMQ; ++m) {
+          const u32x4 w = kw[t][m / H];
+          uint4 a;
+          if constexpr (FP8) {
+            const int h = m % H;
+            const uint32_t w0 = w[2 * h], w1 = w[2 * h + 1];
+            a.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.f, false));
+            a.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.f, true));
+            a.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.f, false));
+            a.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.f, true));
+          } else {
+            a = make_uint4(w[0], w[1], w[2], w[3]);
+          }
+          sg[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qb[m], sg[t], 0, 0, 0);
+        }
+      }
+      // ---- V rows of the step -> LDS as bf16: row 16 t + c16, elements d_of(ld) .. +E ----
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ld = 0; ld < NLD; ++ld) {
+          char* dst = vt + (16 * t + c16) * LROW + 2 * d_of(ld);
+          const u32x4 w = vw[t][ld];
+          if constexpr (FP8) {
+            uint32_t x[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              x[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[k], 1.f, false));
+              x[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[k], 1.f, true));
+            }
+            *reinterpret_cast<uint4*>(dst) = make_uint4(x[0], x[1], x[2], x[3]);
+            *reinterpret_cast<uint4*>(dst + 16) = make_uint4(x[4], x[5], x[6], x[7]);
+          } else {
+            *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+          }
+        }
+      // ---- logits of head c16 for tokens k0 + 16 t + 4 g4 + e, online softmax ----
+      float x[8];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float s = sg[t][e];
+          if (use_cap) {
+            const float e2 = __builtin_amdgcn_exp2f(s * cap_k);
+            s = cap_l2 * (1.f - 2.f * __builtin_amdgcn_rcpf(e2 + 1.f));
+          } else {
+            s *= c_log2;
+          }
+          x[4 * t + e] = (k0 + 16 * t + 4 * g4 + e < lim) ? s : -INFINITY;
+        }
+      float bm = x[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) bm = fmaxf(bm, x[i]);
+      bm = slots_max<4>(bm);                    // over the head's four lane groups
+      if (__any(bm > m_run + 8.f)) {
+        const float m_new = fmaxf(m_run, bm);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first step
+        m_run = m_new;
+        l_run *= alpha;
+        // O rows are heads 4 g4 + e: their alpha sits in lane 4 g4 + e
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a_e = __shfl(alpha, 4 * g4 + e);
+#pragma unroll
+          for (int b = 0; b < NMP; ++b) o[b][e] *= a_e;
+        }
+      }
+      float pr[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f(x[i] - m_run);
+        l_run += pr[i];
+      }
+      const uint4 pw = make_uint4(pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3]),
+                                  pack_bf16(pr[4], pr[5]), pack_bf16(pr[6], pr[7]));
+      const bf16x8 pa = __builtin_bit_cast(bf16x8, pw);
+      // ---- O += P V: B from the transposed V rows (tokens 4 g4 + j and 16 + 4 g4 + j) ----
+      const char* r1 = vt + (4 * g4 + (c16 >> 2)) * LROW + 8 * (c16 & 3);
+      const char* r2 = r1 + 16 * LROW;
+#pragma unroll
+      for (int b = 0; b < NMP; ++b) {
+        const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(r1 + 32 * b));
+        const i16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(r2 + 32 * b));
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        const i16x8 vb = {x1[0], x1[1], x1[2], x1[3], x2[0], x2[1], x2[2], x2[3]};
+        o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, vb), o[b], 0, 0, 0);
+      }
+    };
+
+    u32x4 kA[2][NLD], vA[2][NLD], kB[2][NLD], vB[2][NLD];
+    load_window(lo);
+    load_step(chunk_end(lo), lo, kA, vA);
+    for (int c_lo = lo;;) {
+      const int c_hi = chunk_end(c_lo);
+      for (int k0 = c_lo; k0 < c_hi; k0 += 64) {
+        load_step(c_hi, k0 + 32, kB, vB);
+        compute_step(k0, c_hi, kA, vA);
+        load_step(c_hi, k0 + 64, kA, vA);
+        compute_step(k0 + 32, c_hi, kB, vB);
+      }
+      if (c_hi >= hi) break;
+      c_lo = c_hi;
+      load_window(c_lo);
+      load_step(chunk_end(c_lo), c_lo, kA, vA);
+    }
+
+    // ---- epilogue: l of head c16 over its lane groups; O rows are heads 4 g4 + e ----
+    const float l_tot = slots_sum<4>(l_run);
+    const float vs = p.v_scale;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int hl = 4 * g4 + e;                 // head within the group
+      const float l_h = __shfl(l_tot, hl);
+      const float m_h = __shfl(m_run, hl);
+      if (hl >= G) continue;
+      const int h = g * G + hl;
+      if (part < 0) {
+        float ll = l_h, f = 1.f;
+        if (p.sink) {
+          const float sgk = p.sink[h] * kLog2e;
+          const float mx = fmaxf(m_h, sgk);
+          f = __builtin_amdgcn_exp2f(m_h - mx);
+          ll = ll * f + __builtin_amdgcn_exp2f(sgk - mx);
+        }
+        const float scale = f * vs / ll;
+        uint16_t* op = static_cast<uint16_t*>(p.out) + ((long long)token * p.Hq + h) * D;
+#pragma unroll
+        for (int b = 0; b < NMP; ++b) op[16 * b + c16] = (uint16_t)f32_to_bf16(o[b][e] * scale);
+      } else if (part < p.lay.max_parts) {
+        const long long pb = (long long)part * p.Hq + h;
+        if (c16 == 0) {
+          part_ml[2 * pb] = m_h;
+          part_ml[2 * pb + 1] = l_h;
+        }
+#pragma unroll
+        for (int b = 0; b < NMP; ++b) part_acc[pb * D + 16 * b + c16] = o[b][e];
+      }
+    }
+  }
+}
+
 // Stand-alone merge of the split partials (when no prefill kernel runs after
 // the row kernel to do it): four merge items per workgroup.
 template <typename QT, int D, int G>
@@ -639,9 +929,14 @@ struct RowCfg {
   // load rows per step: 4, or 2 where G x EPL = 64 accumulators leave no room
   // for two 4-row buffers at two waves per SIMD
   static constexpr int NR = (G * EPL >= 64 && (sizeof(CT) >= 2 || G >= 16)) ? 2 : 4;
+  // bf16 queries with G >= 8 q heads per kv head: the MFMA kernel
+  static constexpr bool MF = sizeof(QT) == 2 && G >= 8;
+  static const void* kernel() {
+    if constexpr (MF) return reinterpret_cast<const void*>(&mfma_row_kernel<CT, D, (MF ? G : 8)>);
+    else return reinterpret_cast<const void*>(&row_kernel<QT, CT, D, G, EPL, NR>);
+  }
   static int resident() {
-    static const int cap = resident_blocks(
-        reinterpret_cast<const void*>(&row_kernel<QT, CT, D, G, EPL, NR>), 64 * kWavesPerWG, 0);
+    static const int cap = resident_blocks(kernel(), 64 * kWavesPerWG, 0);
     return cap;
   }
 };
@@ -653,7 +948,8 @@ hipError_t launch_rows_t(const AttnParams& p, hipStream_t s) {
   const long long waves =
       (long long)row_chunks_max(Cfg::resident() * kWavesPerWG, p.Hkv) * p.Hkv;
   dim3 grid((unsigned)((waves + kWavesPerWG - 1) / kWavesPerWG));
-  row_kernel<QT, CT, D, G, Cfg::EPL, Cfg::NR><<<grid, 64 * kWavesPerWG, 0, s>>>(p);
+  if constexpr (Cfg::MF) mfma_row_kernel<CT, D, (Cfg::MF ? G : 8)><<<grid, 64 * kWavesPerWG, 0, s>>>(p);
+  else row_kernel<QT, CT, D, G, Cfg::EPL, Cfg::NR><<<grid, 64 * kWavesPerWG, 0, s>>>(p);
   return hipGetLastError();
 }
 
