@@ -615,16 +615,18 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
 // on the matrix cores and the wave keeps up with its loads.  Same plan, work
 // items, split partials and output as the VALU kernel.
 //
-// A step covers 32 tokens, two groups of 16.  Lane l: c16 = l % 16, g4 = l / 16.
+// A step covers 32 tokens, two groups of 16.  K and V rows are loaded whole
+// (16 bytes per lane, as many lanes as a row needs), widened to bf16 and
+// written to the wave's LDS, from which the MFMA operands are read.
+// Lane l: c16 = l % 16, g4 = l / 16.
 //   S = K Q^T per group (16 tokens x 16 heads): A = K, lane (token c16,
-//     d-slot block g4) straight from its 16-byte load; B = Q^T, lane (head c16,
-//     the same d slots).  The d order inside an MFMA is permuted identically
-//     in both operands.  S lands as lane (head c16, tokens 4 g4 .. 4 g4 + 3).
+//     d 32 m + 8 g4 .. + 8) by ds_read_b128; B = Q^T, lane (head c16, the same
+//     d).  S lands as lane (head c16, tokens 4 g4 .. 4 g4 + 3).
 //   O += P V (16 heads x 16 d per MFMA, k = 32 tokens): A = P, lane (head c16,
 //     token slots 8 g4 + j = tokens 4 g4 + j of group 0 and of group 1), i.e.
 //     exactly the p of the lane's own S values; B = V, lane (d c16, the same
 //     tokens), read transposed (ds_read_b64_tr_b16) from the wave's copy of
-//     the step's V rows in LDS (bf16, rows padded to spread the banks).
+//     the step's V rows in LDS (rows padded to spread the banks).
 //     O lands as lane (d c16 of the block, heads 4 g4 .. 4 g4 + 3).
 // Heads past G (G = 8) have zero q and are never stored.
 // ---------------------------------------------------------------------------
@@ -638,12 +640,16 @@ template <typename CT, int D>
 struct MfCfg {
   static constexpr int ESZ = (int)sizeof(CT);
   static constexpr int E = 16 / ESZ;         // elements per 16-byte load
-  static constexpr int NLD = D / (4 * E);    // 16-byte K (or V) loads per lane per 16 tokens
-  static constexpr int H = E / 8;            // q.k MFMAs fed by one load
+  static constexpr int LPTK = D * ESZ / 16;  // lanes per K (or V) row of a token
+  static constexpr int TPI = 64 / LPTK;      // tokens per load instruction
+  static constexpr int NLI = 32 / TPI;       // load instructions per step (K; as many for V)
   static constexpr int NMQ = D / 32;         // q.k MFMAs per 16 tokens
   static constexpr int NMP = D / 16;         // p.v MFMAs per step
-  static constexpr int LROW = 2 * D + 32;    // LDS bytes per staged V row
-  static constexpr int LWAVE = 32 * LROW;    // LDS bytes per wave
+  // staged bf16 rows, padded: K rows by 16 bytes (16 rows at one column hit
+  // distinct banks), V rows by 32 (4 rows x 32 bytes of a transposed read do)
+  static constexpr int LRK = 2 * D + 16;
+  static constexpr int LRV = 2 * D + 32;
+  static constexpr int LWAVE = 32 * (LRK + LRV);  // LDS bytes per wave
 };
 
 __device__ __forceinline__ u32x4 nt_load16(const char* p) {
@@ -653,11 +659,11 @@ __device__ __forceinline__ u32x4 nt_load16(const char* p) {
 template <typename CT, int D, int G>
 __global__ __launch_bounds__(64 * kWavesPerWG) void mfma_row_kernel(AttnParams p) {
   using Cfg = MfCfg<CT, D>;
-  constexpr int ESZ = Cfg::ESZ, E = Cfg::E, NLD = Cfg::NLD, H = Cfg::H, NMQ = Cfg::NMQ,
-                NMP = Cfg::NMP, LROW = Cfg::LROW;
+  constexpr int ESZ = Cfg::ESZ, E = Cfg::E, LPTK = Cfg::LPTK, TPI = Cfg::TPI, NLI = Cfg::NLI,
+                NMQ = Cfg::NMQ, NMP = Cfg::NMP, LRK = Cfg::LRK, LRV = Cfg::LRV;
   constexpr bool FP8 = sizeof(CT) == 1;
   static_assert(G == 8 || G == 16, "16-head MFMA columns");
-  static_assert(NLD >= 1 && H >= 1, "load split");
+  static_assert(LPTK >= 1 && TPI * NLI == 32, "load split");
   __shared__ __attribute__((aligned(16))) char s_v[kWavesPerWG * Cfg::LWAVE];
 
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(p.ws + p.lay.header);
@@ -669,7 +675,8 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void mfma_row_kernel(AttnParams p
   const int lane = lane_id();
   const int c16 = lane & 15, g4 = lane >> 4;
   const int wave = threadIdx.x >> 6;
-  char* vt = s_v + wave * Cfg::LWAVE;
+  char* kt = s_v + wave * Cfg::LWAVE;          // K rows of the step (bf16)
+  char* vt = kt + 32 * LRK;                     // V rows of the step (bf16)
   const int Hkv = p.Hkv;
   const int n_items = hdr->n_items;
   const long long total = (long long)hdr->n_chunks * Hkv;
@@ -690,8 +697,6 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void mfma_row_kernel(AttnParams p
   const int i_last = min(max(__builtin_amdgcn_readfirstlane(chunk_first[c + 1]), i_first), n_items);
   const char* kv_head = reinterpret_cast<const char*>(p.cache) + 2LL * g * p.Dpad * ESZ;
 
-  // this lane's d offset (elements) of load ld: 4 E ld + E g4
-  auto d_of = [&](int ld) { return 4 * E * ld + E * g4; };
 
   for (int ii = i_first; ii < i_last; ++ii) {
     const ItemDesc dsc = items[ii];
@@ -709,7 +714,7 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void mfma_row_kernel(AttnParams p
                            ((long long)token * p.Hq + g * G + (c16 < G ? c16 : 0)) * D;
 #pragma unroll
       for (int m = 0; m < NMQ; ++m) {
-        const int d0 = d_of(m / H) + 8 * (m % H);
+        const int d0 = 32 * m + 8 * g4;
         const uint4 v = (c16 < G) ? *reinterpret_cast<const uint4*>(qp + d0) : make_uint4(0, 0, 0, 0);
         qb[m] = __builtin_bit_cast(bf16x8, v);
       }
@@ -725,21 +730,33 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void mfma_row_kernel(AttnParams p
       const long long e = ((long long)(k >> sh) + 64) << sh;
       return e < hi ? (int)e : hi;
     };
-    // K and V pieces of the 32 tokens from k0 (tokens from lim on re-read lim - 1)
-    auto load_step = [&](int lim, int k0, u32x4 (*kw)[NLD], u32x4 (*vw)[NLD])
-        __attribute__((always_inline)) {
+    // K and V rows of the 32 tokens from k0: instruction i, lane l loads 16
+    // bytes of token k0 + TPI i + l / LPTK (tokens from lim on re-read lim - 1)
+    auto load_step = [&](int lim, int k0, u32x4* kw, u32x4* vw) __attribute__((always_inline)) {
+      const uint32_t off = 16u * (uint32_t)(lane % LPTK);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int tok = min(k0 + 16 * t + c16, lim - 1);
+      for (int i = 0; i < NLI; ++i) {
+        const int tok = min(k0 + TPI * i + lane / LPTK, lim - 1);
         const int page = __builtin_amdgcn_ds_bpermute(((tok >> sh) - pw0) << 2, page_reg);
         const uint32_t row = ((uint32_t)page << sh) | (uint32_t)(tok & pmask);
-        const char* kp = kv_head + (uint64_t)row * row_bytes;
+        const char* kp = kv_head + (uint64_t)row * row_bytes + off;
+        kw[i] = nt_load16(kp);
+        vw[i] = nt_load16(kp + head_bytes);
+      }
+    };
+    // one loaded 16-byte piece -> bf16 in LDS at dst (16 or 32 bytes)
+    auto stage = [&](const u32x4& w, char* dst) __attribute__((always_inline)) {
+      if constexpr (FP8) {
+        uint32_t x[8];
 #pragma unroll
-        for (int ld = 0; ld < NLD; ++ld) {
-          const uint32_t off = (uint32_t)(ESZ * d_of(ld));
-          kw[t][ld] = nt_load16(kp + off);
-          vw[t][ld] = nt_load16(kp + head_bytes + off);
+        for (int k = 0; k < 4; ++k) {
+          x[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[k], 1.f, false));
+          x[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[k], 1.f, true));
         }
+        *reinterpret_cast<uint4*>(dst) = make_uint4(x[0], x[1], x[2], x[3]);
+        *reinterpret_cast<uint4*>(dst + 16) = make_uint4(x[4], x[5], x[6], x[7]);
+      } else {
+        *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
       }
     };
 
@@ -748,50 +765,29 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void mfma_row_kernel(AttnParams p
     for (int b = 0; b < NMP; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;   // head c16
 
-    auto compute_step = [&](int k0, int lim, u32x4 (*kw)[NLD], u32x4 (*vw)[NLD])
-        __attribute__((always_inline)) {
+    // the step's K and V rows -> LDS as bf16 (row = token - k0)
+    auto stage_step = [&](const u32x4* kw, const u32x4* vw) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < NLI; ++i) {
+        const int r = TPI * i + lane / LPTK;
+        const int cb = 2 * E * (lane % LPTK);
+        stage(kw[i], kt + r * LRK + cb);
+        stage(vw[i], vt + r * LRV + cb);
+      }
+    };
+    auto compute_step = [&](int k0, int lim) __attribute__((always_inline)) {
       // ---- S = K Q^T for the two groups ----
       f32x4 sg[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         sg[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const char* kr = kt + (16 * t + c16) * LRK + 16 * g4;
 #pragma unroll
         for (int m = 0; m < NMQ; ++m) {
-          const u32x4 w = kw[t][m / H];
-          uint4 a;
-          if constexpr (FP8) {
-            const int h = m % H;
-            const uint32_t w0 = w[2 * h], w1 = w[2 * h + 1];
-            a.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.f, false));
-            a.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.f, true));
-            a.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.f, false));
-            a.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.f, true));
-          } else {
-            a = make_uint4(w[0], w[1], w[2], w[3]);
-          }
+          const uint4 a = *reinterpret_cast<const uint4*>(kr + 64 * m);
           sg[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qb[m], sg[t], 0, 0, 0);
         }
       }
-      // ---- V rows of the step -> LDS as bf16: row 16 t + c16, elements d_of(ld) .. +E ----
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int ld = 0; ld < NLD; ++ld) {
-          char* dst = vt + (16 * t + c16) * LROW + 2 * d_of(ld);
-          const u32x4 w = vw[t][ld];
-          if constexpr (FP8) {
-            uint32_t x[8];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              x[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[k], 1.f, false));
-              x[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[k], 1.f, true));
-            }
-            *reinterpret_cast<uint4*>(dst) = make_uint4(x[0], x[1], x[2], x[3]);
-            *reinterpret_cast<uint4*>(dst + 16) = make_uint4(x[4], x[5], x[6], x[7]);
-          } else {
-            *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-          }
-        }
       // ---- logits of head c16 for tokens k0 + 16 t + 4 g4 + e, online softmax ----
       float x[8];
 #pragma unroll
@@ -834,8 +830,8 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void mfma_row_kernel(AttnParams p
                                   pack_bf16(pr[4], pr[5]), pack_bf16(pr[6], pr[7]));
       const bf16x8 pa = __builtin_bit_cast(bf16x8, pw);
       // ---- O += P V: B from the transposed V rows (tokens 4 g4 + j and 16 + 4 g4 + j) ----
-      const char* r1 = vt + (4 * g4 + (c16 >> 2)) * LROW + 8 * (c16 & 3);
-      const char* r2 = r1 + 16 * LROW;
+      const char* r1 = vt + (4 * g4 + (c16 >> 2)) * LRV + 8 * (c16 & 3);
+      const char* r2 = r1 + 16 * LRV;
 #pragma unroll
       for (int b = 0; b < NMP; ++b) {
         const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(r1 + 32 * b));
@@ -846,21 +842,24 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void mfma_row_kernel(AttnParams p
       }
     };
 
-    u32x4 kA[2][NLD], vA[2][NLD], kB[2][NLD], vB[2][NLD];
+    // One register buffer: a step's rows go to LDS first, then the next
+    // step's loads are issued into the same registers and stay in flight while
+    // the step is computed from LDS.  The loads are unconditional (past the
+    // chunk they re-read its last token), so no wait drains them early.
+    u32x4 kb[NLI], vb[NLI];
     load_window(lo);
-    load_step(chunk_end(lo), lo, kA, vA);
+    load_step(chunk_end(lo), lo, kb, vb);
     for (int c_lo = lo;;) {
       const int c_hi = chunk_end(c_lo);
-      for (int k0 = c_lo; k0 < c_hi; k0 += 64) {
-        load_step(c_hi, k0 + 32, kB, vB);
-        compute_step(k0, c_hi, kA, vA);
-        load_step(c_hi, k0 + 64, kA, vA);
-        compute_step(k0 + 32, c_hi, kB, vB);
+      for (int k0 = c_lo; k0 < c_hi; k0 += 32) {
+        stage_step(kb, vb);
+        load_step(c_hi, k0 + 32, kb, vb);
+        compute_step(k0, c_hi);
       }
       if (c_hi >= hi) break;
       c_lo = c_hi;
       load_window(c_lo);
-      load_step(chunk_end(c_lo), c_lo, kA, vA);
+      load_step(chunk_end(c_lo), c_lo, kb, vb);
     }
 
     // ---- epilogue: l of head c16 over its lane groups; O rows are heads 4 g4 + e ----
