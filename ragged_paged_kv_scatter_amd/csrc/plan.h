@@ -66,6 +66,7 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
   int32_t* s_q0 = s_seq_rows + (p.max_num_seqs + 1);   // qsl[s], s <= num_seqs (cached)
   int32_t* s_ctx = s_q0 + (p.max_num_seqs + 1);        // kv_len - q_len (cached)
   __shared__ long long s_w64[kWaves + 1];
+  __shared__ long long s_w64b[kWaves + 1];
   __shared__ int32_t s_w32[kWaves + 1];
   __shared__ int32_t s_w32b[kWaves + 1];
   __shared__ int32_t s_w32c[kWaves + 1];
@@ -85,11 +86,11 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
 
   // ---- pass 1: per-sequence row counts, prefill tiles, visible-key totals ----
   int row_base = 0, pf_base = 0;
-  long long vis_total = 0;
+  long long vis_total = 0, pf_vis_total = 0;
   for (int base = 0; base < num_seqs; base += kT) {
     const int s = base + threadIdx.x;
     int n_rows = 0, n_pf = 0;
-    long long vis = 0;
+    long long vis = 0, pf_vis = 0;
     int q0 = 0, q_len = 0, ctx = 0;
     if (s < num_seqs) {
       q0 = p.qsl[s];
@@ -103,6 +104,7 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
       if (q_len > 0) {
         if (q_len >= p.prefill_min_q) {
           n_pf = (q_len + kPrefillBQ - 1) / kPrefillBQ;
+          pf_vis = visible_sum(ctx, q_len, W);
         } else {
           n_rows = q_len;
           vis = visible_sum(ctx, q_len, W);
@@ -110,10 +112,11 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
       }
     }
     int tot_rows, tot_pf;
-    long long tot_vis;
+    long long tot_vis, tot_pf_vis;
     const int my_row = block_exclusive_scan(n_rows, &tot_rows, s_w32) + row_base;
     const int my_pf = block_exclusive_scan(n_pf, &tot_pf, s_w32b) + pf_base;
     block_exclusive_scan(vis, &tot_vis, s_w64);
+    block_exclusive_scan(pf_vis, &tot_pf_vis, s_w64b);
     if (s < num_seqs) {
       s_seq_rows[s] = my_row;
       // heaviest tiles first within a sequence (causal: later tiles see more keys)
@@ -130,6 +133,7 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
     row_base += tot_rows;
     pf_base += tot_pf;
     vis_total += tot_vis;
+    pf_vis_total += tot_pf_vis;
   }
   if (threadIdx.x == 0) s_seq_rows[num_seqs] = row_base;
   __syncthreads();
@@ -140,7 +144,16 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
   // shorter); a chunk is the work of one wave per kv head, so the waves of the
   // row kernel get equal work, and only rows cut by a chunk boundary leave
   // split partials to merge. ----
-  const long long want = row_chunks_max(p.row_waves, p.Hkv);
+  // Side by side: when the batch has both decode rows and prefill tiles and
+  // the rows' HBM time (KV bytes at ~6 TB/s) is at least the tiles' MFMA time
+  // (4 D FLOPs per visible (query, key, q head) at ~1 PFLOP/s), the row kernel
+  // keeps kCoRowEighths / 8 of its resident waves and the prefill kernel,
+  // running at the same time on another stream, takes the rest of the CUs.
+  const long long dec_bytes = vis_total * 2 * p.Hkv * p.D * p.kv_elem;
+  const long long pf_flops = pf_vis_total * 4 * p.D * p.Hq;
+  const bool co_run = p.co_allowed && row_base > 0 && pf_base > 0 &&
+                      dec_bytes * 500 >= pf_flops * 3;
+  const long long want = row_chunks_max(co_run ? p.row_waves / 8 * kCoRowEighths : p.row_waves, p.Hkv);
   long long C = (vis_total + want - 1) / want;
   if (C < kMinSplit) C = kMinSplit;
   const int n_chunks = (int)min((vis_total + C - 1) / C, (long long)kTargetItems);
@@ -245,6 +258,7 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
     h.n_pf_items = min(pf_base, p.lay.max_pf_items);
     h.row_next = 0;
     h.pf_next = 0;
+    h.co_run = co_run ? 1 : 0;
     *hdr = h;
   }
 }

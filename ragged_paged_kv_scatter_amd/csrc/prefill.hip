@@ -230,12 +230,19 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
   // XCDs and the head slot -> (kv head = slot mod Hkv) mapping keeps the q
   // heads of one kv head on one XCD and L2.  Once a round's unit is past the
   // end, every later round's is too.
-  const bool snake = (gridDim.x & 7) == 0;
+  //
+  // When the planner runs this kernel beside the row kernel (co_run), only
+  // the first (8 - kCoRowEighths) / 8 of the grid (a multiple of 8) takes
+  // units, leaving the other slots of the CUs to the row kernel's waves.
+  unsigned grid = gridDim.x;
+  if (hdr->co_run && grid >= 64) grid = grid / 64 * (8 - kCoRowEighths) * 8;
+  if (blockIdx.x >= grid) return;
+  const bool snake = (grid & 7) == 0;
   for (long long k = 0;; ++k) {
-    const long long b = (snake && (k & 1)) ? (long long)(gridDim.x / 8 - 1 - blockIdx.x / 8) * 8 +
+    const long long b = (snake && (k & 1)) ? (long long)(grid / 8 - 1 - blockIdx.x / 8) * 8 +
                                                  (blockIdx.x & 7)
                                            : (long long)blockIdx.x;
-    const long long u = k * gridDim.x + b;
+    const long long u = k * grid + b;
     if (u >= n_units) break;
     const int item_i = (int)(u / Hq);
     const int hh = (int)(u - (long long)item_i * Hq);

@@ -105,6 +105,44 @@ hipEvent_t take_event() {
   return e;
 }
 
+// ---- the prefill kernel's own stream (one per device) ----------------------
+// rpa_forward forks the prefill kernel onto it after the planner and joins it
+// back before returning, so that prefill tiles can run beside the row kernel.
+// The fork / join events are shared by all callers on a device, hence the
+// lock around their record / wait pairs.
+constexpr int kMaxDevices = 64;
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+// The device's side stream, created on first use; caller holds g_side_mu.
+hipError_t side_stream(SideStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  SideStream& ss = g_side[dev];
+  if (!ss.s) {
+    hipStream_t st = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if ((e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&f, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&j, hipEventDisableTiming)) != hipSuccess) {
+      if (f) (void)hipEventDestroy(f);
+      (void)hipStreamDestroy(st);
+      return e;
+    }
+    ss.s = st;
+    ss.fork = f;
+    ss.join = j;
+  }
+  *out = &ss;
+  return hipSuccess;
+}
+
 }  // namespace
 
 void prof_begin(const char* name, hipStream_t s) {
@@ -367,6 +405,14 @@ int rpa_forward(const rpa_desc* desc, const rpa_options* opts, const void* queri
   pp.Hkv = desc->num_kv_heads;
   pp.row_waves = row_waves((rpa_dtype)desc->q_dtype, (rpa_dtype)desc->cache_dtype,
                            desc->head_dim, desc->num_q_heads / desc->num_kv_heads);
+  pp.Hq = desc->num_q_heads;
+  pp.D = desc->head_dim;
+  pp.kv_elem = elem_size(desc->cache_dtype);
+  // More tokens than sequences means some sequence has two or more queries,
+  // so the batch has prefill tiles: only then does the prefill kernel go to
+  // the side stream (decode-only batches keep one stream and no fork / join).
+  const bool side = prefill_supported(*desc) && desc->total_tokens > desc->max_num_seqs;
+  pp.co_allowed = side ? 1 : 0;
   // one launch: the planner, and the cache update when new tokens come along
   ScatterParams sp = {};
   if (keys)
@@ -403,22 +449,51 @@ int rpa_forward(const rpa_desc* desc, const rpa_options* opts, const void* queri
   ap.cap = opts->logits_soft_cap;
   const rpa_dtype qd = (rpa_dtype)desc->q_dtype, cd = (rpa_dtype)desc->cache_dtype;
 
-  // rows, then either the prefill kernel (which first merges the rows'
-  // split partials) or the stand-alone merge
+  if (!side) {
+    // one stream: rows, then the prefill kernel (which first merges the
+    // rows' split partials), or the stand-alone merge where the dtype has no
+    // prefill kernel
+    prof_begin("decode", s);
+    e = launch_rows(ap, qd, cd, s);
+    prof_end(s);
+    if (e != hipSuccess) return hip_fail(e);
+    if (prefill_supported(*desc)) {
+      ap.fuse_merge = 1;
+      prof_begin("prefill", s);
+      e = launch_prefill(ap, qd, cd, s);
+    } else {
+      prof_begin("merge", s);
+      e = launch_merge(ap, qd, s);
+    }
+    prof_end(s);
+    return e == hipSuccess ? RPA_OK : hip_fail(e);
+  }
+
+  // The prefill tiles on the side stream, the rows and then the merge of
+  // their splits on the caller's stream; the caller's stream waits for both.
+  // The planner's co_run flag sizes both kernels to share the CUs when the
+  // batch has enough of each kind of work.
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  SideStream* ss = nullptr;
+  if ((e = side_stream(&ss)) != hipSuccess) return hip_fail(e);
+  if ((e = hipEventRecord(ss->fork, s)) != hipSuccess ||
+      (e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess)
+    return hip_fail(e);
+  ap.fuse_merge = 0;
+  prof_begin("prefill", ss->s);
+  e = launch_prefill(ap, qd, cd, ss->s);
+  prof_end(ss->s);
+  if (e != hipSuccess) return hip_fail(e);
+  if ((e = hipEventRecord(ss->join, ss->s)) != hipSuccess) return hip_fail(e);
   prof_begin("decode", s);
   e = launch_rows(ap, qd, cd, s);
   prof_end(s);
   if (e != hipSuccess) return hip_fail(e);
-  if (prefill_supported(*desc)) {
-    ap.fuse_merge = 1;
-    prof_begin("prefill", s);
-    e = launch_prefill(ap, qd, cd, s);
-  } else {
-    prof_begin("merge", s);
-    e = launch_merge(ap, qd, s);
-  }
+  prof_begin("merge", s);
+  e = launch_merge(ap, qd, s);
   prof_end(s);
   if (e != hipSuccess) return hip_fail(e);
+  if ((e = hipStreamWaitEvent(s, ss->join, 0)) != hipSuccess) return hip_fail(e);
   return RPA_OK;
 }
 

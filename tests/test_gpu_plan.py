@@ -62,3 +62,59 @@ def test_plan_extremes_match_oracle(label):
     err = np.abs(o - ref[:n_valid]).max()
     print(f"[{label}] max_abs={err:.3e} tol={tolerance(w):.0e}", flush=True)
     assert err <= tolerance(w)
+
+
+# PlanHeader field order: num_seqs, n_rows, n_items, split, n_merge_rows,
+# n_pf_items, row_next, pf_next, n_chunks, co_run
+_CO_RUN = 9
+
+
+def _mode_case(label, seed):
+    rng = np.random.default_rng(seed)
+    args = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, q_dtype="bf16",
+                kv_in_dtype="bf16", cache_dtype="bf16", softmax_scale=1 / math.sqrt(128),
+                seed=seed, device="cuda", rng=rng)
+    if label == "decode_heavy":        # rows' HBM time exceeds the tile's MFMA time
+        q_lens = [1] * 32 + [64]
+        kv_lens = [int(x) for x in rng.integers(1500, 2500, size=32)] + [164]
+        dist = (32, 1, 0)
+    elif label == "prefill_heavy":     # one long chunk next to two short decode rows
+        q_lens, kv_lens, dist = [1, 1, 512], [50, 60, 1512], (2, 1, 0)
+    elif label == "one_stream":        # tokens <= sequences: prefill tile on the caller's stream
+        q_lens, kv_lens, dist = [1, 1, 0, 3, 0, 0], [700, 90, 40, 300, 5, 1], (2, 4, 0)
+    else:
+        raise KeyError(label)
+    return W.build(label, q_lens=q_lens, kv_lens=kv_lens, distribution=dist, **args)
+
+
+@pytest.mark.parametrize("label,co_run", [("decode_heavy", 1), ("prefill_heavy", 0),
+                                          ("one_stream", 0)])
+def test_side_by_side_modes_match_oracle(label, co_run):
+    """Batches with prefill tiles fork the prefill kernel onto a side stream;
+    the planner runs it beside the row kernel (each on half of every CU) only
+    when the rows' HBM time is at least the tiles' MFMA time.  Every mode
+    gives the oracle's output and cache."""
+    import ragged_paged_kv_scatter_amd as rpa
+    print(f"\n[case] plan mode {label}", flush=True)
+    w = _mode_case(label, seed=9300 + len(label))
+    poison_unused(w)
+    before = bits(w.kv_cache, w.cache_dtype)
+    ref, ref_cache = oracle_forward(w, cache_bits=before)
+    kv_t = torch.from_numpy(np.ascontiguousarray(w.kv_lens)).cuda()
+    bt_t = torch.from_numpy(np.ascontiguousarray(w.block_tables)).cuda()
+    nbytes = rpa.rpa_workspace_bytes(
+        rpa._desc(w.queries, rpa._dtype(w.keys), w.kv_cache, kv_t, bt_t),
+        rpa._options(**w.options(), chunk_prefill_size=None, num_kv_pages_per_block=None,
+                     num_queries_per_block=None, vmem_limit_bytes=None))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    out = gpu_forward(w, workspace=ws)
+    torch.cuda.synchronize()
+    hdr = ws[:64].view(torch.int32).cpu().numpy()
+    assert hdr[5] > 0, "the batch has prefill tiles"
+    assert hdr[_CO_RUN] == co_run
+    np.testing.assert_array_equal(bits(w.kv_cache, w.cache_dtype), ref_cache)
+    n_valid = int(w.query_start_loc[w.num_seqs])
+    o = out[:n_valid].double().cpu().numpy()
+    err = np.abs(o - ref[:n_valid]).max()
+    print(f"[{label}] co_run={hdr[_CO_RUN]} max_abs={err:.3e} tol={tolerance(w):.0e}", flush=True)
+    assert err <= tolerance(w)
