@@ -74,3 +74,42 @@ def test_sweep_case_matches_oracle(label):
     print(f"[{label}] max_abs={err:.3e} tol={tolerance(w):.0e}", flush=True)
     assert err <= tolerance(w)
     assert torch.isnan(out[n_valid:].float()).all()
+
+
+# Soft cap at head_dim 64 over the range of x = s * scale / cap: deep in the
+# saturated part of tanh, around its bend, and in its near-linear part.
+CAP_CASES = {
+    "saturated": (1.0, 1.0),         # (cap, softmax_scale): |x| ~ 8
+    "bend": (30.0, 1.0),             # x ~ N(0, 0.27)
+    "linear": (30.0, 0.125),         # x ~ N(0, 0.03)
+}
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+@pytest.mark.parametrize("label", list(CAP_CASES))
+def test_soft_cap_paths_d64(label, cache):
+    print(f"\n[case] soft cap {label} {cache}", flush=True)
+    cap, scale = CAP_CASES[label]
+    seed = 7300 + list(CAP_CASES).index(label) + (10 if cache == "fp8" else 0)
+    rng = np.random.default_rng(seed)
+    q_lens = [1, 1, 90, 200]
+    kv_lens = [int(rng.integers(50, 400)), 700, 90 + int(rng.integers(0, 200)), 350]
+    scales = (0.05, 0.05) if cache == "fp8" else (0.0, 0.0)
+    w = W.build(label, q_lens=q_lens, kv_lens=kv_lens, distribution=(2, 2, 0), num_q_heads=16,
+                num_kv_heads=2, head_dim=64, page_size=32, q_dtype="bf16", kv_in_dtype="bf16",
+                cache_dtype=cache, softmax_scale=scale, seed=seed, logits_soft_cap=cap,
+                k_scale=scales[0], v_scale=scales[1], device="cuda", rng=rng)
+    poison_unused(w)
+    before = bits(w.kv_cache, w.cache_dtype)
+    ref, ref_cache = oracle_forward(w, cache_bits=before)
+    out = gpu_forward(w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(w.kv_cache, w.cache_dtype), ref_cache)
+    n_valid = int(w.query_start_loc[w.num_seqs])
+    o = out[:n_valid].double().cpu().numpy()
+    err = np.abs(o - ref[:n_valid]).max()
+    rel = np.linalg.norm(o - ref[:n_valid]) / np.linalg.norm(ref[:n_valid])
+    print(f"[cap {label} {cache}] max_abs={err:.3e} rel={rel:.2e} tol={tolerance(w):.0e}",
+          flush=True)
+    assert err <= tolerance(w)
+    assert rel <= 2e-2
