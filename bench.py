@@ -25,15 +25,21 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
 
 
-def work_counts(w):
+def work_counts(w, split=False):
     """Algorithmic work of one step.
 
     kv_bytes: every KV token some query of a sequence can see is read once
     per sequence, 2 * Hkv * D * elem bytes per token (K and V of all heads).
     flops: 4 * D per visible (query, key, q head) triple (2D for q.k, 2D for p.v).
+    With split=True also returns the share of each attention kernel: the KV
+    bytes of the sequences the row kernel serves (q_len 1, or all of them for
+    f32, which has no prefill kernel) and the FLOPs of the prefill tiles.
     """
     kvb = 0
     pairs = 0
+    row_kvb = 0
+    pf_pairs = 0
+    has_prefill_kernel = w.q_dtype == "bf16"
     tok_bytes = 2 * w.num_kv_heads * w.head_dim * ELEM[w.cache_dtype]
     W = w.sliding_window
     for s in range(w.num_seqs):
@@ -49,7 +55,13 @@ def work_counts(w):
         if W:
             vis = np.minimum(vis, W)
         pairs += int(vis.sum())
+        if has_prefill_kernel and q_len >= 2:
+            pf_pairs += int(vis.sum())
+        else:
+            row_kvb += (kv - lo) * tok_bytes
     flops = 4 * w.head_dim * pairs * w.num_q_heads
+    if split:
+        return kvb, flops, row_kvb, 4 * w.head_dim * pf_pairs * w.num_q_heads
     return kvb, flops
 
 
@@ -413,22 +425,28 @@ def main():
     kstats = rpa.profile_read()
     ms = (t1 - t0) * 1e3 / args.steps
 
-    kvb, flops = work_counts(w)
+    kvb, flops, row_kvb, pf_flops = work_counts(w, split=True)
     decode_like = args.workload != "prefill_bf16"   # prefill reports TFLOP/s, the rest KV GB/s
     if decode_like:
         value, unit = kvb / (ms * 1e-3) / 1e9, "GB/s"
     else:
         value, unit = flops / (ms * 1e-3) / 1e12, "TFLOP/s"
-    # dominant kernel: the one with the largest summed time
-    dom = max(kstats.items(), key=lambda kv: kv[1][1]) if kstats else ("none", (1, 0.0))
+    # dominant kernel: of the two attention kernels, the one with the larger
+    # summed time among those with work in this batch (on the side-stream path
+    # a kernel with no work still spans the other's run while it waits for
+    # slots, so it is not a candidate); its roofline is priced on its own
+    # algorithmic work: the row kernel's KV bytes, the prefill tiles' FLOPs
+    cands = {k: v for k, v in kstats.items()
+             if (k == "decode" and row_kvb > 0) or (k == "prefill" and pf_flops > 0)}
+    dom = max(cands.items(), key=lambda kv: kv[1][1]) if cands else ("none", (1, 0.0))
     dom_name, (dom_n, dom_ms) = dom
     dom_avg_ms = dom_ms / max(dom_n, 1)
-    if dom_name == "prefill" and not decode_like:
-        achieved = flops / (dom_avg_ms * 1e-3) / 1e12
+    if dom_name == "prefill":
+        achieved = pf_flops / (dom_avg_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=achieved, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=achieved / BF16_PEAK_TFLOPS, traffic=None)
     else:
-        achieved = kvb / (dom_avg_ms * 1e-3) / 1e9
+        achieved = row_kvb / (dom_avg_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=achieved / HBM_PEAK_GBS, traffic=None)
     roof["kernel"] = dom_name
