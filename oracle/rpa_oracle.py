@@ -35,7 +35,7 @@ Sources (page titles and sections):
 * tpu-inference 0.11.1rc3 ``layers/vllm/attention.py``: new K/V are quantised
   to the cache dtype with k/v scales before the kernel (``quantize_kv``).
 
-Readings where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
 distribution = (n_decode, n_prefill, n_mixed) counts with num_seqs = their sum;
 combined head index 2h holds K and 2h+1 holds V, pad lanes zero-filled;
 soft cap is cap*tanh(s/cap) after all scales; the sink is a per-q-head logit
@@ -338,7 +338,7 @@ def written_slots(kv_lens, block_tables, query_start_loc, distribution, *, page_
 # mapping" step, cuda-graph padding with PAD_SLOT_ID, and populate_kv_cache's
 # reshape_and_cache_flash call on kv_cache[0], kv_cache[1] with the flattened
 # slot mapping, the cache dtype and the k/v scales).  The pages show the calls
-# only; the readings taken (listed in the design doc): a slot is
+# only; the readings taken: a slot is
 # block * block_size + offset of the token's position, rows past the last
 # sequence carry PAD_SLOT, and a store skips PAD_SLOT (and, as a guard, any
 # slot outside the pool).
@@ -391,7 +391,7 @@ def reshape_and_cache(key_cache_bits, value_cache_bits, keys_bits, values_bits, 
 # plane kv_cache[1] with one src_to_dst table; copy_blocks applies
 # ops.copy_blocks to the K and V planes of every layer's cache with one
 # src_to_dists table).  The pages show the calls only; the reading taken
-# (listed in the design doc): a table is int64 [n, 2] of (source block,
+# here: a table is int64 [n, 2] of (source block,
 # destination block) pairs and each pair copies one whole block, all of its
 # bytes; destinations are distinct and no destination is also a source.
 # ---------------------------------------------------------------------------

@@ -1,7 +1,7 @@
 """Builds librpa.so (the HIP kernels and the C ABI) in-tree with hipcc for gfx950.
 
-Run as ``python -m ragged_paged_kv_scatter_amd.build``; ``__graft_entry__.build()``
-calls :func:`build`.  Every call recompiles."""
+Run as ``python -m ragged_paged_kv_scatter_amd.build``, or call :func:`build`.
+Every call recompiles."""
 import os
 import subprocess
 import sys
