@@ -175,6 +175,16 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
   const float c_eff = CAP ? 1.f : c_scale;       // stored logits -> log2 units
   const float cap_k = CAP ? c_scale * 2.f * kLog2e / p.cap : 0.f;
   const float cap_l2 = CAP ? p.cap * kLog2e : 0.f;
+  // With a soft cap, a block keeps r = 1 / (2^a + 1) per logit, with
+  // a = q.k * cap_k = 2 x log2 e for x = q.k * scale / cap, instead of the
+  // capped logit
+  // cap log2 e tanh(x) = cap_l2 (1 - 2 r): the row max becomes a min over r
+  // (a masked logit is r = +inf) and p = 2^(cap_l2 (1 - 2 r) - m) is one fma
+  // and one exp2.
+  constexpr float kRedInit = CAP ? INFINITY : -INFINITY;
+  auto red = [](float a, float b) { return CAP ? fminf(a, b) : fmaxf(a, b); };
+  // reduced block value -> row max in log2 units
+  auto to_mx = [&](float v) { return CAP ? fmaf(v, -2.f * cap_l2, cap_l2) : v * c_eff; };
 
   // Direct loads: instruction j of a wave writes LDS rows 16 wave + RPI j +
   // lane / CPR, physical chunk lane % CPR, which holds logical chunk
@@ -410,9 +420,8 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
     // k0 + 32 (e >> 4) + 8 ((e & 15) >> 2) + 4 kg + (e & 3)
     auto logit = [&](auto masked, int k0, float s, int e) __attribute__((always_inline)) -> float {
       if constexpr (CAP) {
-        // cap * tanh(s * scale / cap) in log2 units, tanh(x) = 1 - 2 / (e^{2x} + 1)
-        const float e2 = __builtin_amdgcn_exp2f(s * cap_k);
-        s = cap_l2 * (1.f - 2.f * __builtin_amdgcn_rcpf(e2 + 1.f));
+        // tanh(x) = 1 - 2 r with r = 1 / (e^{2x} + 1)
+        s = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(s * cap_k) + 1.f);
       }
       if constexpr (decltype(masked)::value) {
         // key j = k0 + 4 kg + ko with ko a constant: visible iff
@@ -420,7 +429,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
         const int ko = (e >> 4) * 32 + ((e & 15) >> 2) * 8 + (e & 3);
         const int lim = pos - k0 - 4 * kg;
         const bool vis = ko <= lim && (W <= 0 || ko > lim - W);
-        s = vis ? s : -INFINITY;
+        s = vis ? s : kRedInit;
       }
       return s;
     };
@@ -445,6 +454,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
           for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
       }
       const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      const float c_bias = cap_l2 - m_use;                 // cap path: p = 2^(c_bias - 2 cap_l2 r)
       const char* kn = kbuf(blk + 1);
       const char* vb = vbuf(blk);
       __builtin_amdgcn_sched_barrier(0);
@@ -460,7 +470,8 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
       uint32_t pk[16];
       float ls0 = 0.f, ls1 = 0.f;
       auto expo = [&](int e) __attribute__((always_inline)) {
-        pf[e] = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 4][e & 15], c_eff, -m_use));
+        pf[e] = CAP ? __builtin_amdgcn_exp2f(fmaf(sacc[e >> 4][e & 15], -2.f * cap_l2, c_bias))
+                    : __builtin_amdgcn_exp2f(fmaf(sacc[e >> 4][e & 15], c_eff, -m_use));
         if (e & 1) {
           pk[e >> 1] = pack_bf16(pf[e - 1], pf[e]);
           const bf16x2 pw = __builtin_bit_cast(bf16x2, pk[e >> 1]);
@@ -503,7 +514,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
 
       // (2) O^T += V^T(b) P^T(b)
       const int k0n = (blk + 1) * BK;
-      float m0 = -INFINITY, m1 = -INFINITY;
+      float m0 = kRedInit, m1 = kRedInit;
       bf16x8 va = ld_vt(vb, 0, 0);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -526,8 +537,8 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
               const int e = (m - 2 * DT) * MB + x;
               const float sv = logit(mask_next, k0n, s2[e >> 4][e & 15], e);
               s2[e >> 4][e & 15] = sv;
-              if (x & 1) m1 = fmaxf(m1, sv);
-              else m0 = fmaxf(m0, sv);
+              if (x & 1) m1 = red(m1, sv);
+              else m0 = red(m0, sv);
             }
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -536,8 +547,8 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
       }
       __builtin_amdgcn_s_setprio(0);
       l_run += ls0 + ls1;
-      mx = fmaxf(m0, m1);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c_eff;
+      const float mr = red(m0, m1);
+      mx = to_mx(red(mr, __shfl_xor(mr, 32)));
       end_step(blk);
     };
     // steps [blk, end) in pairs; on return S(blk) is in sa again
@@ -577,13 +588,14 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
         sa[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_k(kb, ks, 0), qreg[ks], sa[0], 0, 0, 0);
         sa[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_k(kb, ks, 1), qreg[ks], sa[1], 0, 0, 0);
       }
+      float t = kRedInit;
 #pragma unroll
       for (int e = 0; e < 32; ++e) {
         const float s = logit(std::true_type{}, b0 * BK, sa[e >> 4][e & 15], e);
         sa[e >> 4][e & 15] = s;
-        mx = fmaxf(mx, s);
+        t = red(t, s);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c_eff;
+      mx = to_mx(red(t, __shfl_xor(t, 32)));
     }
     if constexpr (!DIRECT) {
       stage_staged(vr, vbuf(b0));
