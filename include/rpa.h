@@ -42,7 +42,8 @@
  *   differential_flash_attn.py, context_len/query_len/seq_len diagram), so
  *   query t sits at position kv_len - q_len + t and sees keys j <= that
  *   position (and, with a window W > 0, the W most recent of them).
- * - Device-side preconditions (documented, not checked):
+ * - Device-side preconditions (not checked by the update or the attention
+ *   calls; rpa_validate_metadata checks them on the device):
  *   0 <= q_len <= kv_len <= pages_per_seq*page_size; qsl non-decreasing from
  *   0 with qsl[num_seqs] <= total_tokens; block-table entries that cover
  *   [0, kv_len) are < num_pages; the slots written by one update are
@@ -234,6 +235,35 @@ int rpa_forward(const rpa_desc* desc, const rpa_options* opts, const void* queri
                 const int32_t* block_tables, const int32_t* query_start_loc,
                 const int32_t* distribution, const float* attention_sink, void* out,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bits of the device status word written by rpa_validate_metadata. */
+enum {
+  RPA_META_QSL = 1,           /* qsl[0] != 0, qsl decreasing, or qsl[num_seqs] > total_tokens */
+  RPA_META_LENS = 2,          /* kv_len < 0, q_len > kv_len, or kv_len > pages_per_seq*page_size */
+  RPA_META_BLOCK_TABLE = 4,   /* an entry covering [0, kv_len) outside [0, num_pages) */
+  RPA_META_SLOTS = 8,         /* two new tokens of the update map to one cache slot */
+  RPA_META_DISTRIBUTION = 16  /* a negative count, or counts summing past max_num_seqs */
+};
+
+/* Device-side check of the metadata preconditions listed at the top of this
+ * file, for the sizes in `desc` (total_tokens, max_num_seqs, pages_per_seq,
+ * num_pages, page_size).  The pages state the cache-update rule (position
+ * kv_len - q_len + t of a sequence goes to slot (block_tables page, offset))
+ * but not what an inconsistent table does; the update and attention calls do
+ * not check it on the device, so a caller can run this first.
+ * Enqueues three small kernels on `stream` and returns without a host sync;
+ * when they have run, *status (device int32) holds the OR of the RPA_META_*
+ * bits of every violated precondition, 0 when all hold.  slot_bits is device
+ * scratch of (num_pages * page_size + 31) / 32 uint32 words, caller owned,
+ * contents need not be initialised (cleared by a fill kernel, so the call can
+ * be captured in a HIP graph).  Every read stays inside the documented array
+ * sizes whatever their contents.  Returns RPA_OK or a host-side error code
+ * (NULL pointer, invalid shape, HIP launch failure).
+ */
+int rpa_validate_metadata(const rpa_desc* desc, const int32_t* kv_lens,
+                          const int32_t* block_tables, const int32_t* query_start_loc,
+                          const int32_t* distribution, uint32_t* slot_bits, int32_t* status,
+                          void* stream);
 
 /* Human-readable text of a status code (for RPA_ERR_HIP, includes the last
  * HIP error seen by the library). */

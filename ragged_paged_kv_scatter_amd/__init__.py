@@ -18,8 +18,12 @@ from . import _lib
 from ._lib import RpaDesc, RpaError, RpaKernelStat, RpaOptions
 
 __all__ = ["rpa_update_kv_cache", "rpa_forward", "rpa_workspace_bytes", "rpa_slot_mapping",
-           "rpa_reshape_and_cache", "rpa_copy_blocks", "rpa_swap_blocks", "profile_enable",
-           "profile_read", "RpaError"]
+           "rpa_reshape_and_cache", "rpa_copy_blocks", "rpa_swap_blocks",
+           "rpa_validate_metadata", "profile_enable", "profile_read", "RpaError",
+           "META_QSL", "META_LENS", "META_BLOCK_TABLE", "META_SLOTS", "META_DISTRIBUTION"]
+
+# bits of rpa_validate_metadata's status word (include/rpa.h RPA_META_*)
+META_QSL, META_LENS, META_BLOCK_TABLE, META_SLOTS, META_DISTRIBUTION = 1, 2, 4, 8, 16
 
 _DT = {torch.float32: _lib.RPA_F32, torch.bfloat16: _lib.RPA_BF16, torch.uint8: _lib.RPA_FP8_E4M3,
        torch.float8_e4m3fn: _lib.RPA_FP8_E4M3}
@@ -123,6 +127,31 @@ def rpa_update_kv_cache(keys, values, kv_cache, kv_lens, block_tables, query_sta
         _ptr(block_tables), _ptr(query_start_loc), _ptr(distribution),
         float(k_scale or 0.0), float(v_scale or 0.0), _stream(dev)))
     return kv_cache
+
+
+def rpa_validate_metadata(queries, kv_cache, kv_lens, block_tables, query_start_loc,
+                          distribution, *, kv_in_dtype=None, status=None, slot_bits=None):
+    """Check on the device the metadata preconditions of rpa_update_kv_cache and
+    rpa_forward for these tensors' sizes.  Returns the device int32[1] status
+    tensor (the OR of META_* bits, 0 when all hold); the C call does not
+    synchronise, so read it with ``int(status.item())``."""
+    dev = _check_dev(queries, kv_cache, kv_lens, block_tables, query_start_loc, distribution)
+    for t, n in ((kv_lens, "kv_lens"), (block_tables, "block_tables"),
+                 (query_start_loc, "query_start_loc"), (distribution, "distribution")):
+        _meta(t, n)
+    kin = kv_in_dtype if kv_in_dtype is not None else _dtype(kv_cache)
+    d = _desc(queries, kin, kv_cache, kv_lens, block_tables)
+    words = (d.num_pages * d.page_size + 31) // 32
+    if slot_bits is None:
+        slot_bits = torch.empty(words, dtype=torch.int32, device=dev)
+    elif slot_bits.numel() < words or slot_bits.dtype != torch.int32:
+        raise ValueError(f"slot_bits must be int32 with at least {words} elements")
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=dev)
+    _lib.check(_lib.load().rpa_validate_metadata(
+        ctypes.byref(d), _ptr(kv_lens), _ptr(block_tables), _ptr(query_start_loc),
+        _ptr(distribution), _ptr(slot_bits), _ptr(status), _stream(dev)))
+    return status
 
 
 def _flat_desc(total_tokens, max_num_seqs, pages_per_seq, num_pages, page_size, num_kv_heads,

@@ -14,7 +14,8 @@ STATUS = {0: "RPA_OK", 1: "RPA_ERR_NULL_POINTER", 2: "RPA_ERR_INVALID_SHAPE",
           6: "RPA_ERR_HIP"}
 EXPORTS = ("rpa_update_kv_cache", "rpa_workspace_bytes", "rpa_forward", "rpa_error_string",
            "rpa_profile_enable", "rpa_profile_read", "rpa_slot_mapping",
-           "rpa_reshape_and_cache", "rpa_copy_blocks", "rpa_swap_blocks")
+           "rpa_reshape_and_cache", "rpa_copy_blocks", "rpa_swap_blocks",
+           "rpa_validate_metadata")
 
 
 class RpaDesc(ctypes.Structure):
@@ -90,6 +91,8 @@ def load():
     lib.rpa_swap_blocks.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P,
                                     ctypes.c_int32, P]
     lib.rpa_swap_blocks.restype = ctypes.c_int
+    lib.rpa_validate_metadata.argtypes = [ctypes.POINTER(RpaDesc), P, P, P, P, P, P, P]
+    lib.rpa_validate_metadata.restype = ctypes.c_int
     del I32P
     _lib = lib
     return lib

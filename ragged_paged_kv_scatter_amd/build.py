@@ -12,7 +12,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "librpa.so")
-SOURCES = ["rpa_api.cpp", "scatter.hip", "plan.hip", "decode.hip", "prefill.hip", "slots.hip"]
+SOURCES = ["rpa_api.cpp", "scatter.hip", "plan.hip", "decode.hip", "prefill.hip", "slots.hip",
+           "validate.hip"]
 ARCH = os.environ.get("RPA_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

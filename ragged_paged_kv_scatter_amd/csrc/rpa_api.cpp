@@ -363,6 +363,34 @@ int rpa_swap_blocks(const void* src_cache, void* dst_cache, int64_t src_blocks,
   return RPA_OK;
 }
 
+int rpa_validate_metadata(const rpa_desc* desc, const int32_t* kv_lens,
+                          const int32_t* block_tables, const int32_t* query_start_loc,
+                          const int32_t* distribution, uint32_t* slot_bits, int32_t* status,
+                          void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if ((st = check_meta(kv_lens, block_tables, query_start_loc, distribution))) return st;
+  if (!slot_bits || !status) return RPA_ERR_NULL_POINTER;
+  ValidateParams p = {};
+  p.kv_lens = kv_lens;
+  p.block_tables = block_tables;
+  p.qsl = query_start_loc;
+  p.dist = distribution;
+  p.slot_bits = slot_bits;
+  p.status = status;
+  p.slot_words = ((long long)desc->num_pages * desc->page_size + 31) / 32;
+  p.max_num_seqs = desc->max_num_seqs;
+  p.T = desc->total_tokens;
+  p.pps = desc->pages_per_seq;
+  p.page_size = desc->page_size;
+  p.num_pages = desc->num_pages;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  prof_begin("validate", s);
+  const hipError_t e = launch_validate(p, s);
+  prof_end(s);
+  return e == hipSuccess ? RPA_OK : hip_fail(e);
+}
+
 int rpa_workspace_bytes(const rpa_desc* desc, const rpa_options* opts, size_t* bytes) {
   int st = check_desc(desc);
   if (st) return st;

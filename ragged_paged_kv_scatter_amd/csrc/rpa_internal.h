@@ -191,6 +191,18 @@ hipError_t launch_prefill(const AttnParams& p, rpa_dtype q_dt, rpa_dtype cache_d
                           hipStream_t s);
 bool prefill_supported(const rpa_desc& d);
 hipError_t launch_slot_mapping(const SlotMapParams& p, hipStream_t s);
+
+struct ValidateParams {   // rpa_validate_metadata
+  const int32_t* kv_lens;
+  const int32_t* block_tables;
+  const int32_t* qsl;
+  const int32_t* dist;
+  uint32_t* slot_bits;    // one bit per cache slot (num_pages * page_size)
+  int32_t* status;        // OR of RPA_META_* bits
+  long long slot_words;
+  int32_t max_num_seqs, T, pps, page_size, num_pages;
+};
+hipError_t launch_validate(const ValidateParams& p, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t s);
 hipError_t launch_reshape_and_cache(const ReshapeParams& p, rpa_dtype in_dt, rpa_dtype cache_dt,
                                     hipStream_t s);

@@ -134,6 +134,21 @@ def test_split_cache_calls_check_before_launch(lib):
                                      None) == 3
 
 
+def test_metadata_check_checks_before_launch(lib):
+    d = good_desc()
+    fake = ctypes.c_void_p(4096)   # never dereferenced: every call below fails host checks
+    # NULL status word, NULL slot bitmap, NULL metadata, NULL or unsupported desc
+    assert lib.rpa_validate_metadata(ctypes.byref(d), fake, fake, fake, fake, fake, None,
+                                     None) == 1
+    assert lib.rpa_validate_metadata(ctypes.byref(d), fake, fake, fake, fake, None, fake,
+                                     None) == 1
+    assert lib.rpa_validate_metadata(ctypes.byref(d), fake, None, fake, fake, fake, fake,
+                                     None) == 1
+    assert lib.rpa_validate_metadata(None, fake, fake, fake, fake, fake, fake, None) == 1
+    assert lib.rpa_validate_metadata(ctypes.byref(good_desc(page_size=24)), fake, fake, fake,
+                                     fake, fake, fake, None) == 3
+
+
 def test_block_copy_calls_check_before_launch(lib):
     fake = ctypes.c_void_p(4096)
     arr = (ctypes.c_void_p * 2)(4096, 8192)
