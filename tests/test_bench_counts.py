@@ -1,0 +1,59 @@
+"""The algorithmic work bench.py prices its rooflines on, checked on the CPU
+against closed forms: the tiny batch by hand, causal prefill pair counts, the
+window's cap on visible keys, and the split between the two attention
+kernels (row kernel: q_len 1 sequences, or all of them for f32; prefill
+kernel: the rest)."""
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from ragged_paged_kv_scatter_amd import workloads as W  # noqa: E402
+
+
+def test_tiny_batch_by_hand():
+    # q {1,1,5}, kv {9,17,5}: visible pairs 9 + 17 + (1+2+3+4+5) = 41; 4 q heads, D 64
+    w = W.make("tiny_fp32")
+    kvb, flops, row_kvb, pf_flops = bench.work_counts(w, split=True)
+    tok = 2 * 2 * 64 * 4                          # K+V of 2 kv heads, D 64, f32
+    assert kvb == (9 + 17 + 5) * tok
+    assert flops == 4 * 64 * 41 * 4
+    assert row_kvb == kvb and pf_flops == 0       # f32: every row to the row kernel
+
+
+def test_long_prefill_closed_form():
+    w = W.make("prefill_bf16")
+    kvb, flops, row_kvb, pf_flops = bench.work_counts(w, split=True)
+    n = 8192
+    assert flops == 2 * 64 * (n * (n + 1) // 2) * 4 * 128
+    assert kvb == 2 * n * 2 * 8 * 128 * 2
+    assert row_kvb == 0 and pf_flops == flops
+
+
+def test_split_partitions_the_step():
+    for name in ("decode_bf16", "mixed_bf16", "fp8_full"):
+        w = W.make(name, small=True)
+        kvb, flops, row_kvb, pf_flops = bench.work_counts(w, split=True)
+        q = np.diff(np.asarray(w.query_start_loc))[:w.num_seqs]
+        assert 0 <= row_kvb <= kvb and 0 <= pf_flops <= flops
+        if (q >= 2).any():
+            assert pf_flops > 0
+        else:
+            assert pf_flops == 0 and row_kvb == kvb
+        if (q == 1).any():
+            assert row_kvb > 0
+
+
+def test_window_caps_visible_keys():
+    # one decode row with kv 5000 and window 4096 sees 4096 keys
+    w = W.build("win", q_lens=[1], kv_lens=[5000], distribution=(1, 0, 0), num_q_heads=8,
+                num_kv_heads=1, head_dim=64, page_size=32, q_dtype="bf16", kv_in_dtype="bf16",
+                cache_dtype="fp8", softmax_scale=0.125, seed=3, sliding_window=4096,
+                k_scale=0.05, v_scale=0.05, rng=np.random.default_rng(3))
+    kvb, flops = bench.work_counts(w)
+    assert kvb == 4096 * 2 * 1 * 64 * 1
+    assert flops == 4 * 64 * 4096 * 8
