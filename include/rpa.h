@@ -225,7 +225,7 @@ int rpa_workspace_bytes(const rpa_desc* desc, const rpa_options* opts, size_t* b
  * Concurrent calls must use distinct workspaces.
  * When the batch has more tokens than max_num_seqs (so some sequence has
  * prefill rows), the prefill kernel runs on the library's own stream for the
- * current device (created with two events on the first such call and kept
+ * device of `stream` (created with two events on the first such call and kept
  * until the process ends): it is forked off `stream` after the planner and
  * joined back before the call returns, so all of the call's work is still
  * ordered on `stream`, including under HIP graph capture.

@@ -302,11 +302,12 @@ def rpa_forward(queries, keys, values, kv_cache, kv_lens, block_tables, query_st
     if out is None:
         out = torch.empty(queries.shape, dtype=queries.dtype, device=dev)
     lib = _lib.load()
-    _lib.check(lib.rpa_forward(
-        ctypes.byref(d), ctypes.byref(o), _ptr(queries), _ptr(keys), _ptr(values),
-        _ptr(kv_cache), _ptr(kv_lens), _ptr(block_tables), _ptr(query_start_loc),
-        _ptr(distribution), _ptr(attention_sink), _ptr(out), _ptr(workspace),
-        ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(dev)))
+    with torch.cuda.device(dev):    # the library sizes launches for the current device
+        _lib.check(lib.rpa_forward(
+            ctypes.byref(d), ctypes.byref(o), _ptr(queries), _ptr(keys), _ptr(values),
+            _ptr(kv_cache), _ptr(kv_lens), _ptr(block_tables), _ptr(query_start_loc),
+            _ptr(distribution), _ptr(attention_sink), _ptr(out), _ptr(workspace),
+            ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(dev)))
     return out, kv_cache
 
 

@@ -118,21 +118,32 @@ struct SideStream {
 std::mutex g_side_mu;
 SideStream g_side[kMaxDevices];
 
-// The device's side stream, created on first use; caller holds g_side_mu.
-hipError_t side_stream(SideStream** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+// The side stream of the device that `caller` (NULL: the current device's
+// default stream) belongs to, created on first use with that device current;
+// the caller holds g_side_mu.
+hipError_t side_stream(hipStream_t caller, SideStream** out) {
+  int dev = 0, cur = 0;
+  hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return e;
+  dev = cur;
+  if (caller) {
+    hipDevice_t d = 0;
+    if ((e = hipStreamGetDevice(caller, &d)) != hipSuccess) return e;
+    dev = d;
+  }
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   SideStream& ss = g_side[dev];
   if (!ss.s) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
     hipStream_t st = nullptr;
     hipEvent_t f = nullptr, j = nullptr;
-    if ((e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&f, hipEventDisableTiming)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&j, hipEventDisableTiming)) != hipSuccess) {
+    e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+    if (e == hipSuccess && (e = hipEventCreateWithFlags(&f, hipEventDisableTiming)) == hipSuccess)
+      e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess) {
       if (f) (void)hipEventDestroy(f);
-      (void)hipStreamDestroy(st);
+      if (st) (void)hipStreamDestroy(st);
       return e;
     }
     ss.s = st;
@@ -503,7 +514,7 @@ int rpa_forward(const rpa_desc* desc, const rpa_options* opts, const void* queri
   // batch has enough of each kind of work.
   std::lock_guard<std::mutex> lk(g_side_mu);
   SideStream* ss = nullptr;
-  if ((e = side_stream(&ss)) != hipSuccess) return hip_fail(e);
+  if ((e = side_stream(s, &ss)) != hipSuccess) return hip_fail(e);
   if ((e = hipEventRecord(ss->fork, s)) != hipSuccess ||
       (e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess)
     return hip_fail(e);
