@@ -259,7 +259,7 @@ __device__ __forceinline__ void store_slice(QT* o, long long base, const float* 
   }
 }
 
-template <typename QT, typename CT, int D, int G, int EPL, int NR>
+template <typename QT, typename CT, int D, int G, int EPL, int NR, bool CAP>
 __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
   constexpr bool F32 = sizeof(CT) == 4;
   constexpr int LPT = D / EPL;          // lanes per token
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
   const uint32_t row_bytes = 2u * Hkv * p.Dpad * (uint32_t)sizeof(CT);  // one cache token row
   const uint32_t head_bytes = p.Dpad * (uint32_t)sizeof(CT);            // K -> V of a head
   const CT* cache = static_cast<const CT*>(p.cache);
-  const bool use_cap = p.cap > 0.f;
+  constexpr bool use_cap = CAP;       // logits soft cap on (p.cap > 0), chosen at launch
   const float c_log2 = p.qk_scale * kLog2e;
   const float cap_k = use_cap ? p.qk_scale * 2.f * kLog2e / p.cap : 0.f;  // x -> 2x log2 e
   const float cap_l2 = p.cap * kLog2e;
@@ -656,7 +656,7 @@ __device__ __forceinline__ u32x4 nt_load16(const char* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-template <typename CT, int D, int G>
+template <typename CT, int D, int G, bool CAP>
 __global__ __launch_bounds__(64 * kWavesPerWG) void mfma_row_kernel(AttnParams p) {
   using Cfg = MfCfg<CT, D>;
   constexpr int ESZ = Cfg::ESZ, E = Cfg::E, LPTK = Cfg::LPTK, TPI = Cfg::TPI, NLI = Cfg::NLI,
@@ -684,7 +684,7 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void mfma_row_kernel(AttnParams p
   const int pmask = (1 << sh) - 1;
   const uint32_t row_bytes = 2u * Hkv * p.Dpad * (uint32_t)ESZ;
   const uint32_t head_bytes = p.Dpad * (uint32_t)ESZ;
-  const bool use_cap = p.cap > 0.f;
+  constexpr bool use_cap = CAP;       // logits soft cap on (p.cap > 0), chosen at launch
   const float c_log2 = p.qk_scale * kLog2e;
   const float cap_k = use_cap ? p.qk_scale * 2.f * kLog2e / p.cap : 0.f;
   const float cap_l2 = p.cap * kLog2e;
@@ -920,7 +920,7 @@ int resident_blocks(const void* kernel, int block_threads, size_t lds) {
 }
 
 // Row kernel configuration for these types and sizes.
-template <typename QT, typename CT, int D, int G>
+template <typename QT, typename CT, int D, int G, bool CAP>
 struct RowCfg {
   // elements per lane: one 16-byte load, at most 64 accumulators per lane
   static constexpr int E16 = 16 / (int)sizeof(CT);
@@ -931,8 +931,8 @@ struct RowCfg {
   // bf16 queries with G >= 8 q heads per kv head: the MFMA kernel
   static constexpr bool MF = sizeof(QT) == 2 && G >= 8;
   static const void* kernel() {
-    if constexpr (MF) return reinterpret_cast<const void*>(&mfma_row_kernel<CT, D, (MF ? G : 8)>);
-    else return reinterpret_cast<const void*>(&row_kernel<QT, CT, D, G, EPL, NR>);
+    if constexpr (MF) return reinterpret_cast<const void*>(&mfma_row_kernel<CT, D, (MF ? G : 8), CAP>);
+    else return reinterpret_cast<const void*>(&row_kernel<QT, CT, D, G, EPL, NR, CAP>);
   }
   static int resident() {
     static const int cap = resident_blocks(kernel(), 64 * kWavesPerWG, 0);
@@ -940,70 +940,83 @@ struct RowCfg {
   }
 };
 
-template <typename QT, typename CT, int D, int G>
+template <typename QT, typename CT, int D, int G, bool CAP>
 hipError_t launch_rows_t(const AttnParams& p, hipStream_t s) {
-  using Cfg = RowCfg<QT, CT, D, G>;
+  using Cfg = RowCfg<QT, CT, D, G, CAP>;
   // one wave per (chunk, kv head) for as many chunks as the planner may make
   const long long waves =
       (long long)row_chunks_max(Cfg::resident() * kWavesPerWG, p.Hkv) * p.Hkv;
   dim3 grid((unsigned)((waves + kWavesPerWG - 1) / kWavesPerWG));
-  if constexpr (Cfg::MF) mfma_row_kernel<CT, D, (Cfg::MF ? G : 8)><<<grid, 64 * kWavesPerWG, 0, s>>>(p);
-  else row_kernel<QT, CT, D, G, Cfg::EPL, Cfg::NR><<<grid, 64 * kWavesPerWG, 0, s>>>(p);
+  if constexpr (Cfg::MF) mfma_row_kernel<CT, D, (Cfg::MF ? G : 8), CAP><<<grid, 64 * kWavesPerWG, 0, s>>>(p);
+  else row_kernel<QT, CT, D, G, Cfg::EPL, Cfg::NR, CAP><<<grid, 64 * kWavesPerWG, 0, s>>>(p);
   return hipGetLastError();
 }
 
-template <typename QT, typename CT, int D>
+template <typename QT, typename CT, int D, bool CAP>
 int row_waves_g(int G) {
   switch (G) {
-    case 1: return RowCfg<QT, CT, D, 1>::resident() * kWavesPerWG;
-    case 2: return RowCfg<QT, CT, D, 2>::resident() * kWavesPerWG;
-    case 4: return RowCfg<QT, CT, D, 4>::resident() * kWavesPerWG;
-    case 8: return RowCfg<QT, CT, D, 8>::resident() * kWavesPerWG;
-    case 16: return RowCfg<QT, CT, D, 16>::resident() * kWavesPerWG;
+    case 1: return RowCfg<QT, CT, D, 1, CAP>::resident() * kWavesPerWG;
+    case 2: return RowCfg<QT, CT, D, 2, CAP>::resident() * kWavesPerWG;
+    case 4: return RowCfg<QT, CT, D, 4, CAP>::resident() * kWavesPerWG;
+    case 8: return RowCfg<QT, CT, D, 8, CAP>::resident() * kWavesPerWG;
+    case 16: return RowCfg<QT, CT, D, 16, CAP>::resident() * kWavesPerWG;
     default: return 0;
   }
 }
 
-template <typename QT, typename CT>
+template <typename QT, typename CT, bool CAP>
 int row_waves_d(int D, int G) {
-  if (D == 64) return row_waves_g<QT, CT, 64>(G);
-  if (D == 128) return row_waves_g<QT, CT, 128>(G);
+  if (D == 64) return row_waves_g<QT, CT, 64, CAP>(G);
+  if (D == 128) return row_waves_g<QT, CT, 128, CAP>(G);
   return 0;
 }
 
-template <typename QT, typename CT, int D>
+template <typename QT, typename CT, int D, bool CAP>
 hipError_t launch_rows_g(const AttnParams& p, hipStream_t s) {
   switch (p.Hq / p.Hkv) {
-    case 1: return launch_rows_t<QT, CT, D, 1>(p, s);
-    case 2: return launch_rows_t<QT, CT, D, 2>(p, s);
-    case 4: return launch_rows_t<QT, CT, D, 4>(p, s);
-    case 8: return launch_rows_t<QT, CT, D, 8>(p, s);
-    case 16: return launch_rows_t<QT, CT, D, 16>(p, s);
+    case 1: return launch_rows_t<QT, CT, D, 1, CAP>(p, s);
+    case 2: return launch_rows_t<QT, CT, D, 2, CAP>(p, s);
+    case 4: return launch_rows_t<QT, CT, D, 4, CAP>(p, s);
+    case 8: return launch_rows_t<QT, CT, D, 8, CAP>(p, s);
+    case 16: return launch_rows_t<QT, CT, D, 16, CAP>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename QT, typename CT>
+template <typename QT, typename CT, bool CAP>
 hipError_t launch_rows_d(const AttnParams& p, hipStream_t s) {
-  if (p.D == 64) return launch_rows_g<QT, CT, 64>(p, s);
-  if (p.D == 128) return launch_rows_g<QT, CT, 128>(p, s);
+  if (p.D == 64) return launch_rows_g<QT, CT, 64, CAP>(p, s);
+  if (p.D == 128) return launch_rows_g<QT, CT, 128, CAP>(p, s);
+  return hipErrorInvalidValue;
+}
+
+template <bool CAP>
+int row_waves_c(rpa_dtype q_dt, rpa_dtype cache_dt, int D, int G) {
+  if (q_dt == RPA_F32 && cache_dt == RPA_F32) return row_waves_d<float, float, CAP>(D, G);
+  if (q_dt == RPA_BF16 && cache_dt == RPA_BF16) return row_waves_d<uint16_t, uint16_t, CAP>(D, G);
+  if (q_dt == RPA_BF16 && cache_dt == RPA_FP8_E4M3) return row_waves_d<uint16_t, uint8_t, CAP>(D, G);
+  return 0;
+}
+
+template <bool CAP>
+hipError_t launch_rows_c(const AttnParams& p, rpa_dtype q_dt, rpa_dtype cache_dt, hipStream_t s) {
+  if (q_dt == RPA_F32 && cache_dt == RPA_F32) return launch_rows_d<float, float, CAP>(p, s);
+  if (q_dt == RPA_BF16 && cache_dt == RPA_BF16) return launch_rows_d<uint16_t, uint16_t, CAP>(p, s);
+  if (q_dt == RPA_BF16 && cache_dt == RPA_FP8_E4M3) return launch_rows_d<uint16_t, uint8_t, CAP>(p, s);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-int row_waves(rpa_dtype q_dt, rpa_dtype cache_dt, int D, int G) {
-  if (q_dt == RPA_F32 && cache_dt == RPA_F32) return row_waves_d<float, float>(D, G);
-  if (q_dt == RPA_BF16 && cache_dt == RPA_BF16) return row_waves_d<uint16_t, uint16_t>(D, G);
-  if (q_dt == RPA_BF16 && cache_dt == RPA_FP8_E4M3) return row_waves_d<uint16_t, uint8_t>(D, G);
-  return 0;
+// The soft cap is a template choice of the row kernels, so that the per-logit
+// code of the uncapped kernels carries no test of it.
+int row_waves(rpa_dtype q_dt, rpa_dtype cache_dt, int D, int G, bool cap) {
+  return cap ? row_waves_c<true>(q_dt, cache_dt, D, G) : row_waves_c<false>(q_dt, cache_dt, D, G);
 }
 
 hipError_t launch_rows(const AttnParams& p, rpa_dtype q_dt, rpa_dtype cache_dt, hipStream_t s) {
-  if (q_dt == RPA_F32 && cache_dt == RPA_F32) return launch_rows_d<float, float>(p, s);
-  if (q_dt == RPA_BF16 && cache_dt == RPA_BF16) return launch_rows_d<uint16_t, uint16_t>(p, s);
-  if (q_dt == RPA_BF16 && cache_dt == RPA_FP8_E4M3) return launch_rows_d<uint16_t, uint8_t>(p, s);
-  return hipErrorInvalidValue;
+  return p.cap > 0.f ? launch_rows_c<true>(p, q_dt, cache_dt, s)
+                     : launch_rows_c<false>(p, q_dt, cache_dt, s);
 }
 
 namespace {

@@ -443,7 +443,8 @@ int rpa_forward(const rpa_desc* desc, const rpa_options* opts, const void* queri
   pp.prefill_min_q = prefill_min_q(*desc);
   pp.Hkv = desc->num_kv_heads;
   pp.row_waves = row_waves((rpa_dtype)desc->q_dtype, (rpa_dtype)desc->cache_dtype,
-                           desc->head_dim, desc->num_q_heads / desc->num_kv_heads);
+                           desc->head_dim, desc->num_q_heads / desc->num_kv_heads,
+                           opts->logits_soft_cap > 0.f);
   pp.Hq = desc->num_q_heads;
   pp.D = desc->head_dim;
   pp.kv_elem = elem_size(desc->cache_dtype);

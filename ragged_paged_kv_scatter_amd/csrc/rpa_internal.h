@@ -185,7 +185,7 @@ hipError_t launch_prep(const PlanParams& pp, const ScatterParams* sp, rpa_dtype 
                        rpa_dtype cache_dt, hipStream_t s);
 hipError_t launch_rows(const AttnParams& p, rpa_dtype q_dt, rpa_dtype cache_dt, hipStream_t s);
 // waves of the row kernel for these types and sizes that fit on the device at once
-int row_waves(rpa_dtype q_dt, rpa_dtype cache_dt, int D, int G);
+int row_waves(rpa_dtype q_dt, rpa_dtype cache_dt, int D, int G, bool cap);
 hipError_t launch_merge(const AttnParams& p, rpa_dtype q_dt, hipStream_t s);
 hipError_t launch_prefill(const AttnParams& p, rpa_dtype q_dt, rpa_dtype cache_dt,
                           hipStream_t s);
