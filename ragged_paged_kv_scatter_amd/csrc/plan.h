@@ -16,36 +16,86 @@ namespace plan_detail {
 constexpr int kT = kPlanThreads;
 constexpr int kWaves = kT / 64;
 
-// Exclusive prefix sum over the workgroup; returns the prefix of this thread
-// and writes the total to *total.  All threads must call it.
+// A DPP move of v from another lane; lanes that the row mask leaves out, or
+// whose source lies outside their row of 16, get 0.  64-bit values move as
+// two 32-bit halves.
+template <int CTRL, int ROW_MASK, typename V>
+__device__ __forceinline__ V dpp_or_zero(V v) {
+  if constexpr (sizeof(V) == 4) {
+    return (V)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+  } else {
+    const unsigned long long u = (unsigned long long)v;
+    const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)u, CTRL, ROW_MASK, 0xF, false);
+    const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(u >> 32), CTRL, ROW_MASK, 0xF, false);
+    return (V)(((unsigned long long)hi << 32) | lo);
+  }
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active), on
+// VALU moves only: shifts by 1, 2, 4 and 8 within each row of 16 lanes give
+// every row its own prefix; then lane 15's total goes into rows 1 and 3
+// (row_bcast:15) and lane 31's, by now the total of rows 0-1, into rows 2
+// and 3 (row_bcast:31).
+template <typename V>
+__device__ __forceinline__ V wave_inclusive_scan(V x) {
+  x += dpp_or_zero<0x111, 0xF>(x);                  // row_shr:1
+  x += dpp_or_zero<0x112, 0xF>(x);                  // row_shr:2
+  x += dpp_or_zero<0x114, 0xF>(x);                  // row_shr:4
+  x += dpp_or_zero<0x118, 0xF>(x);                  // row_shr:8
+  x += dpp_or_zero<0x142, 0xA>(x);                  // row_bcast:15, rows 1 and 3
+  x += dpp_or_zero<0x143, 0xC>(x);                  // row_bcast:31, rows 2 and 3
+  return x;
+}
+
+// Exclusive prefix sums over the workgroup in three steps, so that several
+// sums share one pair of barriers:
+//   scan_up    (all threads)  the wave's inclusive sum; lane 63 publishes
+//                             the wave total in s_waves[wave];
+//   barrier;
+//   scan_waves (wave 0 only)  the wave totals -> their exclusive prefixes,
+//                             the grand total in s_waves[kWaves];
+//   barrier;
+//   scan_down  (all threads)  this thread's exclusive prefix and the total.
+// Entry w < kWaves of s_waves is read after the scan only by wave w, and the
+// grand total is rewritten only behind the next scan's first barrier, so an
+// array may serve the next scan with no barrier in between.
+template <typename V>
+__device__ __forceinline__ V scan_up(V v, V* s_waves) {
+  const V x = wave_inclusive_scan(v);
+  if ((threadIdx.x & 63) == 63) s_waves[threadIdx.x >> 6] = x;
+  return x;
+}
+template <typename V>
+__device__ __forceinline__ void scan_waves(V* s_waves) {
+  const int lane = threadIdx.x & 63;
+  const V t = lane < kWaves ? s_waves[lane] : V(0);
+  const V inc = wave_inclusive_scan(t);
+  if (lane < kWaves) s_waves[lane] = inc - t;
+  if (lane == kWaves - 1) s_waves[kWaves] = inc;
+}
+template <typename V>
+__device__ __forceinline__ V scan_down(V v, V x, const V* s_waves, V* total) {
+  *total = s_waves[kWaves];
+  return x - v + s_waves[threadIdx.x >> 6];
+}
+
+// One exclusive prefix sum over the workgroup; all threads must call it.
 template <typename V>
 __device__ V block_exclusive_scan(V v, V* total, V* s_waves) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  V x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    V y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) s_waves[wave] = x;
+  const V x = scan_up(v, s_waves);
   __syncthreads();
-  if (wave == 0) {
-    // the kWaves wave totals, scanned by wave 0's lanes (no serial LDS chain)
-    const V t = lane < kWaves ? s_waves[lane] : V(0);
-    V inc = t;
-#pragma unroll
-    for (int o = 1; o < kWaves; o <<= 1) {
-      V y = __shfl_up(inc, o);
-      if (lane >= o) inc += y;
-    }
-    if (lane < kWaves) s_waves[lane] = inc - t;
-    if (lane == kWaves - 1) s_waves[kWaves] = inc;
-  }
+  if (threadIdx.x < 64) scan_waves(s_waves);
   __syncthreads();
-  V res = x - v + s_waves[wave];
-  *total = s_waves[kWaves];
-  __syncthreads();
-  return res;
+  return scan_down(v, x, s_waves, total);
+}
+
+// a / b for a >= 0, b > 0: a 32-bit division when both fit, as they do but
+// for huge batches (the 64-bit one is a long instruction sequence, run here
+// by every wave of the workgroup).
+__device__ __forceinline__ long long div_nonneg(long long a, long long b) {
+  if ((((unsigned long long)a | (unsigned long long)b) >> 32) == 0)
+    return (long long)((unsigned)a / (unsigned)b);
+  return a / b;
 }
 
 __device__ __forceinline__ long long visible_sum(int ctx, int q_len, int window) {
@@ -70,6 +120,8 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
   __shared__ int32_t s_w32[kWaves + 1];
   __shared__ int32_t s_w32b[kWaves + 1];
   __shared__ int32_t s_w32c[kWaves + 1];
+  __shared__ int32_t s_pf_first[kT + 1];            // a block's first prefill item per thread
+  __shared__ int32_t s_pf_qlen[kT];
 
   char* ws = p.ws;
   PlanHeader* hdr = reinterpret_cast<PlanHeader*>(ws + p.lay.header);
@@ -113,21 +165,45 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
     }
     int tot_rows, tot_pf;
     long long tot_vis, tot_pf_vis;
-    const int my_row = block_exclusive_scan(n_rows, &tot_rows, s_w32) + row_base;
-    const int my_pf = block_exclusive_scan(n_pf, &tot_pf, s_w32b) + pf_base;
-    block_exclusive_scan(vis, &tot_vis, s_w64);
-    block_exclusive_scan(pf_vis, &tot_pf_vis, s_w64b);
-    if (s < num_seqs) {
-      s_seq_rows[s] = my_row;
-      // heaviest tiles first within a sequence (causal: later tiles see more keys)
-      for (int i = 0; i < n_pf; ++i) {
-        const int tile = n_pf - 1 - i;
+    const int x_rows = scan_up(n_rows, s_w32);
+    const int x_pf = scan_up(n_pf, s_w32b);
+    scan_up(vis, s_w64);
+    scan_up(pf_vis, s_w64b);
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      scan_waves(s_w32);
+      scan_waves(s_w32b);
+      scan_waves(s_w64);
+      scan_waves(s_w64b);
+    }
+    __syncthreads();
+    const int my_row = scan_down(n_rows, x_rows, s_w32, &tot_rows) + row_base;
+    const int my_pf = scan_down(n_pf, x_pf, s_w32b, &tot_pf) + pf_base;
+    tot_vis = s_w64[kWaves];
+    tot_pf_vis = s_w64b[kWaves];
+    if (s < num_seqs) s_seq_rows[s] = my_row;
+    if (tot_pf > 0) {
+      // the block's prefill items, written by all threads: item j belongs to
+      // the last thread t whose first item is <= j (threads without tiles
+      // share the next one's first item, threads past num_seqs have tot_pf)
+      s_pf_first[threadIdx.x] = my_pf - pf_base;
+      s_pf_qlen[threadIdx.x] = q_len;
+      if (threadIdx.x == 0) s_pf_first[kT] = tot_pf;
+      __syncthreads();
+      for (int j = threadIdx.x; j < tot_pf; j += kT) {
+        int a = 0, b = min(kT, num_seqs - base) - 1;
+        while (a < b) {
+          const int mid = (a + b + 1) >> 1;
+          if (s_pf_first[mid] <= j) a = mid; else b = mid - 1;
+        }
+        // heaviest tiles first within a sequence (causal: later tiles see more keys)
+        const int tile = s_pf_first[a + 1] - 1 - j;
         PrefillItem it;
-        it.seq = s;
+        it.seq = base + a;
         it.q_begin = tile * kPrefillBQ;
-        it.q_end = min(q_len, (tile + 1) * kPrefillBQ);
+        it.q_end = min(s_pf_qlen[a], (tile + 1) * kPrefillBQ);
         it.pad = 0;
-        if (my_pf + i < p.lay.max_pf_items) pf[my_pf + i] = it;
+        if (pf_base + j < p.lay.max_pf_items) pf[pf_base + j] = it;
       }
     }
     row_base += tot_rows;
@@ -154,9 +230,9 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
   const bool co_run = p.co_allowed && row_base > 0 && pf_base > 0 &&
                       dec_bytes * 500 >= pf_flops * 3;
   const long long want = row_chunks_max(co_run ? p.row_waves / 8 * kCoRowEighths : p.row_waves, p.Hkv);
-  long long C = (vis_total + want - 1) / want;
+  long long C = div_nonneg(vis_total + want - 1, want);
   if (C < kMinSplit) C = kMinSplit;
-  const int n_chunks = (int)min((vis_total + C - 1) / C, (long long)kTargetItems);
+  const int n_chunks = (int)min(div_nonneg(vis_total + C - 1, C), (long long)kTargetItems);
   int32_t* chunk_first = reinterpret_cast<int32_t*>(ws + p.lay.chunks);
 
   // row r -> (seq, token, visible range [lo, hi))
@@ -195,13 +271,23 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
     }
     long long tot_len;
     const long long off = block_exclusive_scan(len, &tot_len, s_w64) + stream_base;
-    const int n_split = (r < n_rows) ? (int)((off + len - 1) / C - off / C + 1) : 0;
+    const long long c0 = div_nonneg(off, C);
+    const int n_split = (r < n_rows) ? (int)(div_nonneg(off + len - 1, C) - c0 + 1) : 0;
+    const int v_part = n_split > 1 ? n_split : 0, v_merge = n_split > 1 ? 1 : 0;
     int tot_items, tot_parts, tot_merge;
-    const int my_item = block_exclusive_scan(n_split, &tot_items, s_w32) + item_base;
-    const int my_part =
-        block_exclusive_scan(n_split > 1 ? n_split : 0, &tot_parts, s_w32b) + part_base;
-    const int my_merge = block_exclusive_scan(n_split > 1 ? 1 : 0, &tot_merge, s_w32c) +
-                         merge_base;
+    const int x_item = scan_up(n_split, s_w32);
+    const int x_part = scan_up(v_part, s_w32b);
+    const int x_merge = scan_up(v_merge, s_w32c);
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      scan_waves(s_w32);
+      scan_waves(s_w32b);
+      scan_waves(s_w32c);
+    }
+    __syncthreads();
+    const int my_item = scan_down(n_split, x_item, s_w32, &tot_items) + item_base;
+    const int my_part = scan_down(v_part, x_part, s_w32b, &tot_parts) + part_base;
+    const int my_merge = scan_down(v_merge, x_merge, s_w32c, &tot_merge) + merge_base;
     if (r < n_rows) {
       RowDesc rd;
       rd.token = token;
@@ -212,7 +298,6 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
       rd.part_base = n_split > 1 ? my_part : -1;
       rd.pad[0] = rd.pad[1] = 0;
       rows[r] = rd;
-      const long long c0 = off / C;
       for (int j = 0; j < n_split; ++j) {
         const int slot = my_item + j;
         if (slot >= p.lay.max_items) break;
@@ -245,7 +330,7 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
     merge_base += tot_merge;
   }
   // chunks that hold keys (all of them unless rows were cut off at max_rows)
-  const int n_chunks_laid = (int)min((long long)n_chunks, (stream_base + C - 1) / C);
+  const int n_chunks_laid = (int)min((long long)n_chunks, div_nonneg(stream_base + C - 1, C));
   if (threadIdx.x == 0) {
     chunk_first[n_chunks_laid] = min(item_base, p.lay.max_items);
     PlanHeader h = {};

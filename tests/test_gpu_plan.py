@@ -6,7 +6,10 @@ per resident wave and kv head); these cases push that cut to its ends:
   * thousands of tiny rows, so that a chunk walks many rows' pieces (with the
     planner's per-sequence tables in LDS, and past that cache's size);
   * the f32 path, where every row of a prefill chunk goes to the row kernel
-    and the causal rows of one sequence share chunks.
+    and the causal rows of one sequence share chunks;
+  * thousands of short prefill sequences between decode rows, so that the
+    planner's prefill tiles span several blocks of sequences and one block
+    holds more tiles than the planner has threads.
 Each compares rpa_forward with the oracle to the dtype's tolerance and the
 updated cache bit for bit."""
 import math
@@ -36,6 +39,21 @@ def _case(label, seed, device="cuda"):
         kv_lens = [int(x) for x in rng.integers(1, 41, size=n)]
         args = dict(num_q_heads=4, num_kv_heads=2, head_dim=128, page_size=16,
                     q_dtype="bf16", kv_in_dtype="bf16", cache_dtype="bf16", distribution=(n, 0, 0))
+    elif label == "many_prefill_seqs":
+        # 2300 sequences, every fourth a decode row, the rest prefill chunks
+        # of 2..300 tokens (1 to 3 tiles) after up to 40 cached tokens
+        n = 2300
+        q_lens, kv_lens = [], []
+        for i in range(n):
+            if i % 4 == 0:
+                q_lens.append(1)
+                kv_lens.append(int(rng.integers(1, 61)))
+            else:
+                q = int(rng.integers(2, 301))
+                q_lens.append(q)
+                kv_lens.append(q + int(rng.integers(0, 41)))
+        args = dict(num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=16,
+                    q_dtype="bf16", kv_in_dtype="bf16", cache_dtype="bf16", distribution=(0, 0, n))
     elif label == "f32_prefill_rows":
         q_lens, kv_lens = [300, 1, 5], [5000, 3000, 5]
         args = dict(num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=32,
@@ -47,7 +65,7 @@ def _case(label, seed, device="cuda"):
 
 
 @pytest.mark.parametrize("label", ["one_long_row", "tiny_rows_3000", "tiny_rows_4500",
-                                   "f32_prefill_rows"])
+                                   "many_prefill_seqs", "f32_prefill_rows"])
 def test_plan_extremes_match_oracle(label):
     print(f"\n[case] plan {label}", flush=True)
     w = _case(label, seed=9100 + len(label))
