@@ -898,14 +898,13 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void mfma_row_kernel(AttnParams p
 }
 
 // Stand-alone merge of the split partials (when no prefill kernel runs after
-// the row kernel to do it): four merge items per workgroup.
+// the row kernel to do it): four merge items per workgroup, or one per
+// workgroup for rows with many parts.
 template <typename QT, int D, int G>
 __global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
+  __shared__ float s_merge[merge_wg_floats<D, G>()];
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(p.ws + p.lay.header);
-  const long long total = (long long)hdr->n_merge_rows * p.Hkv;
-  for (long long idx = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); idx < total;
-       idx += (long long)gridDim.x * 4)
-    merge_one<QT, D, G>(p, idx);
+  merge_all<QT, D, G>(p, (long long)hdr->n_merge_rows * p.Hkv, s_merge);
 }
 
 // Workgroups of `kernel` that fit on the device at once (occupancy x CUs).

@@ -4,7 +4,10 @@
 // m in log2 units.  One wave merges one (row, kv head) with its G q heads: the
 // lanes of a head split its d range.  The running form (M, L, acc rescaled as
 // M grows) takes one pass over the partials, and the split loop is unrolled
-// so that the loads of several partials are in flight at once.  Used by the
+// so that the loads of several partials are in flight at once.  A row cut
+// into many parts (a long context over few rows) is merged by a whole
+// workgroup instead: each of its 4 waves runs the same pass over every fourth
+// part, and the four states are combined by the same rule.  Used by the
 // stand-alone merge kernel and by the prefill kernel, which merges before its
 // own work.
 #pragma once
@@ -44,34 +47,42 @@ __device__ __forceinline__ void load_floats(const float* src, float* dst) {
   }
 }
 
-// Merge item idx = merge-row index * Hkv + kv head, by the calling wave.
-template <typename QT, int D, int G>
-__device__ __forceinline__ void merge_one(const AttnParams& p, long long idx) {
-  constexpr int LPH = 64 / G;           // lanes per head
-  constexpr int E = D / LPH;            // d elements per lane
-  constexpr float kLog2eM = 1.4426950408889634f;
+// Rows with at least this many parts are merged by a workgroup of 4 waves.
+constexpr int kMergeWgParts = 16;
+constexpr float kMergeLog2e = 1.4426950408889634f;
+
+// Where a lane works in merge item idx = merge-row index * Hkv + kv head:
+// its q head h and d slice sub, and the item's merge descriptor.
+template <int D, int G>
+struct MergeLane {
+  static constexpr int LPH = 64 / G;    // lanes per head
+  static constexpr int E = D / LPH;     // d elements per lane
   static_assert(LPH * G == 64 && E * LPH == D, "merge lane split");
-  const MergeDesc* merge_rows = reinterpret_cast<const MergeDesc*>(p.ws + p.lay.merge_rows);
+  int h, sub;
+  MergeDesc md;
+  __device__ __forceinline__ MergeLane(const AttnParams& p, long long idx) {
+    const MergeDesc* merge_rows = reinterpret_cast<const MergeDesc*>(p.ws + p.lay.merge_rows);
+    const int lane = lane_id();
+    const int mi = (int)(idx / p.Hkv);
+    const int g = (int)(idx - (long long)mi * p.Hkv);
+    h = g * G + lane / LPH;
+    sub = lane % LPH;
+    md = merge_rows[mi];
+  }
+};
+
+// The running merge over parts j0, j0 + step, ... of the lane's item.
+template <int D, int G>
+__device__ __forceinline__ void merge_scan(const AttnParams& p, const MergeLane<D, G>& ml_,
+                                           int j0, int step, float& M, float& L,
+                                           float (&o)[MergeLane<D, G>::E]) {
+  constexpr int E = MergeLane<D, G>::E;
   const float* part_ml = reinterpret_cast<const float*>(p.ws + p.lay.part_ml);
   const float* part_acc = reinterpret_cast<const float*>(p.ws + p.lay.part_acc);
-  const int lane = lane_id();
-  const int hi = lane / LPH, sub = lane % LPH;
-  const int Hq = p.Hq, Hkv = p.Hkv;
-  const int mi = (int)(idx / Hkv);
-  const int g = (int)(idx - (long long)mi * Hkv);
-  const int h = g * G + hi;
-  const MergeDesc md = merge_rows[mi];
-  // running state; the sink enters as a partial with l = 1 and acc = 0
-  float M = -INFINITY, L = 0.f;
-  if (p.sink) {
-    M = p.sink[h] * kLog2eM;
-    L = 1.f;
-  }
-  float o[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = 0.f;
+  const int Hq = p.Hq, h = ml_.h, sub = ml_.sub;
+  const MergeDesc& md = ml_.md;
 #pragma unroll 4
-  for (int j = 0; j < md.n_split; ++j) {
+  for (int j = j0; j < md.n_split; j += step) {
     const long long pb = (long long)(md.part_base + j) * Hq + h;
     const float2 ml = *reinterpret_cast<const float2*>(part_ml + 2 * pb);
     float a[E];
@@ -85,22 +96,116 @@ __device__ __forceinline__ void merge_one(const AttnParams& p, long long idx) {
 #pragma unroll
     for (int e = 0; e < E; ++e) o[e] = fmaf(w, a[e], o[e] * r);
   }
+}
+
+template <typename QT, int D, int G>
+__device__ __forceinline__ void merge_store(const AttnParams& p, const MergeLane<D, G>& ml_,
+                                            float L, const float (&o)[MergeLane<D, G>::E]) {
+  constexpr int E = MergeLane<D, G>::E;
   const float sc = p.v_scale / L;
   QT* op = static_cast<QT*>(p.out);
-  const long long base = ((long long)md.token * Hq + h) * D + sub * E;
+  const long long base = ((long long)ml_.md.token * p.Hq + ml_.h) * D + ml_.sub * E;
 #pragma unroll
   for (int e = 0; e < E; ++e) store_out<QT>(op, base + e, o[e] * sc);
 }
 
+// Merge item idx by the calling wave.
+template <typename QT, int D, int G>
+__device__ __forceinline__ void merge_one(const AttnParams& p, long long idx) {
+  constexpr int E = MergeLane<D, G>::E;
+  const MergeLane<D, G> ml_(p, idx);
+  // running state; the sink enters as a partial with l = 1 and acc = 0
+  float M = -INFINITY, L = 0.f;
+  if (p.sink) {
+    M = p.sink[ml_.h] * kMergeLog2e;
+    L = 1.f;
+  }
+  float o[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = 0.f;
+  merge_scan<D, G>(p, ml_, 0, 1, M, L, o);
+  merge_store<QT, D, G>(p, ml_, L, o);
+}
+
+// LDS floats merge_one_wg needs: the states of waves 1-3.
+template <int D, int G>
+constexpr int merge_wg_floats() { return 3 * 64 * (MergeLane<D, G>::E + 2); }
+
+// Merge item idx by all 4 waves of the workgroup (every thread calls it with
+// the same idx); s holds merge_wg_floats<D, G>() floats of LDS and is free
+// again on return.
+template <typename QT, int D, int G>
+__device__ __forceinline__ void merge_one_wg(const AttnParams& p, long long idx, float* s) {
+  constexpr int E = MergeLane<D, G>::E;
+  constexpr int S = 64 * (E + 2);                 // floats of one wave's state
+  const MergeLane<D, G> ml_(p, idx);
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  float M = -INFINITY, L = 0.f;
+  float o[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = 0.f;
+  merge_scan<D, G>(p, ml_, wave, 4, M, L, o);
+  if (wave > 0) {
+    float* b = s + (wave - 1) * S;
+    b[lane] = M;
+    b[64 + lane] = L;
+#pragma unroll
+    for (int e = 0; e < E; ++e) b[(2 + e) * 64 + lane] = o[e];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float Mx = M;
+#pragma unroll
+    for (int w = 0; w < 3; ++w) Mx = fmaxf(Mx, s[w * S + lane]);
+    const float sink = p.sink ? p.sink[ml_.h] * kMergeLog2e : -INFINITY;
+    Mx = fmaxf(Mx, sink);
+    const float r0 = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mx);
+    L *= r0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] *= r0;
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+      const float Mw = s[w * S + lane];
+      const float rw = Mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mw - Mx);
+      L = fmaf(rw, s[w * S + 64 + lane], L);
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] = fmaf(rw, s[w * S + (2 + e) * 64 + lane], o[e]);
+    }
+    if (p.sink) L += __builtin_amdgcn_exp2f(sink - Mx);
+    merge_store<QT, D, G>(p, ml_, L, o);
+  }
+  __syncthreads();
+}
+
+// Parts of merge item idx (uniform over the caller).
+__device__ __forceinline__ int merge_parts(const AttnParams& p, long long idx) {
+  const MergeDesc* merge_rows = reinterpret_cast<const MergeDesc*>(p.ws + p.lay.merge_rows);
+  return merge_rows[idx / p.Hkv].n_split;
+}
+
+// Every merge item of the step: items with few parts one per wave (4 per
+// workgroup, strided over the grid), then items with many parts one per
+// workgroup.  s: merge_wg_floats<D, G>() floats of LDS.
+template <typename QT, int D, int G>
+__device__ __forceinline__ void merge_all(const AttnParams& p, long long total, float* s) {
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  for (long long idx = (long long)blockIdx.x * 4 + wave; idx < total;
+       idx += (long long)gridDim.x * 4)
+    if (merge_parts(p, idx) < kMergeWgParts) merge_one<QT, D, G>(p, idx);
+  for (long long idx = blockIdx.x; idx < total; idx += gridDim.x)
+    if (merge_parts(p, idx) >= kMergeWgParts) merge_one_wg<QT, D, G>(p, idx, s);
+}
+
 // The same with the group size G = Hq / Hkv read at run time.
 template <typename QT, int D>
-__device__ __forceinline__ void merge_one_g(const AttnParams& p, long long idx) {
+__device__ __forceinline__ void merge_all_g(const AttnParams& p, long long total, float* s) {
   switch (p.Hq / p.Hkv) {
-    case 1: merge_one<QT, D, 1>(p, idx); break;
-    case 2: merge_one<QT, D, 2>(p, idx); break;
-    case 4: merge_one<QT, D, 4>(p, idx); break;
-    case 8: merge_one<QT, D, 8>(p, idx); break;
-    case 16: merge_one<QT, D, 16>(p, idx); break;
+    case 1: merge_all<QT, D, 1>(p, total, s); break;
+    case 2: merge_all<QT, D, 2>(p, total, s); break;
+    case 4: merge_all<QT, D, 4>(p, total, s); break;
+    case 8: merge_all<QT, D, 8>(p, total, s); break;
+    case 16: merge_all<QT, D, 16>(p, total, s); break;
     default: break;
   }
 }

@@ -15,6 +15,18 @@ namespace plan_detail {
 
 constexpr int kT = kPlanThreads;
 constexpr int kWaves = kT / 64;
+// Rows cut into more pieces than this have them written by all lanes of
+// their wave (one such row after another) rather than by their own thread.
+constexpr int kWavePieces = 8;
+
+__device__ __forceinline__ int lane_value(int v, int lane) {
+  return __builtin_amdgcn_readlane(v, lane);
+}
+__device__ __forceinline__ long long lane_value(long long v, int lane) {
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)v, lane);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)((unsigned long long)v >> 32), lane);
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
 
 // A DPP move of v from another lane; lanes that the row mask leaves out, or
 // whose source lies outside their row of 16, get 0.  64-bit values move as
@@ -288,6 +300,27 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
     const int my_item = scan_down(n_split, x_item, s_w32, &tot_items) + item_base;
     const int my_part = scan_down(v_part, x_part, s_w32b, &tot_parts) + part_base;
     const int my_merge = scan_down(v_merge, x_merge, s_w32c, &tot_merge) + merge_base;
+    // piece j of a row: its part of chunk c0 + j; the piece that starts a
+    // chunk is that chunk's first item
+    auto write_piece = [&](int j, long long off_r, long long len_r, long long c0_r, int lo_r,
+                           int token_r, int seq_r, int item_r, int part_r, int n_split_r,
+                           int r_r) {
+      const int slot = item_r + j;
+      if (slot >= p.lay.max_items) return;
+      const long long s0 = max(off_r, (c0_r + j) * C);
+      const long long s1 = min(off_r + len_r, (c0_r + j + 1) * C);
+      ItemDesc it;
+      it.token = token_r;
+      it.seq = seq_r;
+      it.lo = lo_r + (int)(s0 - off_r);
+      it.hi = lo_r + (int)(s1 - off_r);
+      it.part = n_split_r > 1 ? part_r + j : -1;
+      it.row = r_r;
+      it.pad[0] = it.pad[1] = 0;
+      items[slot] = it;
+      if (s0 == (c0_r + j) * C && c0_r + j < n_chunks) chunk_first[c0_r + j] = slot;
+    };
+    const bool heavy = n_split > kWavePieces;
     if (r < n_rows) {
       RowDesc rd;
       rd.token = token;
@@ -298,23 +331,9 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
       rd.part_base = n_split > 1 ? my_part : -1;
       rd.pad[0] = rd.pad[1] = 0;
       rows[r] = rd;
-      for (int j = 0; j < n_split; ++j) {
-        const int slot = my_item + j;
-        if (slot >= p.lay.max_items) break;
-        const long long s0 = max(off, (c0 + j) * C);
-        const long long s1 = min(off + len, (c0 + j + 1) * C);
-        ItemDesc it;
-        it.token = token;
-        it.seq = seq;
-        it.lo = lo + (int)(s0 - off);
-        it.hi = lo + (int)(s1 - off);
-        it.part = n_split > 1 ? my_part + j : -1;
-        it.row = r;
-        it.pad[0] = it.pad[1] = 0;
-        items[slot] = it;
-        // every chunk has exactly one piece that starts at its first key
-        if (s0 == (c0 + j) * C && c0 + j < n_chunks) chunk_first[c0 + j] = slot;
-      }
+      if (!heavy)
+        for (int j = 0; j < n_split; ++j)
+          write_piece(j, off, len, c0, lo, token, seq, my_item, my_part, n_split, r);
       if (n_split > 1 && my_merge < p.lay.max_merge_rows) {
         MergeDesc md;
         md.token = token;
@@ -323,6 +342,18 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
         md.pad = 0;
         merge_rows[my_merge] = md;
       }
+    }
+    // the heavy rows of this wave, one after another, by all 64 lanes
+    for (unsigned long long m = __ballot(heavy); m != 0; m &= m - 1) {
+      const int L = __builtin_ctzll(m);
+      const int n_L = lane_value(n_split, L);
+      const long long off_L = lane_value(off, L), len_L = lane_value(len, L),
+                      c0_L = lane_value(c0, L);
+      const int lo_L = lane_value(lo, L), token_L = lane_value(token, L),
+                seq_L = lane_value(seq, L), item_L = lane_value(my_item, L),
+                part_L = lane_value(my_part, L), r_L = lane_value(r, L);
+      for (int j = threadIdx.x & 63; j < n_L; j += 64)
+        write_piece(j, off_L, len_L, c0_L, lo_L, token_L, seq_L, item_L, part_L, n_L, r_L);
     }
     stream_base += tot_len;
     item_base += tot_items;

@@ -223,14 +223,13 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
     return __builtin_bit_cast(bf16x8, av);
   };
 
-  // Split-KV partials of the row kernel (launched before this one): one wave
-  // per (row, kv head).  They touch rows this kernel does not write.
-  if (p.fuse_merge) {
-    const long long n_merge = (long long)hdr->n_merge_rows * Hkv;
-    for (long long mi = (long long)blockIdx.x * 4 + wave; mi < n_merge;
-         mi += (long long)gridDim.x * 4)
-      merge_one_g<uint16_t, D>(p, mi);
-  }
+  // Split-KV partials of the row kernel (launched before this one), by (row,
+  // kv head); they touch rows this kernel does not write.  Rows with many
+  // parts are merged by the whole workgroup in s_k, before any copy into it.
+  static_assert(NT == 256, "the workgroup merge takes 4 waves");
+  static_assert(merge_wg_floats<D, 16>() * 4 <= 2 * BLKB, "merge scratch fits in s_k");
+  if (p.fuse_merge)
+    merge_all_g<uint16_t, D>(p, (long long)hdr->n_merge_rows * Hkv, reinterpret_cast<float*>(s_k));
 
   // Persistent grid: in round k block b takes unit k * grid + b, except that
   // odd rounds reverse the order of the groups of 8 blocks (when the grid is
