@@ -17,7 +17,10 @@ constexpr int kT = kPlanThreads;
 constexpr int kWaves = kT / 64;
 // Rows cut into more pieces than this have them written by all lanes of
 // their wave (one such row after another) rather than by their own thread.
-constexpr int kWavePieces = 8;
+// With at most kTargetItems chunks, at most kTargetItems / 64 rows of a step
+// pass it, so the wave's walk over them stays short; a lower bound would
+// serialise the many rows of a batch with a handful of pieces each.
+constexpr int kWavePieces = 64;
 
 __device__ __forceinline__ int lane_value(int v, int lane) {
   return __builtin_amdgcn_readlane(v, lane);
