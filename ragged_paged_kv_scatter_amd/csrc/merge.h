@@ -193,8 +193,16 @@ __device__ __forceinline__ void merge_all(const AttnParams& p, long long total, 
   for (long long idx = (long long)blockIdx.x * 4 + wave; idx < total;
        idx += (long long)gridDim.x * 4)
     if (merge_parts(p, idx) < kMergeWgParts) merge_one<QT, D, G>(p, idx);
-  for (long long idx = blockIdx.x; idx < total; idx += gridDim.x)
-    if (merge_parts(p, idx) >= kMergeWgParts) merge_one_wg<QT, D, G>(p, idx, s);
+  // the workgroup's items blockIdx.x + k * gridDim.x, 64 at a time: lane k
+  // checks item k (one round of loads, not a chain), and every wave forms the
+  // same mask, so the workgroup walks the many-part items together
+  const long long stride = gridDim.x;
+  for (long long base = blockIdx.x; base < total; base += 64 * stride) {
+    const long long mine = base + (long long)lane_id() * stride;
+    const bool many = mine < total && merge_parts(p, mine) >= kMergeWgParts;
+    for (unsigned long long m = __ballot(many); m != 0; m &= m - 1)
+      merge_one_wg<QT, D, G>(p, base + (long long)__builtin_ctzll(m) * stride, s);
+  }
 }
 
 // The same with the group size G = Hq / Hkv read at run time.
