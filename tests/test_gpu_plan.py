@@ -9,7 +9,11 @@ per resident wave and kv head); these cases push that cut to its ends:
     and the causal rows of one sequence share chunks;
   * thousands of short prefill sequences between decode rows, so that the
     planner's prefill tiles span several blocks of sequences and one block
-    holds more tiles than the planner has threads.
+    holds more tiles than the planner has threads;
+  * long rows cut into hundreds of pieces, which a whole wave writes and a
+    whole workgroup merges: with sinks, soft cap and an e4m3 cache in the
+    prefill kernel's merge; in the stand-alone merge kernel (f32); and beside
+    a prefill chunk on the side stream.
 Each compares rpa_forward with the oracle to the dtype's tolerance and the
 updated cache bit for bit."""
 import math
@@ -54,6 +58,19 @@ def _case(label, seed, device="cuda"):
                 kv_lens.append(q + int(rng.integers(0, 41)))
         args = dict(num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=16,
                     q_dtype="bf16", kv_in_dtype="bf16", cache_dtype="bf16", distribution=(0, 0, n))
+    elif label == "long_row_sink_fp8":
+        q_lens, kv_lens = [1, 1], [120_000, int(rng.integers(100, 400))]
+        args = dict(num_q_heads=16, num_kv_heads=2, head_dim=64, page_size=32, q_dtype="bf16",
+                    kv_in_dtype="bf16", cache_dtype="fp8", distribution=(2, 0, 0),
+                    logits_soft_cap=30.0, with_sink=True, k_scale=0.05, v_scale=0.05)
+    elif label == "long_row_f32":
+        q_lens, kv_lens = [1, 1], [60_000, int(rng.integers(100, 400))]
+        args = dict(num_q_heads=4, num_kv_heads=1, head_dim=64, page_size=16, q_dtype="f32",
+                    kv_in_dtype="f32", cache_dtype="f32", distribution=(2, 0, 0), with_sink=True)
+    elif label == "long_row_beside_prefill":
+        q_lens, kv_lens = [1, 300], [100_000, 500]
+        args = dict(num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16, q_dtype="bf16",
+                    kv_in_dtype="bf16", cache_dtype="bf16", distribution=(1, 1, 0))
     elif label == "f32_prefill_rows":
         q_lens, kv_lens = [300, 1, 5], [5000, 3000, 5]
         args = dict(num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=32,
@@ -64,16 +81,35 @@ def _case(label, seed, device="cuda"):
     return W.build(label, q_lens=q_lens, kv_lens=kv_lens, **args, **common)
 
 
+def _workspace(w):
+    import ragged_paged_kv_scatter_amd as rpa
+    kv_t = torch.from_numpy(np.ascontiguousarray(w.kv_lens)).cuda()
+    bt_t = torch.from_numpy(np.ascontiguousarray(w.block_tables)).cuda()
+    nbytes = rpa.rpa_workspace_bytes(
+        rpa._desc(w.queries, rpa._dtype(w.keys), w.kv_cache, kv_t, bt_t),
+        rpa._options(**w.options(), chunk_prefill_size=None, num_kv_pages_per_block=None,
+                     num_queries_per_block=None, vmem_limit_bytes=None))
+    return torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+
+
 @pytest.mark.parametrize("label", ["one_long_row", "tiny_rows_3000", "tiny_rows_4500",
-                                   "many_prefill_seqs", "f32_prefill_rows"])
+                                   "many_prefill_seqs", "long_row_sink_fp8", "long_row_f32",
+                                   "long_row_beside_prefill", "f32_prefill_rows"])
 def test_plan_extremes_match_oracle(label):
     print(f"\n[case] plan {label}", flush=True)
     w = _case(label, seed=9100 + len(label))
     poison_unused(w)
     before = bits(w.kv_cache, w.cache_dtype)
     ref, ref_cache = oracle_forward(w, cache_bits=before)
-    out = gpu_forward(w)
+    ws = _workspace(w)
+    out = gpu_forward(w, workspace=ws)
     torch.cuda.synchronize()
+    if label.startswith("long_row"):
+        # the long row alone is cut into more than 64 pieces: written by its
+        # whole wave and merged by a whole workgroup
+        n_items = int(ws[:64].view(torch.int32)[2])
+        print(f"[{label}] items={n_items}", flush=True)
+        assert n_items > 64 + 2
     np.testing.assert_array_equal(bits(w.kv_cache, w.cache_dtype), ref_cache)
     n_valid = int(w.query_start_loc[w.num_seqs])
     o = out[:n_valid].double().cpu().numpy()
