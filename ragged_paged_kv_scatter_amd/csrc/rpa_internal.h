@@ -20,7 +20,11 @@ namespace rpa {
 // split partials (the rows cut by a chunk boundary) and fewer than
 // kTargetItems split rows.
 constexpr int kTargetItems = 2048;    // chunks at most
-constexpr int kMinSplit = 128;        // never cut a row's KV range finer than this
+// Never cut a row's KV range finer than kMinSplit keys.  Finer pieces add
+// partials to merge without speeding up the row kernel: a long row over few
+// kv heads (one 200K-key row at Hkv 1) ran 80 us in all at 128 keys, 51 us at
+// 256; at 512 the row kernel of small batches had too few waves.
+constexpr int kMinSplit = 256;
 // Chunks the planner may make for a row kernel with this many resident waves;
 // the row kernel is launched with this many waves per kv head.
 __host__ __device__ inline int row_chunks_max(int row_waves, int Hkv) {
