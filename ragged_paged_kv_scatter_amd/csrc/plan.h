@@ -21,6 +21,12 @@ constexpr int kWaves = kT / 64;
 // pass it, so the wave's walk over them stays short; a lower bound would
 // serialise the many rows of a batch with a handful of pieces each.
 constexpr int kWavePieces = 64;
+// A row is cut into at most about kRowPieces pieces: chunks hold at least
+// (longest row's visible keys) / kRowPieces keys.  One 200K-key row at Hkv 1
+// in 128-, 256- and 512-key pieces ran 80, 51 and 41 us in all (the merge of
+// its partials shrinks faster than the row kernel slows); batches of short
+// rows keep the finer chunks their row kernel needs.
+constexpr int kRowPieces = 256;
 
 __device__ __forceinline__ int lane_value(int v, int lane) {
   return __builtin_amdgcn_readlane(v, lane);
@@ -59,6 +65,18 @@ __device__ __forceinline__ V wave_inclusive_scan(V x) {
   x += dpp_or_zero<0x118, 0xF>(x);                  // row_shr:8
   x += dpp_or_zero<0x142, 0xA>(x);                  // row_bcast:15, rows 1 and 3
   x += dpp_or_zero<0x143, 0xC>(x);                  // row_bcast:31, rows 2 and 3
+  return x;
+}
+
+// Inclusive running max over the 64 lanes of a wave for values >= 0 (lanes
+// outside a shift's reach read 0, the identity), on the same DPP moves.
+__device__ __forceinline__ int wave_inclusive_max(int x) {
+  x = max(x, dpp_or_zero<0x111, 0xF>(x));
+  x = max(x, dpp_or_zero<0x112, 0xF>(x));
+  x = max(x, dpp_or_zero<0x114, 0xF>(x));
+  x = max(x, dpp_or_zero<0x118, 0xF>(x));
+  x = max(x, dpp_or_zero<0x142, 0xA>(x));
+  x = max(x, dpp_or_zero<0x143, 0xC>(x));
   return x;
 }
 
@@ -135,6 +153,7 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
   __shared__ int32_t s_w32[kWaves + 1];
   __shared__ int32_t s_w32b[kWaves + 1];
   __shared__ int32_t s_w32c[kWaves + 1];
+  __shared__ int32_t s_wmax[kWaves + 1];             // longest row: wave maxima, then the block's
   __shared__ int32_t s_pf_first[kT + 1];            // a block's first prefill item per thread
   __shared__ int32_t s_pf_qlen[kT];
 
@@ -154,9 +173,10 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
   // ---- pass 1: per-sequence row counts, prefill tiles, visible-key totals ----
   int row_base = 0, pf_base = 0;
   long long vis_total = 0, pf_vis_total = 0;
+  int vmax_total = 0;                               // visible keys of the longest row
   for (int base = 0; base < num_seqs; base += kT) {
     const int s = base + threadIdx.x;
-    int n_rows = 0, n_pf = 0;
+    int n_rows = 0, n_pf = 0, vmax = 0;
     long long vis = 0, pf_vis = 0;
     int q0 = 0, q_len = 0, ctx = 0;
     if (s < num_seqs) {
@@ -175,6 +195,7 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
         } else {
           n_rows = q_len;
           vis = visible_sum(ctx, q_len, W);
+          vmax = (W > 0) ? min(ctx + q_len, W) : ctx + q_len;   // its last row
         }
       }
     }
@@ -184,14 +205,19 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
     const int x_pf = scan_up(n_pf, s_w32b);
     scan_up(vis, s_w64);
     scan_up(pf_vis, s_w64b);
+    const int x_max = wave_inclusive_max(vmax);
+    if ((threadIdx.x & 63) == 63) s_wmax[threadIdx.x >> 6] = x_max;
     __syncthreads();
     if (threadIdx.x < 64) {
       scan_waves(s_w32);
       scan_waves(s_w32b);
       scan_waves(s_w64);
       scan_waves(s_w64b);
+      const int m = wave_inclusive_max(threadIdx.x < kWaves ? s_wmax[threadIdx.x] : 0);
+      if (threadIdx.x == kWaves - 1) s_wmax[kWaves] = m;
     }
     __syncthreads();
+    vmax_total = max(vmax_total, s_wmax[kWaves]);
     const int my_row = scan_down(n_rows, x_rows, s_w32, &tot_rows) + row_base;
     const int my_pf = scan_down(n_pf, x_pf, s_w32b, &tot_pf) + pf_base;
     tot_vis = s_w64[kWaves];
@@ -247,6 +273,8 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
   const long long want = row_chunks_max(co_run ? p.row_waves / 8 * kCoRowEighths : p.row_waves, p.Hkv);
   long long C = div_nonneg(vis_total + want - 1, want);
   if (C < kMinSplit) C = kMinSplit;
+  if (C < div_nonneg(vmax_total + kRowPieces - 1, kRowPieces))
+    C = div_nonneg(vmax_total + kRowPieces - 1, kRowPieces);
   const int n_chunks = (int)min(div_nonneg(vis_total + C - 1, C), (long long)kTargetItems);
   int32_t* chunk_first = reinterpret_cast<int32_t*>(ws + p.lay.chunks);
 
