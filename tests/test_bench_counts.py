@@ -57,3 +57,13 @@ def test_window_caps_visible_keys():
     kvb, flops = bench.work_counts(w)
     assert kvb == 4096 * 2 * 1 * 64 * 1
     assert flops == 4 * 64 * 4096 * 8
+
+
+def test_more_than_one_gpu_is_refused():
+    # the path needs no collective; bench.py measures one GPU and says so
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout.strip() == ""
