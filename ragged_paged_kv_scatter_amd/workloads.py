@@ -251,12 +251,26 @@ def fp8_full(device="cpu", seed=1004, n_decode=64, decode_kv=(2048, 16384), n_pr
                  seed=seed, device=device, rng=rng, **args)
 
 
+def long_decode_bf16(device="cpu", seed=1005, kv_len=131072, **kw) -> Workload:
+    """One decode sequence over a long context: q_len 1, kv_len 131072;
+    page_size 16; Hq 32, Hkv 8, D 128, bf16 (the decode workload's heads).
+    Its single row is cut across the GPU and merged by log-sum-exp."""
+    rng = np.random.default_rng(seed)
+    args = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16)
+    args.update(kw)
+    return build("long_decode_bf16", q_lens=[1], kv_lens=[kv_len], distribution=(1, 0, 0),
+                 q_dtype="bf16", kv_in_dtype="bf16", cache_dtype="bf16",
+                 softmax_scale=1 / math.sqrt(args["head_dim"]), seed=seed, device=device,
+                 rng=rng, **args)
+
+
 RECIPES = {
     "tiny_fp32": tiny_fp32,
     "decode_bf16": decode_bf16,
     "mixed_bf16": mixed_bf16,
     "prefill_bf16": prefill_bf16,
     "fp8_full": fp8_full,
+    "long_decode_bf16": long_decode_bf16,
 }
 
 # Scaled-down variants with the same structure, for CPU oracle runs and fast
@@ -268,6 +282,7 @@ SMALL = {
     "prefill_bf16": dict(n_seqs=2, seq_len=300),
     "fp8_full": dict(n_decode=8, decode_kv=(40, 600), n_prefill=2, chunk=100, ctx=150,
                      sliding_window=128),
+    "long_decode_bf16": dict(kv_len=5000),
 }
 
 

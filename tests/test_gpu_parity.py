@@ -17,7 +17,7 @@ from tests.helpers import (bits, compact_pages, gpu_forward, oracle_forward, poi
                            tolerance)
 
 pytestmark = pytest.mark.gpu
-NAMES = ["tiny_fp32", "decode_bf16", "mixed_bf16", "prefill_bf16", "fp8_full"]
+NAMES = ["tiny_fp32", "decode_bf16", "mixed_bf16", "prefill_bf16", "fp8_full", "long_decode_bf16"]
 
 
 def report(name, out, ref, rows):
@@ -144,7 +144,7 @@ def _with(w, **kw):
 
 
 FULL = [("tiny_fp32", 3, 8), ("decode_bf16", 24, 1), ("mixed_bf16", 12, 24),
-        ("prefill_bf16", 2, 24), ("fp8_full", 12, 24)]
+        ("prefill_bf16", 2, 24), ("fp8_full", 12, 24), ("long_decode_bf16", 1, 1)]
 
 
 @pytest.mark.parametrize("name,n_seqs,rows_per_seq", FULL)
