@@ -99,7 +99,9 @@ typedef struct rpa_desc {
 
 /* Scalar options of rpa_forward (the v3 keyword arguments). */
 typedef struct rpa_options {
-  float softmax_scale;      /* multiplies q.k (v3 default 1.0; pass it explicitly) */
+  float softmax_scale;      /* multiplies q.k (v3 default 1.0; pass it explicitly).  Any
+                               finite value: 0 gives every visible key equal weight, a
+                               negative scale favours the least similar keys */
   int32_t sliding_window;   /* 0 = off; W > 0: key j visible iff pos - j < W */
   float logits_soft_cap;    /* 0 = off; c > 0: s -> c * tanh(s / c), after all scales */
   float q_scale;            /* 0 = none (1.0); multiplies the logits */
@@ -224,17 +226,41 @@ int rpa_workspace_bytes(const rpa_desc* desc, const rpa_options* opts, size_t* b
  * owned, contents need not be initialised; it is overwritten).
  * Concurrent calls must use distinct workspaces.
  * When the batch has more tokens than max_num_seqs (so some sequence has
- * prefill rows), the prefill kernel runs on the library's own stream for the
- * device of `stream` (created with two events on the first such call and kept
- * until the process ends): it is forked off `stream` after the planner and
- * joined back before the call returns, so all of the call's work is still
- * ordered on `stream`, including under HIP graph capture.
+ * prefill rows), the prefill kernel runs on a side stream of the library's:
+ * one per (device, caller stream), created with two events on the first such
+ * call from that stream and kept until the process ends.  It is forked off
+ * `stream` after the planner and joined back before the call returns, so all
+ * of the call's work is still ordered on `stream`, including under HIP graph
+ * capture; calls from different streams never share a side stream, so a
+ * capture on one stream does not reach calls made from another.
  */
 int rpa_forward(const rpa_desc* desc, const rpa_options* opts, const void* queries,
                 const void* keys, const void* values, void* kv_cache, const int32_t* kv_lens,
                 const int32_t* block_tables, const int32_t* query_start_loc,
                 const int32_t* distribution, const float* attention_sink, void* out,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Tracing.  With the environment variable RPA_TRACE set (to anything but
+ * "0"), every rpa_forward call writes its trace to stderr: one "[rpa] forward"
+ * line with the sizes and options, one "[rpa] workspace" line with the byte
+ * offset of every workspace section and the bounds they are sized for, one
+ * "[rpa] streams" line, one "[rpa] launch" line per kernel (name, grid,
+ * block, LDS bytes, stream), and a last "[rpa] plan" line with the plan
+ * header the device wrote (its counts of rows, items, chunks, merges and
+ * prefill tiles, and the side-by-side flag).  Reading the plan back
+ * synchronises the stream, so it is skipped while the stream is being
+ * captured into a graph.  The tpu-inference v3 kernel diff has the same kind
+ * of switchable debug printing ("[RPA debug]" lines).
+ *
+ * rpa_trace_format writes into buf the trace an rpa_forward with these sizes
+ * and options (with or without the update) would print before its plan line,
+ * without touching any device memory or launching anything: the same checks,
+ * workspace layout and launch sequence, run dry.  The text is NUL-terminated
+ * and cut to buf_bytes - 1 characters; *text_bytes (if non-NULL) receives its
+ * full length.  Returns the status rpa_forward would return from its host
+ * checks. */
+int rpa_trace_format(const rpa_desc* desc, const rpa_options* opts, int with_update, char* buf,
+                     size_t buf_bytes, size_t* text_bytes);
 
 /* Bits of the device status word written by rpa_validate_metadata. */
 enum {

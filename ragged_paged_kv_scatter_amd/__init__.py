@@ -19,7 +19,8 @@ from ._lib import RpaDesc, RpaError, RpaKernelStat, RpaOptions
 
 __all__ = ["rpa_update_kv_cache", "rpa_forward", "rpa_workspace_bytes", "rpa_slot_mapping",
            "rpa_reshape_and_cache", "rpa_copy_blocks", "rpa_swap_blocks",
-           "rpa_validate_metadata", "profile_enable", "profile_read", "RpaError",
+           "rpa_validate_metadata", "rpa_trace_format", "profile_enable", "profile_read",
+           "RpaError",
            "META_QSL", "META_LENS", "META_BLOCK_TABLE", "META_SLOTS", "META_DISTRIBUTION"]
 
 # bits of rpa_validate_metadata's status word (include/rpa.h RPA_META_*)
@@ -59,6 +60,37 @@ def _meta(t: torch.Tensor, name: str):
     if t.dtype != torch.int32:
         raise TypeError(f"{name} must be int32")
     return t
+
+
+def _check_meta(kv_lens, block_tables, query_start_loc, distribution):
+    """dtype and sizes of the metadata: the C ABI reads kv_lens[max_num_seqs],
+    block_tables[max_num_seqs * pages_per_seq], query_start_loc[max_num_seqs + 1]
+    and distribution[3] and cannot see their lengths."""
+    for t, n in ((kv_lens, "kv_lens"), (block_tables, "block_tables"),
+                 (query_start_loc, "query_start_loc"), (distribution, "distribution")):
+        _meta(t, n)
+    if kv_lens.dim() != 1:
+        raise ValueError("kv_lens must be 1-D [max_num_seqs]")
+    max_num_seqs = kv_lens.shape[0]
+    if query_start_loc.numel() < max_num_seqs + 1:
+        raise ValueError(f"query_start_loc needs max_num_seqs + 1 = {max_num_seqs + 1} "
+                         f"entries, got {query_start_loc.numel()}")
+    if distribution.numel() != 3:
+        raise ValueError("distribution must hold 3 counts (decode, prefill, mixed)")
+    if max_num_seqs > 0 and (block_tables.numel() == 0 or block_tables.numel() % max_num_seqs):
+        raise ValueError("block_tables must hold max_num_seqs * pages_per_seq entries")
+
+
+def _check_new_kv(keys, values, T, Hkv, D):
+    """keys / values: [T, Hkv, D], one dtype."""
+    if keys.dim() != 3 or tuple(keys.shape) != (T, Hkv, D):
+        raise ValueError(f"keys must be [{T}, {Hkv}, {D}] (total_tokens, num_kv_heads, "
+                         f"head_dim), got {tuple(keys.shape)}")
+    if tuple(values.shape) != tuple(keys.shape):
+        raise ValueError(f"values must have the shape of keys {tuple(keys.shape)}, got "
+                         f"{tuple(values.shape)}")
+    if values.dtype != keys.dtype:
+        raise TypeError(f"values dtype {values.dtype} differs from keys dtype {keys.dtype}")
 
 
 def _cache_dims(kv_cache: torch.Tensor):
@@ -112,11 +144,15 @@ def _stream(dev):
 def rpa_update_kv_cache(keys, values, kv_cache, kv_lens, block_tables, query_start_loc,
                         distribution, *, k_scale=None, v_scale=None, queries_dtype=None):
     """Write new tokens' K/V ([T, Hkv, D]) into their pages of `kv_cache` in place."""
-    dev = _check_dev(keys, values, kv_cache, kv_lens, block_tables, query_start_loc, distribution)
-    for t, n in ((kv_lens, "kv_lens"), (block_tables, "block_tables"),
-                 (query_start_loc, "query_start_loc"), (distribution, "distribution")):
-        _meta(t, n)
+    _check_meta(kv_lens, block_tables, query_start_loc, distribution)
+    if keys.dim() != 3:
+        raise ValueError("keys must be [total_tokens, num_kv_heads, head_dim]")
     T, Hkv, D = keys.shape
+    _check_new_kv(keys, values, T, Hkv, D)
+    _, _, two_h, _ = _cache_dims(kv_cache)
+    if two_h != 2 * Hkv:
+        raise ValueError(f"kv_cache holds {two_h} head rows per token, keys need 2 * {Hkv}")
+    dev = _check_dev(keys, values, kv_cache, kv_lens, block_tables, query_start_loc, distribution)
     qdt = queries_dtype if queries_dtype is not None else (
         torch.float32 if keys.dtype == torch.float32 else torch.bfloat16)
     fake_q = torch.empty((T, Hkv, D), dtype=qdt, device="meta")
@@ -135,10 +171,8 @@ def rpa_validate_metadata(queries, kv_cache, kv_lens, block_tables, query_start_
     rpa_forward for these tensors' sizes.  Returns the device int32[1] status
     tensor (the OR of META_* bits, 0 when all hold); the C call does not
     synchronise, so read it with ``int(status.item())``."""
+    _check_meta(kv_lens, block_tables, query_start_loc, distribution)
     dev = _check_dev(queries, kv_cache, kv_lens, block_tables, query_start_loc, distribution)
-    for t, n in ((kv_lens, "kv_lens"), (block_tables, "block_tables"),
-                 (query_start_loc, "query_start_loc"), (distribution, "distribution")):
-        _meta(t, n)
     kin = kv_in_dtype if kv_in_dtype is not None else _dtype(kv_cache)
     d = _desc(queries, kin, kv_cache, kv_lens, block_tables)
     words = (d.num_pages * d.page_size + 31) // 32
@@ -170,13 +204,9 @@ def rpa_slot_mapping(kv_lens, block_tables, query_start_loc, distribution, *, pa
                      total_tokens, out=None):
     """Flat cache slot (int64 [total_tokens]) of every new token row; -1 for rows
     past the last sequence."""
+    _check_meta(kv_lens, block_tables, query_start_loc, distribution)
     dev = _check_dev(kv_lens, block_tables, query_start_loc, distribution, out)
-    for t, n in ((kv_lens, "kv_lens"), (block_tables, "block_tables"),
-                 (query_start_loc, "query_start_loc"), (distribution, "distribution")):
-        _meta(t, n)
     max_num_seqs = kv_lens.shape[0]
-    if block_tables.numel() % max(max_num_seqs, 1):
-        raise ValueError("block_tables must hold max_num_seqs * pages_per_seq entries")
     pps = block_tables.numel() // max(max_num_seqs, 1)
     if out is None:
         out = torch.empty(total_tokens, dtype=torch.int64, device=dev)
@@ -272,6 +302,46 @@ def rpa_workspace_bytes(desc: RpaDesc, opts: RpaOptions) -> int:
     return n.value
 
 
+def _forward_args(queries, keys, values, kv_cache, kv_lens, block_tables, query_start_loc,
+                  distribution, attention_sink, out, workspace, softmax_scale, sliding_window,
+                  logits_soft_cap, q_scale, k_scale, v_scale, chunk_prefill_size,
+                  num_kv_pages_per_block, num_queries_per_block, vmem_limit_bytes):
+    """Checks and marshalling of rpa_forward's arguments:
+    every size and dtype check runs before the device check (no launch on a
+    mismatch).  Returns (device, desc, options, out)."""
+    if (keys is None) != (values is None):
+        raise ValueError("keys and values must both be given or both be None")
+    _check_meta(kv_lens, block_tables, query_start_loc, distribution)
+    if queries.dim() != 3:
+        raise ValueError("queries must be [total_tokens, num_q_heads, head_dim]")
+    T, Hq, D = queries.shape
+    _, _, two_h, _ = _cache_dims(kv_cache)
+    if keys is not None:
+        _check_new_kv(keys, values, T, two_h // 2, D)
+    if attention_sink is not None:
+        if attention_sink.dtype != torch.float32:
+            raise TypeError("attention_sink must be float32")
+        if attention_sink.numel() != Hq:
+            raise ValueError(f"attention_sink must hold num_q_heads = {Hq} values, got "
+                             f"{attention_sink.numel()}")
+    if out is not None:
+        if tuple(out.shape) != tuple(queries.shape) or out.dtype != queries.dtype:
+            raise ValueError(f"out must be {tuple(queries.shape)} {queries.dtype}, got "
+                             f"{tuple(out.shape)} {out.dtype}")
+        if not out.is_contiguous():
+            raise ValueError("out must be contiguous")
+    dev = _check_dev(queries, keys, values, kv_cache, kv_lens, block_tables, query_start_loc,
+                     distribution, attention_sink, out, workspace)
+    kv_in = _dtype(keys) if keys is not None else _dtype(kv_cache)
+    d = _desc(queries, kv_in, kv_cache, kv_lens, block_tables)
+    o = _options(softmax_scale, sliding_window, logits_soft_cap, q_scale, k_scale, v_scale,
+                 chunk_prefill_size, num_kv_pages_per_block, num_queries_per_block,
+                 vmem_limit_bytes)
+    if out is None:
+        out = torch.empty(queries.shape, dtype=queries.dtype, device=dev)
+    return dev, d, o, out
+
+
 def rpa_forward(queries, keys, values, kv_cache, kv_lens, block_tables, query_start_loc,
                 distribution, attention_sink=None, *, softmax_scale=1.0, sliding_window=None,
                 logits_soft_cap=None, q_scale=None, k_scale=None, v_scale=None,
@@ -280,27 +350,14 @@ def rpa_forward(queries, keys, values, kv_cache, kv_lens, block_tables, query_st
     """Ragged paged attention (v3 semantics).  `keys`/`values` may be None to
     attend over the cache as it is.  Returns ``(out, kv_cache)``; the cache is
     updated in place."""
-    if (keys is None) != (values is None):
-        raise ValueError("keys and values must both be given or both be None")
-    dev = _check_dev(queries, keys, values, kv_cache, kv_lens, block_tables, query_start_loc,
-                     distribution, attention_sink, out, workspace)
-    for t, n in ((kv_lens, "kv_lens"), (block_tables, "block_tables"),
-                 (query_start_loc, "query_start_loc"), (distribution, "distribution")):
-        _meta(t, n)
-    if attention_sink is not None and attention_sink.dtype != torch.float32:
-        raise TypeError("attention_sink must be float32")
-    kv_in = _dtype(keys) if keys is not None else _dtype(kv_cache)
-    d = _desc(queries, kv_in, kv_cache, kv_lens, block_tables)
-    if keys is not None and keys.shape[1] != d.num_kv_heads:
-        raise ValueError("keys head count does not match the cache")
-    o = _options(softmax_scale, sliding_window, logits_soft_cap, q_scale, k_scale, v_scale,
-                 chunk_prefill_size, num_kv_pages_per_block, num_queries_per_block,
-                 vmem_limit_bytes)
+    dev, d, o, out = _forward_args(
+        queries, keys, values, kv_cache, kv_lens, block_tables, query_start_loc, distribution,
+        attention_sink, out, workspace, softmax_scale, sliding_window, logits_soft_cap, q_scale,
+        k_scale, v_scale, chunk_prefill_size, num_kv_pages_per_block, num_queries_per_block,
+        vmem_limit_bytes)
     nbytes = rpa_workspace_bytes(d, o)
     if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    if out is None:
-        out = torch.empty(queries.shape, dtype=queries.dtype, device=dev)
     lib = _lib.load()
     with torch.cuda.device(dev):    # the library sizes launches for the current device
         _lib.check(lib.rpa_forward(
@@ -309,6 +366,20 @@ def rpa_forward(queries, keys, values, kv_cache, kv_lens, block_tables, query_st
             _ptr(distribution), _ptr(attention_sink), _ptr(out), _ptr(workspace),
             ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(dev)))
     return out, kv_cache
+
+
+def rpa_trace_format(desc: RpaDesc, opts: RpaOptions, with_update: bool = True) -> str:
+    """The trace an rpa_forward with these sizes and options prints under
+    RPA_TRACE=1 (before its plan line), computed on the host without touching
+    the device."""
+    need = ctypes.c_size_t(0)
+    lib = _lib.load()
+    _lib.check(lib.rpa_trace_format(ctypes.byref(desc), ctypes.byref(opts), int(with_update),
+                                    None, 0, ctypes.byref(need)))
+    buf = ctypes.create_string_buffer(need.value + 1)
+    _lib.check(lib.rpa_trace_format(ctypes.byref(desc), ctypes.byref(opts), int(with_update),
+                                    buf, need.value + 1, ctypes.byref(need)))
+    return buf.value.decode()
 
 
 def profile_enable(on: bool = True):

@@ -15,7 +15,7 @@ STATUS = {0: "RPA_OK", 1: "RPA_ERR_NULL_POINTER", 2: "RPA_ERR_INVALID_SHAPE",
 EXPORTS = ("rpa_update_kv_cache", "rpa_workspace_bytes", "rpa_forward", "rpa_error_string",
            "rpa_profile_enable", "rpa_profile_read", "rpa_slot_mapping",
            "rpa_reshape_and_cache", "rpa_copy_blocks", "rpa_swap_blocks",
-           "rpa_validate_metadata")
+           "rpa_validate_metadata", "rpa_trace_format")
 
 
 class RpaDesc(ctypes.Structure):
@@ -93,6 +93,10 @@ def load():
     lib.rpa_swap_blocks.restype = ctypes.c_int
     lib.rpa_validate_metadata.argtypes = [ctypes.POINTER(RpaDesc), P, P, P, P, P, P, P]
     lib.rpa_validate_metadata.restype = ctypes.c_int
+    lib.rpa_trace_format.argtypes = [ctypes.POINTER(RpaDesc), ctypes.POINTER(RpaOptions),
+                                     ctypes.c_int, ctypes.c_char_p, ctypes.c_size_t,
+                                     ctypes.POINTER(ctypes.c_size_t)]
+    lib.rpa_trace_format.restype = ctypes.c_int
     del I32P
     _lib = lib
     return lib

@@ -23,6 +23,7 @@
 // of the i-th page of a 64-page window and lanes fetch theirs with a bpermute.
 #include <math.h>
 
+#include <cstdio>
 #include <utility>
 
 #include "device_common.h"
@@ -946,6 +947,16 @@ hipError_t launch_rows_t(const AttnParams& p, hipStream_t s) {
   const long long waves =
       (long long)row_chunks_max(Cfg::resident() * kWavesPerWG, p.Hkv) * p.Hkv;
   dim3 grid((unsigned)((waves + kWavesPerWG - 1) / kWavesPerWG));
+  if (trace_active()) {
+    char nm[96];
+    if constexpr (Cfg::MF)
+      std::snprintf(nm, sizeof nm, "mfma_row_kernel<%s,D%d,G%d%s>", elem_name<CT>(), D, G,
+                    CAP ? ",cap" : "");
+    else
+      std::snprintf(nm, sizeof nm, "row_kernel<%s,%s,D%d,G%d,EPL%d,NR%d%s>", elem_name<QT>(),
+                    elem_name<CT>(), D, G, Cfg::EPL, Cfg::NR, CAP ? ",cap" : "");
+    if (trace_launch(nm, grid.x, 64 * kWavesPerWG, 0, s)) return hipSuccess;
+  }
   if constexpr (Cfg::MF) mfma_row_kernel<CT, D, (Cfg::MF ? G : 8), CAP><<<grid, 64 * kWavesPerWG, 0, s>>>(p);
   else row_kernel<QT, CT, D, G, Cfg::EPL, Cfg::NR, CAP><<<grid, 64 * kWavesPerWG, 0, s>>>(p);
   return hipGetLastError();
@@ -1021,6 +1032,11 @@ hipError_t launch_rows(const AttnParams& p, rpa_dtype q_dt, rpa_dtype cache_dt, 
 namespace {
 template <typename QT, int D>
 hipError_t launch_merge_d(const AttnParams& p, dim3 grid, hipStream_t s) {
+  if (trace_active()) {
+    char nm[64];
+    std::snprintf(nm, sizeof nm, "merge_kernel<%s,D%d,G%d>", elem_name<QT>(), D, p.Hq / p.Hkv);
+    if (trace_launch(nm, grid.x, 256, 0, s)) return hipSuccess;
+  }
   switch (p.Hq / p.Hkv) {
     case 1: merge_kernel<QT, D, 1><<<grid, 256, 0, s>>>(p); break;
     case 2: merge_kernel<QT, D, 2><<<grid, 256, 0, s>>>(p); break;

@@ -275,7 +275,9 @@ __device__ __forceinline__ void plan_body(const PlanParams& p, int32_t* s_seq_ro
   if (C < kMinSplit) C = kMinSplit;
   if (C < div_nonneg(vmax_total + kRowPieces - 1, kRowPieces))
     C = div_nonneg(vmax_total + kRowPieces - 1, kRowPieces);
-  const int n_chunks = (int)min(div_nonneg(vis_total + C - 1, C), (long long)kTargetItems);
+  // (C >= vis_total / want keeps this within `want`, which is at most the
+  // layout's max_chunks: the bound only guards the chunk table)
+  const int n_chunks = (int)min(div_nonneg(vis_total + C - 1, C), (long long)p.lay.max_chunks);
   int32_t* chunk_first = reinterpret_cast<int32_t*>(ws + p.lay.chunks);
 
   // row r -> (seq, token, visible range [lo, hi))

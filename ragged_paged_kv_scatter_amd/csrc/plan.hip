@@ -3,6 +3,7 @@
 // write them into the paged cache (scatter.h).  The two parts touch disjoint
 // memory and neither reads the other's output, so one launch serves both.
 #include <algorithm>
+#include <cstdio>
 
 #include "plan.h"
 #include "scatter.h"
@@ -35,6 +36,14 @@ hipError_t launch_prep(const PlanParams& pp, const ScatterParams* sp, rpa_dtype 
     grid = 1u + (unsigned)((p.T + tpw - 1) / tpw);
   } else {
     in_dt = cache_dt = RPA_BF16;                    // planner only
+  }
+  if (trace_active()) {
+    char nm[96];
+    std::snprintf(nm, sizeof nm, "prep_kernel<%s,%s>(plan%s, rows_per_wg=%d)",
+                  in_dt == RPA_F32 ? "f32" : in_dt == RPA_BF16 ? "bf16" : "fp8",
+                  cache_dt == RPA_F32 ? "f32" : cache_dt == RPA_BF16 ? "bf16" : "fp8",
+                  grid > 1 ? "+scatter" : "", tpw);
+    if (trace_launch(nm, grid, kPlanThreads, lds, s)) return hipSuccess;
   }
   if (in_dt == RPA_F32 && cache_dt == RPA_F32) {
     prep_kernel<float, float><<<grid, kPlanThreads, lds, s>>>(pp, p, tpw);

@@ -28,6 +28,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <cstdio>
 
 #include <type_traits>
 
@@ -171,7 +172,17 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
   const int pmask = (1 << sh) - 1;
   const uint32_t row_bytes = 2u * Hkv * p.Dpad * (uint32_t)ESZ;  // one cache token row
   const uint32_t v_bytes = (uint32_t)p.Dpad * ESZ;               // K row -> V row
-  const float c_scale = CAP ? p.qk_scale : p.qk_scale * kLog2e;
+  // Logits are masked before they are scaled (see logit() and expo()), which
+  // needs a positive scale: a masked -inf times 0 is NaN and times a negative
+  // scale turns into +inf.  The logit q.k * scale is therefore formed as
+  // (sign(scale) q).k * |scale|: a negative scale flips the sign bits of the
+  // bf16 q (exact), and a zero scale zeroes q and keeps a scale of 1, so every
+  // visible logit is exactly 0, as the definition gives.
+  const bool q_zero = p.qk_scale == 0.f;
+  const uint32_t q_and = q_zero ? 0u : 0xFFFFFFFFu;
+  const uint32_t q_xor = p.qk_scale < 0.f ? 0x80008000u : 0u;
+  const float scale_pos = q_zero ? 1.f : fabsf(p.qk_scale);
+  const float c_scale = CAP ? scale_pos : scale_pos * kLog2e;
   const float c_eff = CAP ? 1.f : c_scale;       // stored logits -> log2 units
   const float cap_k = CAP ? c_scale * 2.f * kLog2e / p.cap : 0.f;
   const float cap_l2 = CAP ? p.cap * kLog2e : 0.f;
@@ -401,6 +412,8 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qp + 16 * ks) : make_uint4(0, 0, 0, 0);
+        v = make_uint4((v.x & q_and) ^ q_xor, (v.y & q_and) ^ q_xor, (v.z & q_and) ^ q_xor,
+                       (v.w & q_and) ^ q_xor);
         qreg[ks] = __builtin_bit_cast(bf16x8, v);
       }
     }
@@ -662,6 +675,12 @@ hipError_t launch_d(const AttnParams& p, long long blocks, hipStream_t s) {
   static const long long resident =
       resident_grid(reinterpret_cast<const void*>(&prefill_kernel<CT, D, CAP>));
   if (blocks > resident) blocks = resident;
+  if (trace_active()) {
+    char nm[80];
+    std::snprintf(nm, sizeof nm, "prefill_kernel<%s,D%d%s>(%s)", elem_name<CT>(), D,
+                  CAP ? ",cap" : "", p.fuse_merge ? "merge+tiles" : "tiles");
+    if (trace_launch(nm, (unsigned)blocks, NT, 0, s)) return hipSuccess;
+  }
   prefill_kernel<CT, D, CAP><<<dim3((unsigned)blocks), NT, 0, s>>>(p);
   return hipGetLastError();
 }

@@ -5,8 +5,11 @@
 
 #include <climits>
 #include <cmath>
+#include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -91,8 +94,58 @@ std::mutex g_prof_mu;
 bool g_prof_on = false;
 std::vector<ProfRec> g_prof_recs;
 std::vector<hipEvent_t> g_event_pool;
-ProfRec g_pending;
-bool g_have_pending = false;
+// A launch's begin and end are recorded by the thread that launches it, so
+// the pending record is per thread: concurrent callers pair their own events.
+thread_local ProfRec t_pending;
+thread_local bool t_have_pending = false;
+
+// ---- tracing (RPA_TRACE=1, or rpa_trace_format's dry run) ------------------
+// One call's trace: its sizes and options, the workspace layout, every launch
+// with its geometry, and (RPA_TRACE only, outside graph capture) the plan
+// header read back from the device.  In a dry run nothing is launched or
+// recorded on a stream: the launchers report their geometry and return.
+struct TraceState {
+  bool on = false;
+  bool dry = false;
+  std::string* sink = nullptr;   // dry run: the text goes here, else to stderr
+};
+thread_local TraceState t_trace;
+
+bool env_trace() {
+  const char* v = std::getenv("RPA_TRACE");
+  return v && v[0] && !(v[0] == '0' && v[1] == 0);
+}
+
+void trace_printf(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+void trace_printf(const char* fmt, ...) {
+  if (!t_trace.on) return;
+  char buf[640];
+  va_list ap;
+  va_start(ap, fmt);
+  const int n = std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (n <= 0) return;
+  const size_t len = std::min((size_t)n, sizeof buf - 1);
+  if (t_trace.sink) t_trace.sink->append(buf, len);
+  else std::fwrite(buf, 1, len, stderr);
+}
+
+struct TraceScope {          // sets this thread's trace state for one call
+  TraceState saved;
+  TraceScope(bool on, bool dry, std::string* sink) : saved(t_trace) {
+    t_trace.on = on;
+    t_trace.dry = dry;
+    t_trace.sink = sink;
+  }
+  ~TraceScope() {
+    if (t_trace.on && !t_trace.sink) std::fflush(stderr);
+    t_trace = saved;
+  }
+};
+
+const char* dtype_name(int dt) {
+  return dt == RPA_F32 ? "f32" : dt == RPA_BF16 ? "bf16" : dt == RPA_FP8_E4M3 ? "fp8_e4m3" : "?";
+}
 
 hipEvent_t take_event() {
   if (!g_event_pool.empty()) {
@@ -105,22 +158,24 @@ hipEvent_t take_event() {
   return e;
 }
 
-// ---- the prefill kernel's own stream (one per device) ----------------------
-// rpa_forward forks the prefill kernel onto it after the planner and joins it
-// back before returning, so that prefill tiles can run beside the row kernel.
-// The fork / join events are shared by all callers on a device, hence the
-// lock around their record / wait pairs.
-constexpr int kMaxDevices = 64;
+// ---- side streams for the prefill kernel ----------------------------------
+// rpa_forward forks the prefill kernel onto a side stream after the planner
+// and joins it back before returning, so that prefill tiles can run beside
+// the row kernel.  There is one side stream, with its fork / join events, per
+// (device, caller stream): calls issued from different streams never share
+// one, so a HIP graph capture on one stream cannot pull another stream's
+// calls into it.  The record / wait pairs on one side stream are serialised
+// by g_side_mu.  Side streams and their events live until the process ends.
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
 };
 std::mutex g_side_mu;
-SideStream g_side[kMaxDevices];
+std::map<std::pair<int, hipStream_t>, SideStream> g_side;
 
-// The side stream of the device that `caller` (NULL: the current device's
-// default stream) belongs to, created on first use with that device current;
-// the caller holds g_side_mu.
+// The side stream of `caller` (NULL: the current device's default stream),
+// created on first use with the caller's device current; the caller holds
+// g_side_mu.
 hipError_t side_stream(hipStream_t caller, SideStream** out) {
   int dev = 0, cur = 0;
   hipError_t e = hipGetDevice(&cur);
@@ -131,8 +186,7 @@ hipError_t side_stream(hipStream_t caller, SideStream** out) {
     if ((e = hipStreamGetDevice(caller, &d)) != hipSuccess) return e;
     dev = d;
   }
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  SideStream& ss = g_side[dev];
+  SideStream& ss = g_side[std::make_pair(dev, caller)];
   if (!ss.s) {
     if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
     hipStream_t st = nullptr;
@@ -156,22 +210,39 @@ hipError_t side_stream(hipStream_t caller, SideStream** out) {
 
 }  // namespace
 
+bool trace_active() { return t_trace.on; }
+
+bool trace_launch(const char* kernel, unsigned grid, unsigned block, size_t lds, hipStream_t s) {
+  trace_printf("[rpa] launch %s grid=%u block=%u lds=%zu stream=%p\n", kernel, grid, block, lds,
+               (void*)s);
+  return t_trace.dry;
+}
+
 void prof_begin(const char* name, hipStream_t s) {
-  std::lock_guard<std::mutex> lk(g_prof_mu);
-  if (!g_prof_on) return;
-  g_pending.name = name;
-  g_pending.start = take_event();
-  g_pending.stop = take_event();
-  g_have_pending = g_pending.start && g_pending.stop;
-  if (g_have_pending) (void)hipEventRecord(g_pending.start, s);
+  t_have_pending = false;
+  if (t_trace.dry) return;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on) return;
+    t_pending.name = name;
+    t_pending.start = take_event();
+    t_pending.stop = take_event();
+    if (!t_pending.start || !t_pending.stop) {
+      if (t_pending.start) g_event_pool.push_back(t_pending.start);
+      if (t_pending.stop) g_event_pool.push_back(t_pending.stop);
+      return;
+    }
+  }
+  t_have_pending = true;
+  (void)hipEventRecord(t_pending.start, s);
 }
 
 void prof_end(hipStream_t s) {
+  if (!t_have_pending) return;
+  t_have_pending = false;
+  (void)hipEventRecord(t_pending.stop, s);
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  if (!g_prof_on || !g_have_pending) return;
-  (void)hipEventRecord(g_pending.stop, s);
-  g_prof_recs.push_back(g_pending);
-  g_have_pending = false;
+  g_prof_recs.push_back(t_pending);
 }
 
 bool prefill_supported(const rpa_desc& d);
@@ -180,16 +251,30 @@ int prefill_min_q(const rpa_desc& d) {
   return prefill_supported(d) ? 2 : INT_MAX;
 }
 
-Workspace workspace_layout(const rpa_desc& d) {
+// Resident waves of the row kernel for this call: the planner makes at most
+// row_chunks_max(waves, Hkv) chunks, which bounds the work lists.
+int row_waves_of(const rpa_desc& d, const rpa_options& o) {
+  return row_waves((rpa_dtype)d.q_dtype, (rpa_dtype)d.cache_dtype, d.head_dim,
+                   d.num_q_heads / d.num_kv_heads, o.logits_soft_cap > 0.f);
+}
+
+Workspace workspace_layout(const rpa_desc& d, const rpa_options& o) {
   Workspace w = {};
   const long long T = d.total_tokens;
   const int pmq = prefill_min_q(d);
   long long max_rows = T;
   if (pmq != INT_MAX) max_rows = std::min<long long>(T, (long long)d.max_num_seqs * (pmq - 1));
   w.max_rows = (int32_t)std::max<long long>(max_rows, 1);
-  w.max_items = kTargetItems + w.max_rows;
-  w.max_parts = std::min(2 * kTargetItems, w.max_items);
-  w.max_merge_rows = std::min(kTargetItems, w.max_rows);
+  // The rows' keys are cut into at most `chunks` chunks: every boundary
+  // between two chunks adds one item and cuts at most one row, and a chunk
+  // holds at most two pieces of rows it does not hold whole (its first and
+  // its last), so there are at most 2 * chunks split partials and fewer than
+  // `chunks` split rows.
+  const int chunks = row_chunks_max(row_waves_of(d, o), d.num_kv_heads);
+  w.max_chunks = chunks;
+  w.max_items = chunks + w.max_rows;
+  w.max_parts = std::min(2 * chunks, w.max_items);
+  w.max_merge_rows = std::min(chunks, w.max_rows);
   w.max_pf_items = (pmq != INT_MAX)
                        ? (int32_t)((T + kPrefillBQ - 1) / kPrefillBQ + d.max_num_seqs + 1)
                        : 1;
@@ -203,7 +288,7 @@ Workspace workspace_layout(const rpa_desc& d) {
   w.items = off;
   off = align256(off + (size_t)w.max_items * sizeof(ItemDesc));
   w.chunks = off;
-  off = align256(off + (size_t)(kTargetItems + 1) * sizeof(int32_t));
+  off = align256(off + (size_t)(chunks + 1) * sizeof(int32_t));
   w.merge_rows = off;
   off = align256(off + (size_t)w.max_merge_rows * sizeof(MergeDesc));
   w.pf_items = off;
@@ -407,15 +492,22 @@ int rpa_workspace_bytes(const rpa_desc* desc, const rpa_options* opts, size_t* b
   if (st) return st;
   if ((st = check_options(opts))) return st;
   if (!bytes) return RPA_ERR_NULL_POINTER;
-  *bytes = workspace_layout(*desc).total;
+  *bytes = workspace_layout(*desc, *opts).total;
   return RPA_OK;
 }
 
-int rpa_forward(const rpa_desc* desc, const rpa_options* opts, const void* queries,
-                const void* keys, const void* values, void* kv_cache, const int32_t* kv_lens,
-                const int32_t* block_tables, const int32_t* query_start_loc,
-                const int32_t* distribution, const float* attention_sink, void* out,
-                void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// rpa_forward's work.  one_stream: every kernel on the caller's stream (no
+// side stream, nothing created).  dry: check and trace only, launch nothing.
+int forward_impl(const rpa_desc* desc, const rpa_options* opts, const void* queries,
+                 const void* keys, const void* values, void* kv_cache, const int32_t* kv_lens,
+                 const int32_t* block_tables, const int32_t* query_start_loc,
+                 const int32_t* distribution, const float* attention_sink, void* out,
+                 void* workspace, size_t workspace_bytes, hipStream_t s, bool one_stream,
+                 bool dry) {
   int st = check_desc(desc);
   if (st) return st;
   if ((st = check_options(opts))) return st;
@@ -425,11 +517,26 @@ int rpa_forward(const rpa_desc* desc, const rpa_options* opts, const void* queri
   if (!aligned16(queries) || !aligned16(kv_cache) || !aligned16(out) ||
       (keys && (!aligned16(keys) || !aligned16(values))))
     return RPA_ERR_INVALID_SHAPE;
-  const Workspace lay = workspace_layout(*desc);
+  const Workspace lay = workspace_layout(*desc, *opts);
   if (!workspace || workspace_bytes < lay.total || !aligned16(workspace)) return RPA_ERR_WORKSPACE;
+  trace_printf("[rpa] forward total_tokens=%d max_num_seqs=%d pages_per_seq=%d num_pages=%d "
+               "page_size=%d num_q_heads=%d num_kv_heads=%d head_dim=%d head_dim_padded=%d "
+               "dtypes=%s/%s/%s update=%d softmax_scale=%g sliding_window=%d soft_cap=%g "
+               "q_scale=%g k_scale=%g v_scale=%g sink=%d\n",
+               desc->total_tokens, desc->max_num_seqs, desc->pages_per_seq, desc->num_pages,
+               desc->page_size, desc->num_q_heads, desc->num_kv_heads, desc->head_dim,
+               desc->head_dim_padded, dtype_name(desc->q_dtype), dtype_name(desc->kv_in_dtype),
+               dtype_name(desc->cache_dtype), keys ? 1 : 0, opts->softmax_scale,
+               opts->sliding_window, opts->logits_soft_cap, opts->q_scale, opts->k_scale,
+               opts->v_scale, attention_sink ? 1 : 0);
+  trace_printf("[rpa] workspace bytes=%zu header=%zu zeros=%zu rows=%zu items=%zu chunks=%zu "
+               "merge_rows=%zu prefill_items=%zu part_ml=%zu part_acc=%zu max_rows=%d "
+               "max_items=%d max_chunks=%d max_parts=%d max_merge_rows=%d max_prefill_items=%d\n",
+               lay.total, lay.header, lay.zeros, lay.rows, lay.items, lay.chunks, lay.merge_rows,
+               lay.pf_items, lay.part_ml, lay.part_acc, lay.max_rows, lay.max_items,
+               lay.max_chunks, lay.max_parts, lay.max_merge_rows, lay.max_pf_items);
   if (desc->total_tokens == 0 || desc->max_num_seqs == 0) return RPA_OK;
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   PlanParams pp = {};
   pp.kv_lens = kv_lens;
@@ -442,17 +549,17 @@ int rpa_forward(const rpa_desc* desc, const rpa_options* opts, const void* queri
   pp.window = opts->sliding_window;
   pp.prefill_min_q = prefill_min_q(*desc);
   pp.Hkv = desc->num_kv_heads;
-  pp.row_waves = row_waves((rpa_dtype)desc->q_dtype, (rpa_dtype)desc->cache_dtype,
-                           desc->head_dim, desc->num_q_heads / desc->num_kv_heads,
-                           opts->logits_soft_cap > 0.f);
+  pp.row_waves = row_waves_of(*desc, *opts);
   pp.Hq = desc->num_q_heads;
   pp.D = desc->head_dim;
   pp.kv_elem = elem_size(desc->cache_dtype);
   // More tokens than sequences means some sequence has two or more queries,
   // so the batch has prefill tiles: only then does the prefill kernel go to
   // the side stream (decode-only batches keep one stream and no fork / join).
-  const bool side = prefill_supported(*desc) && desc->total_tokens > desc->max_num_seqs;
+  const bool side =
+      !one_stream && prefill_supported(*desc) && desc->total_tokens > desc->max_num_seqs;
   pp.co_allowed = side ? 1 : 0;
+  trace_printf("[rpa] streams %s row_waves=%d\n", side ? "caller+side" : "caller", pp.row_waves);
   // one launch: the planner, and the cache update when new tokens come along
   ScatterParams sp = {};
   if (keys)
@@ -506,35 +613,92 @@ int rpa_forward(const rpa_desc* desc, const rpa_options* opts, const void* queri
       e = launch_merge(ap, qd, s);
     }
     prof_end(s);
-    return e == hipSuccess ? RPA_OK : hip_fail(e);
+    if (e != hipSuccess) return hip_fail(e);
+  } else {
+    // The prefill tiles on the side stream, the rows and then the merge of
+    // their splits on the caller's stream; the caller's stream waits for
+    // both.  The planner's co_run flag sizes both kernels to share the CUs
+    // when the batch has enough of each kind of work.
+    std::unique_lock<std::mutex> lk(g_side_mu, std::defer_lock);
+    SideStream dry_side;
+    SideStream* ss = &dry_side;
+    if (!dry) {
+      lk.lock();
+      if ((e = side_stream(s, &ss)) != hipSuccess) return hip_fail(e);
+      if ((e = hipEventRecord(ss->fork, s)) != hipSuccess ||
+          (e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess)
+        return hip_fail(e);
+    }
+    ap.fuse_merge = 0;
+    prof_begin("prefill", ss->s);
+    e = launch_prefill(ap, qd, cd, ss->s);
+    prof_end(ss->s);
+    if (e != hipSuccess) return hip_fail(e);
+    if (!dry && (e = hipEventRecord(ss->join, ss->s)) != hipSuccess) return hip_fail(e);
+    prof_begin("decode", s);
+    e = launch_rows(ap, qd, cd, s);
+    prof_end(s);
+    if (e != hipSuccess) return hip_fail(e);
+    prof_begin("merge", s);
+    e = launch_merge(ap, qd, s);
+    prof_end(s);
+    if (e != hipSuccess) return hip_fail(e);
+    if (!dry && (e = hipStreamWaitEvent(s, ss->join, 0)) != hipSuccess) return hip_fail(e);
   }
-
-  // The prefill tiles on the side stream, the rows and then the merge of
-  // their splits on the caller's stream; the caller's stream waits for both.
-  // The planner's co_run flag sizes both kernels to share the CUs when the
-  // batch has enough of each kind of work.
-  std::lock_guard<std::mutex> lk(g_side_mu);
-  SideStream* ss = nullptr;
-  if ((e = side_stream(s, &ss)) != hipSuccess) return hip_fail(e);
-  if ((e = hipEventRecord(ss->fork, s)) != hipSuccess ||
-      (e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess)
-    return hip_fail(e);
-  ap.fuse_merge = 0;
-  prof_begin("prefill", ss->s);
-  e = launch_prefill(ap, qd, cd, ss->s);
-  prof_end(ss->s);
-  if (e != hipSuccess) return hip_fail(e);
-  if ((e = hipEventRecord(ss->join, ss->s)) != hipSuccess) return hip_fail(e);
-  prof_begin("decode", s);
-  e = launch_rows(ap, qd, cd, s);
-  prof_end(s);
-  if (e != hipSuccess) return hip_fail(e);
-  prof_begin("merge", s);
-  e = launch_merge(ap, qd, s);
-  prof_end(s);
-  if (e != hipSuccess) return hip_fail(e);
-  if ((e = hipStreamWaitEvent(s, ss->join, 0)) != hipSuccess) return hip_fail(e);
+  if (t_trace.on && !dry) {
+    // the plan the device made (a synchronous read: tracing only, and never
+    // while the stream is being captured)
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    PlanHeader h = {};
+    if (hipStreamIsCapturing(s, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone &&
+        hipMemcpyAsync(&h, ws + lay.header, sizeof h, hipMemcpyDeviceToHost, s) == hipSuccess &&
+        hipStreamSynchronize(s) == hipSuccess)
+      trace_printf("[rpa] plan num_seqs=%d rows=%d items=%d chunk_keys=%d chunks=%d "
+                   "merge_rows=%d prefill_items=%d co_run=%d\n",
+                   h.num_seqs, h.n_rows, h.n_items, h.split, h.n_chunks, h.n_merge_rows,
+                   h.n_pf_items, h.co_run);
+    else
+      trace_printf("[rpa] plan not read back (stream capturing or not readable)\n");
+  }
   return RPA_OK;
+}
+
+// Dummy device address for dry runs: aligned, never dereferenced.
+void* dry_ptr() { return reinterpret_cast<void*>(uintptr_t(1) << 12); }
+
+}  // namespace
+
+extern "C" {
+
+int rpa_forward(const rpa_desc* desc, const rpa_options* opts, const void* queries,
+                const void* keys, const void* values, void* kv_cache, const int32_t* kv_lens,
+                const int32_t* block_tables, const int32_t* query_start_loc,
+                const int32_t* distribution, const float* attention_sink, void* out,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  TraceScope ts(env_trace(), false, nullptr);
+  return forward_impl(desc, opts, queries, keys, values, kv_cache, kv_lens, block_tables,
+                      query_start_loc, distribution, attention_sink, out, workspace,
+                      workspace_bytes, static_cast<hipStream_t>(stream), false, false);
+}
+
+int rpa_trace_format(const rpa_desc* desc, const rpa_options* opts, int with_update, char* buf,
+                     size_t buf_bytes, size_t* text_bytes) {
+  std::string text;
+  int st;
+  {
+    TraceScope ts(true, true, &text);
+    void* d = dry_ptr();
+    const int32_t* m = static_cast<const int32_t*>(d);
+    st = forward_impl(desc, opts, d, with_update ? d : nullptr, with_update ? d : nullptr, d, m,
+                      m, m, m, nullptr, d, d, SIZE_MAX, nullptr, false, true);
+  }
+  if (text_bytes) *text_bytes = text.size();
+  if (buf && buf_bytes > 0) {
+    const size_t n = std::min(text.size(), buf_bytes - 1);
+    std::memcpy(buf, text.data(), n);
+    buf[n] = 0;
+  }
+  return st;
 }
 
 const char* rpa_error_string(int status) {

@@ -14,11 +14,11 @@ namespace rpa {
 // Tunables of the plan.
 // ---------------------------------------------------------------------------
 // Row-kernel work: the visible key ranges of the rows, in row order, form one
-// stream cut into at most kTargetItems chunks (one per resident wave and kv
-// head) of at least kMinSplit keys; a chunk's pieces of rows are the items, so
-// there are at most kTargetItems + rows items, fewer than 2 * kTargetItems
-// split partials (the rows cut by a chunk boundary) and fewer than
-// kTargetItems split rows.
+// stream cut into at most row_chunks_max(resident row-kernel waves, Hkv)
+// chunks (one per resident wave and kv head, never more than kTargetItems)
+// of at least kMinSplit keys; a chunk's pieces of rows are the items, so
+// there are at most chunks + rows items, at most 2 * chunks split partials
+// (the rows cut by a chunk boundary) and fewer than chunks split rows.
 constexpr int kTargetItems = 2048;    // chunks at most
 // Never cut a row's KV range finer than kMinSplit keys.  Finer pieces add
 // partials to merge without speeding up the row kernel: a long row over few
@@ -98,9 +98,10 @@ constexpr int kZeroBytes = 1024;      // zero-filled source row for masked key l
 struct Workspace {       // byte offsets into the caller's workspace
   size_t header, zeros, rows, items, chunks, merge_rows, pf_items, part_ml, part_acc, total;
   int32_t max_rows, max_items, max_parts, max_pf_items, max_merge_rows;
+  int32_t max_chunks;    // chunks of the row kernel at most (entries of the chunk table - 1)
 };
 
-Workspace workspace_layout(const rpa_desc& d);
+Workspace workspace_layout(const rpa_desc& d, const rpa_options& o);
 
 // Routing of sequences: rows of sequences with q_len >= prefill_min_q go to the
 // MFMA prefill kernel (when the dtype has one), all others to the row kernel.
@@ -214,5 +215,17 @@ hipError_t launch_reshape_and_cache(const ReshapeParams& p, rpa_dtype in_dt, rpa
 // Profiling hooks used by the launchers' caller.
 void prof_begin(const char* name, hipStream_t s);
 void prof_end(hipStream_t s);
+
+// Tracing hooks of the launchers (RPA_TRACE=1, and rpa_trace_format's dry
+// run): trace_active() says whether this thread's call is traced;
+// trace_launch() records a launch's kernel and geometry and returns true when
+// the launch must be skipped (dry run).
+bool trace_active();
+bool trace_launch(const char* kernel, unsigned grid, unsigned block, size_t lds, hipStream_t s);
+// element type names for traced kernel names (float, uint16_t = bf16, uint8_t = e4m3)
+template <typename T>
+constexpr const char* elem_name() {
+  return sizeof(T) == 4 ? "f32" : sizeof(T) == 2 ? "bf16" : "fp8";
+}
 
 }  // namespace rpa

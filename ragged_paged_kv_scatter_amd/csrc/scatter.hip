@@ -22,6 +22,7 @@ hipError_t launch_scatter(const ScatterParams& p, rpa_dtype in_dt, rpa_dtype cac
   if (p.T <= 0) return hipSuccess;
   const int tpw = std::min(8, std::max(1, (p.T + kTargetWGs - 1) / kTargetWGs));
   dim3 grid((p.T + tpw - 1) / tpw), block(kThreads);
+  if (trace_active() && trace_launch("scatter_kernel", grid.x, kThreads, 0, s)) return hipSuccess;
   if (in_dt == RPA_F32 && cache_dt == RPA_F32) {
     scatter_kernel<float, float><<<grid, block, 0, s>>>(p, tpw);
   } else if (in_dt == RPA_BF16 && cache_dt == RPA_BF16) {

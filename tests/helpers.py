@@ -62,12 +62,37 @@ def poison_unused(w, include_written=True):
 
 
 TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
+# Relative L2 error bound ||out - ref|| / ||ref|| over the checked rows.  The
+# absolute bounds above are loose for outputs whose rows average thousands of
+# N(0,1) values (sigma ~ 0.03): a dropped or misplaced page can pass them.
+# bf16 p and output rounding give about 2e-3 here.
+REL_TOL = {"f32": 1e-5, "bf16": 1e-2, "fp8": 1e-2}
 
 
 def tolerance(w):
     """Max-abs-error bound on the attention output: fp32 workloads 1e-5,
     bf16 2e-2, fp8-KV 6e-2."""
     return TOL["fp8"] if w.cache_dtype == "fp8" else TOL[w.q_dtype]
+
+
+def rel_tolerance(w):
+    return REL_TOL["fp8"] if w.cache_dtype == "fp8" else REL_TOL[w.q_dtype]
+
+
+def check_output(name, w, out, ref, rows):
+    """Assert the output rows `rows` against the oracle: max abs error within
+    the dtype's bound, relative L2 error within REL_TOL, no NaN."""
+    o = out[rows].double().cpu().numpy()
+    r = ref[rows]
+    err = float(np.abs(o - r).max()) if len(rows) else 0.0
+    nr = float(np.linalg.norm(r))
+    rel = float(np.linalg.norm(o - r)) / nr if nr > 0 else float(np.linalg.norm(o - r))
+    print(f"[{name}] rows={len(rows)} max_abs={err:.3e} rel_l2={rel:.3e} "
+          f"tol={tolerance(w):.0e}/{rel_tolerance(w):.0e}", flush=True)
+    assert not np.isnan(o).any(), f"{name}: NaN in the output"
+    assert err <= tolerance(w), f"{name}: max abs error {err:.3e}"
+    assert rel <= rel_tolerance(w), f"{name}: relative L2 error {rel:.3e}"
+    return err, rel
 
 
 def gpu_forward(w, update=True, out=None, **kw):

@@ -179,3 +179,129 @@ def test_binding_rejects_cpu_tensors():
         rpa.rpa_forward(q, None, None, torch.zeros(2, 16, 4, 64), torch.zeros(1, dtype=torch.int32),
                         torch.zeros(1, dtype=torch.int32), torch.zeros(2, dtype=torch.int32),
                         torch.zeros(3, dtype=torch.int32))
+
+
+def _cpu_batch(T=7, Hq=4, Hkv=2, D=64, seqs=3, pps=2, pages=8, ps=16):
+    import torch
+    i32 = torch.int32
+    return dict(queries=torch.zeros(T, Hq, D, dtype=torch.bfloat16),
+                keys=torch.zeros(T, Hkv, D, dtype=torch.bfloat16),
+                values=torch.zeros(T, Hkv, D, dtype=torch.bfloat16),
+                kv_cache=torch.zeros(pages, ps, 2 * Hkv, D, dtype=torch.bfloat16),
+                kv_lens=torch.zeros(seqs, dtype=i32), block_tables=torch.zeros(seqs * pps, dtype=i32),
+                query_start_loc=torch.zeros(seqs + 1, dtype=i32),
+                distribution=torch.zeros(3, dtype=i32))
+
+
+def _forward_err(**over):
+    """The binding's error for a CPU batch with one argument replaced: every
+    size and dtype check runs before the device check, so the message names
+    the mismatch rather than the device."""
+    import torch
+    import ragged_paged_kv_scatter_amd as rpa
+    b = _cpu_batch()
+    b.update(over)
+    extra = {k: b.pop(k) for k in ("attention_sink", "out") if k in b}
+    with pytest.raises((ValueError, TypeError)) as e:
+        rpa.rpa_forward(b["queries"], b["keys"], b["values"], b["kv_cache"], b["kv_lens"],
+                        b["block_tables"], b["query_start_loc"], b["distribution"],
+                        softmax_scale=0.125, **extra)
+    assert "GPU" not in str(e.value), str(e.value)
+    return str(e.value)
+
+
+def test_binding_checks_sizes_before_any_launch():
+    import torch
+    bf = torch.bfloat16
+    i32 = torch.int32
+    assert "out" in _forward_err(out=torch.zeros(7, 4, 32, dtype=bf))
+    assert "out" in _forward_err(out=torch.zeros(7, 4, 64, dtype=torch.float32))
+    assert "out" in _forward_err(out=torch.zeros(7, 4, 128, dtype=bf)[..., :64])
+    assert "keys" in _forward_err(keys=torch.zeros(6, 2, 64, dtype=bf))
+    assert "keys" in _forward_err(keys=torch.zeros(7, 1, 64, dtype=bf))
+    assert "values" in _forward_err(values=torch.zeros(7, 2, 32, dtype=bf))
+    assert "dtype" in _forward_err(values=torch.zeros(7, 2, 64, dtype=torch.float32))
+    assert "attention_sink" in _forward_err(attention_sink=torch.zeros(3))
+    assert "attention_sink" in _forward_err(attention_sink=torch.zeros(4, dtype=torch.float64))
+    assert "query_start_loc" in _forward_err(query_start_loc=torch.zeros(3, dtype=i32))
+    assert "distribution" in _forward_err(distribution=torch.zeros(2, dtype=i32))
+    assert "block_tables" in _forward_err(block_tables=torch.zeros(5, dtype=i32))
+    assert "int32" in _forward_err(kv_lens=torch.zeros(3, dtype=torch.int64))
+
+
+def test_update_binding_checks_sizes_before_any_launch():
+    import torch
+    import ragged_paged_kv_scatter_amd as rpa
+    bf = torch.bfloat16
+
+    def err(**over):
+        b = _cpu_batch()
+        b.update(over)
+        with pytest.raises((ValueError, TypeError)) as e:
+            rpa.rpa_update_kv_cache(b["keys"], b["values"], b["kv_cache"], b["kv_lens"],
+                                    b["block_tables"], b["query_start_loc"], b["distribution"])
+        assert "GPU" not in str(e.value), str(e.value)
+        return str(e.value)
+    assert "values" in err(values=torch.zeros(7, 2, 32, dtype=bf))
+    assert "kv_cache" in err(kv_cache=torch.zeros(8, 16, 2, 64, dtype=bf))
+    assert "query_start_loc" in err(query_start_loc=torch.zeros(2, dtype=torch.int32))
+    assert "distribution" in err(distribution=torch.zeros(4, dtype=torch.int32))
+
+
+def _kv(line):
+    """key=value fields of one trace line."""
+    return dict(f.split("=", 1) for f in line.split()[2:] if "=" in f)
+
+
+@pytest.mark.parametrize("kind", ["decode", "mixed", "f32"])
+def test_trace_format_lines(lib, kind):
+    """rpa_trace_format runs rpa_forward's host path dry: the forward,
+    workspace and stream lines, then one launch line per kernel in launch
+    order (decode-only: plan, rows, prefill kernel merging the splits; with
+    prefill tiles: plan, prefill on the side stream, rows, merge; f32: plan,
+    rows, merge), and the workspace size rpa_workspace_bytes reports."""
+    import ragged_paged_kv_scatter_amd as rpa
+    if kind == "f32":
+        d = good_desc()
+        order = ["prep_kernel", "row_kernel", "merge_kernel"]
+    else:
+        d = good_desc(q_dtype=_lib.RPA_BF16, kv_in_dtype=_lib.RPA_BF16,
+                      cache_dtype=_lib.RPA_BF16, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                      head_dim_padded=128, pages_per_seq=128, num_pages=20000, page_size=64)
+        if kind == "decode":
+            d.total_tokens, d.max_num_seqs = 256, 256
+            order = ["prep_kernel", "row_kernel", "prefill_kernel"]
+        else:
+            d.total_tokens, d.max_num_seqs = 2176, 132
+            order = ["prep_kernel", "prefill_kernel", "row_kernel", "merge_kernel"]
+    o = good_opts()
+    text = rpa.rpa_trace_format(d, o, with_update=True)
+    lines = text.strip().split("\n")
+    assert all(l.startswith("[rpa] ") for l in lines), text
+    assert [l.split()[1] for l in lines[:3]] == ["forward", "workspace", "streams"]
+    fw = _kv(lines[0])
+    assert int(fw["total_tokens"]) == d.total_tokens and int(fw["update"]) == 1
+    assert int(fw["num_q_heads"]) == d.num_q_heads and int(fw["head_dim"]) == d.head_dim
+    ws = _kv(lines[1])
+    assert int(ws["bytes"]) == ws_status(lib, d, o)[1]
+    offs = [int(ws[k]) for k in ("header", "zeros", "rows", "items", "chunks", "merge_rows",
+                                 "prefill_items", "part_ml", "part_acc")]
+    assert offs == sorted(offs) and all(x % 256 == 0 for x in offs)
+    assert int(ws["max_parts"]) <= 2 * int(ws["max_chunks"])
+    assert lines[2].split()[2] == ("caller+side" if kind == "mixed" else "caller")
+    launches = [l for l in lines[3:] if l.split()[1] == "launch"]
+    assert len(launches) == len(lines) - 3
+    assert [l.split()[2].split("<")[0] for l in launches] == order
+    for l in launches:
+        f = _kv(l)
+        assert int(f["grid"]) >= 1 and int(f["block"]) in (256, 1024)
+    # without the update the planner's launch carries no scatter
+    text2 = rpa.rpa_trace_format(d, o, with_update=False)
+    assert "plan+scatter" not in text2 and "update=0" in text2
+
+
+def test_trace_format_reports_host_errors(lib):
+    import ragged_paged_kv_scatter_amd as rpa
+    with pytest.raises(rpa.RpaError) as e:
+        rpa.rpa_trace_format(good_desc(page_size=24), good_opts())
+    assert e.value.code == 3

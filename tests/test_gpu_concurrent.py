@@ -1,9 +1,9 @@
 """rpa_forward from two host threads at once, each on its own stream with its
 own workspace.  Batches with prefill tiles fork the prefill kernel onto the
-library's one side stream per device; the fork / join events are shared, so
-this checks that interleaved calls still order every call's work on its own
-stream: each thread's outputs equal the serial run's bit for bit (the
-kernels are deterministic for a fixed plan)."""
+side stream of their caller's stream, so the two threads' calls use separate
+side streams; this checks that interleaved calls still order every call's
+work on its own stream: each thread's outputs equal the serial run's bit for
+bit (the kernels are deterministic for a fixed plan)."""
 import threading
 
 import numpy as np
@@ -29,9 +29,13 @@ def _call(w, meta, out, ws, cache):
                     workspace=ws, **w.options())
 
 
+@pytest.mark.parametrize("profile", [False, True])
 @pytest.mark.parametrize("names", [("mixed_bf16", "fp8_full"), ("mixed_bf16", "mixed_bf16")])
-def test_two_threads_match_serial(names):
-    print(f"\n[case] concurrent {names}", flush=True)
+def test_two_threads_match_serial(names, profile):
+    """With profiling on, each thread's launches are bracketed by its own
+    events: every launch of both threads is recorded once, with a positive
+    duration."""
+    print(f"\n[case] concurrent {names} profile={profile}", flush=True)
     jobs = [_setup(n, seed=900 + i) for i, n in enumerate(names)]
     cache0 = [w.kv_cache.clone() for w, _ in jobs]
     ref = []
@@ -65,11 +69,24 @@ def test_two_threads_match_serial(names):
             errors.append(repr(e))
 
     threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    if profile:
+        rpa.profile_enable(True)
+        rpa.profile_read()
     for t in threads:
         t.start()
     for t in threads:
         t.join(timeout=120)
     assert not errors, errors
+    if profile:
+        torch.cuda.synchronize()
+        rpa.profile_enable(False)
+        stats = rpa.profile_read()
+        print(f"[profile] {stats}", flush=True)
+        # four launches per call with prefill tiles: plan+scatter, prefill, decode, merge
+        for k in ("plan+scatter", "prefill", "decode", "merge"):
+            n, ms = stats[k]
+            assert n == 2 * reps, (k, n)
+            assert ms > 0.0, k
     for i, (w, _) in enumerate(jobs):
         n = int(w.query_start_loc[w.num_seqs])
         for out, cache in results[i]:

@@ -56,3 +56,57 @@ def test_graph_replays_match_eager(name):
         n_valid = int(w.query_start_loc[w.num_seqs])
         assert torch.equal(out_g[:n_valid].view(torch.uint8), out_e[:n_valid].view(torch.uint8)), rep
         assert torch.equal(w.kv_cache.view(torch.uint8), cache_e.view(torch.uint8)), rep
+
+
+def test_capture_beside_eager_call_on_another_stream():
+    """While one stream captures a batch with prefill tiles (whose prefill
+    kernel forks onto a side stream), an eager call with prefill tiles from a
+    second stream runs inside the capture window.  Side streams belong to
+    their caller's stream, so the eager call neither joins the capture nor
+    waits on it: its output is the plain eager result, and every replay of the
+    graph reproduces the captured call's eager result."""
+    print("\n[case] capture beside another stream", flush=True)
+    jobs = []
+    for seed in (1302, 1303):
+        w = W.make("mixed_bf16", device="cuda", small=True, seed=seed)
+        meta = {k: torch.from_numpy(np.ascontiguousarray(getattr(w, k))).cuda()
+                for k in ("kv_lens", "block_tables", "query_start_loc", "distribution")}
+        ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+        jobs.append((w, meta, ws, w.kv_cache.clone()))
+
+    def call(j, out):
+        w, meta, ws, _ = jobs[j]
+        rpa.rpa_forward(w.queries, w.keys, w.values, w.kv_cache, meta["kv_lens"],
+                        meta["block_tables"], meta["query_start_loc"], meta["distribution"],
+                        w.attention_sink, out=out, workspace=ws, **w.options())
+
+    ref = []
+    for j in range(2):
+        out = torch.full(jobs[j][0].queries.shape, float("nan"), dtype=torch.bfloat16,
+                         device="cuda")
+        call(j, out)
+        torch.cuda.synchronize()
+        ref.append((out.clone(), jobs[j][0].kv_cache.clone()))
+        jobs[j][0].kv_cache.copy_(jobs[j][3])
+    torch.cuda.synchronize()
+    out_g = torch.full_like(ref[0][0], float("nan"))
+    out_o = torch.full_like(ref[1][0], float("nan"))
+    other = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        call(0, out_g)
+        with torch.cuda.stream(other):
+            call(1, out_o)
+    other.synchronize()
+    n1 = int(jobs[1][0].query_start_loc[jobs[1][0].num_seqs])
+    assert torch.equal(out_o[:n1].view(torch.uint8), ref[1][0][:n1].view(torch.uint8))
+    assert torch.equal(jobs[1][0].kv_cache.view(torch.uint8), ref[1][1].view(torch.uint8))
+    n0 = int(jobs[0][0].query_start_loc[jobs[0][0].num_seqs])
+    for rep in range(3):
+        jobs[0][0].kv_cache.copy_(jobs[0][3])
+        out_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g[:n0].view(torch.uint8), ref[0][0][:n0].view(torch.uint8)), rep
+        assert torch.equal(jobs[0][0].kv_cache.view(torch.uint8), ref[0][1].view(torch.uint8)), rep

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from ragged_paged_kv_scatter_amd import workloads as W
-from tests.helpers import bits, gpu_forward, oracle_forward, poison_unused, tolerance
+from tests.helpers import bits, check_output, gpu_forward, oracle_forward, poison_unused
 
 pytestmark = pytest.mark.gpu
 
@@ -69,10 +69,7 @@ def test_sweep_case_matches_oracle(label):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(bits(w.kv_cache, w.cache_dtype), ref_cache)
     n_valid = int(w.query_start_loc[w.num_seqs])
-    o = out[:n_valid].double().cpu().numpy()
-    err = np.abs(o - ref[:n_valid]).max()
-    print(f"[{label}] max_abs={err:.3e} tol={tolerance(w):.0e}", flush=True)
-    assert err <= tolerance(w)
+    check_output(label, w, out, ref, np.arange(n_valid))
     assert torch.isnan(out[n_valid:].float()).all()
 
 
@@ -106,10 +103,45 @@ def test_soft_cap_paths_d64(label, cache):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(bits(w.kv_cache, w.cache_dtype), ref_cache)
     n_valid = int(w.query_start_loc[w.num_seqs])
-    o = out[:n_valid].double().cpu().numpy()
-    err = np.abs(o - ref[:n_valid]).max()
-    rel = np.linalg.norm(o - ref[:n_valid]) / np.linalg.norm(ref[:n_valid])
-    print(f"[cap {label} {cache}] max_abs={err:.3e} rel={rel:.2e} tol={tolerance(w):.0e}",
-          flush=True)
-    assert err <= tolerance(w)
-    assert rel <= 2e-2
+    check_output(f"cap {label} {cache}", w, out, ref, np.arange(n_valid))
+
+
+# Non-positive softmax scales (any finite scale is accepted): 0 gives every
+# visible key equal weight, a negative scale inverts the ranking.  Each case
+# has decode rows and causal prefill chunks, so the row kernels (VALU for
+# G = 2 / 4, MFMA for G = 8) and the prefill kernel's masked diagonal blocks
+# all see the scale.
+SCALE_CASES = {
+    # label: (q, cache, D, Hq, Hkv, page_size, cap, window, sink)
+    "f32_g2": ("f32", "f32", 64, 4, 2, 16, 0.0, 0, False),
+    "bf16_g4": ("bf16", "bf16", 128, 8, 2, 32, 0.0, 0, True),
+    "bf16_g8_cap": ("bf16", "bf16", 64, 16, 2, 16, 5.0, 40, False),
+    "fp8_g8": ("bf16", "fp8", 64, 16, 2, 32, 0.0, 0, False),
+    "fp8_g4_cap": ("bf16", "fp8", 128, 8, 2, 64, 8.0, 0, True),
+}
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.09])
+@pytest.mark.parametrize("label", list(SCALE_CASES))
+def test_nonpositive_softmax_scale(label, scale):
+    print(f"\n[case] scale {scale} {label}", flush=True)
+    qd, cd, D, hq, hkv, ps, cap, win, sink = SCALE_CASES[label]
+    seed = 7400 + list(SCALE_CASES).index(label) + (50 if scale else 0)
+    rng = np.random.default_rng(seed)
+    q_lens = [1, 1, 1, 70, 129]
+    kv_lens = [int(rng.integers(2, 200)), 900, int(rng.integers(200, 500)),
+               70 + int(rng.integers(0, 100)), 129]
+    scales = (0.05, 0.05) if cd == "fp8" else (0.0, 0.0)
+    w = W.build(label, q_lens=q_lens, kv_lens=kv_lens, distribution=(3, 2, 0),
+                num_q_heads=hq, num_kv_heads=hkv, head_dim=D, page_size=ps, q_dtype=qd,
+                kv_in_dtype=qd, cache_dtype=cd, softmax_scale=scale, seed=seed,
+                logits_soft_cap=cap, sliding_window=win, with_sink=sink, k_scale=scales[0],
+                v_scale=scales[1], device="cuda", rng=rng)
+    poison_unused(w)
+    before = bits(w.kv_cache, w.cache_dtype)
+    ref, ref_cache = oracle_forward(w, cache_bits=before)
+    out = gpu_forward(w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(w.kv_cache, w.cache_dtype), ref_cache)
+    n_valid = int(w.query_start_loc[w.num_seqs])
+    check_output(f"scale {scale} {label}", w, out, ref, np.arange(n_valid))

@@ -198,6 +198,22 @@ def test_scatter_matches_hand_derived_slots():
     np.testing.assert_array_equal(after[~touched], before[~touched])
 
 
+@pytest.mark.parametrize("window", [0, 4, 2])
+def test_visible_slots_match_hand_derived_slots(window):
+    """visible_slots decides which cache slots the GPU tests NaN-poison; it is
+    pinned by the slots derived by hand for the tiny batch (golden file)."""
+    w = _tiny_handmade()
+    rows = np.loadtxt(os.path.join(GOLDEN, "tiny_visible_slots.txt"), dtype=np.int64, ndmin=2)
+    exp = np.zeros((w.num_pages, w.page_size), dtype=bool)
+    for win, page, off in rows:
+        if win == window:
+            exp[page, off] = True
+    got = O.visible_slots(w.kv_lens, w.block_tables, w.query_start_loc, w.distribution,
+                          page_size=w.page_size, pages_per_seq=w.pages_per_seq,
+                          num_pages=w.num_pages, sliding_window=window)
+    np.testing.assert_array_equal(got, exp)
+
+
 def test_scatter_zero_fills_pad_lanes_and_roundtrips():
     w = W.make("mixed_bf16", small=True, head_dim=64, head_dim_padded=96)
     before = bits(w.kv_cache, "bf16")
@@ -414,6 +430,34 @@ def test_q_scale_multiplies_logits():
     a = O.attend_sequence(q, k, v, 4, softmax_scale=0.2, q_scale=3.0)
     ref = sdpa_causal(np.concatenate([np.zeros((4, 4, 8)), q]) * 0.6, k, v, 1.0)[4:]
     np.testing.assert_allclose(a, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_zero_scale_averages_visible_values():
+    """softmax_scale 0: every visible logit is 0, so each row is the plain mean
+    of the values it can see (closed form), with or without a soft cap."""
+    q, k, v = rand((5, 4, 8), 43), rand((12, 2, 8), 44), rand((12, 2, 8), 45)
+    ctx = 7
+    for cap in (0.0, 2.0):
+        out = O.attend_sequence(q, k, v, ctx, softmax_scale=0.0, sliding_window=6,
+                                logits_soft_cap=cap)
+        for t in range(5):
+            p = ctx + t
+            lo = max(0, p - 6 + 1)
+            for h in range(4):
+                np.testing.assert_allclose(out[t, h], v[lo:p + 1, h // 2].mean(axis=0),
+                                           rtol=1e-12, atol=1e-14)
+
+
+def test_negative_scale_equals_sdpa():
+    """A negative softmax_scale multiplies the logits like any other: torch
+    SDPA with the same negative scale and an explicit causal boolean mask
+    (no-context prefill).  torch's is_causal=True path is not used here: it
+    masks with -inf before it scales, which a negative scale turns into NaN."""
+    q, k, v = rand((9, 4, 16), 46), rand((9, 2, 16), 47), rand((9, 2, 16), 48)
+    out = O.attend_sequence(q, k, v, 0, softmax_scale=-0.35)
+    mask = np.tril(np.ones((9, 9), dtype=bool))
+    np.testing.assert_allclose(out, sdpa_causal(q, k, v, -0.35, mask=mask), rtol=1e-12,
+                               atol=1e-12)
 
 
 def test_masked_slots_may_hold_nan():

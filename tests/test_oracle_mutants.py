@@ -53,6 +53,15 @@ MUTANTS = [
     ("split_pad_lanes_kept", "        kc[b, o] = 0\n", ""),
     ("swap_direction", "out[d] = src_cache[s]", "out[s] = src_cache[d]"),
     ("copy_reads_destination", "o[d] = c[s]", "o[d] = c[d]"),
+    ("visible_window_off_by_one", "lo = max(0, ctx - sliding_window + 1) if sliding_window else 0",
+     "lo = max(0, ctx - sliding_window) if sliding_window else 0"),
+    ("visible_window_ignored", "lo = max(0, ctx - sliding_window + 1) if sliding_window else 0",
+     "lo = 0"),
+    ("visible_stops_before_last_key",
+     "page, off = slot_of(block_tables, pages_per_seq, page_size, s, np.arange(lo, kv_len))",
+     "page, off = slot_of(block_tables, pages_per_seq, page_size, s, np.arange(lo, kv_len - 1))"),
+    ("scale_sign_dropped", "scale = softmax_scale * (q_scale if q_scale else 1.0)",
+     "scale = abs(softmax_scale) * (q_scale if q_scale else 1.0)"),
 ]
 
 T = test_oracle
@@ -76,6 +85,11 @@ PINS = [
     T.test_fp8_prefill_equals_sdpa_on_library_dequant,
     T.test_q_scale_multiplies_logits,
     T.test_masked_slots_may_hold_nan,
+    lambda: T.test_visible_slots_match_hand_derived_slots(0),
+    lambda: T.test_visible_slots_match_hand_derived_slots(4),
+    lambda: T.test_visible_slots_match_hand_derived_slots(2),
+    T.test_zero_scale_averages_visible_values,
+    T.test_negative_scale_equals_sdpa,
     test_fp8_codec.test_decode_all_codes_match_torch,
     test_fp8_codec.test_closed_forms,
     test_fp8_codec.test_encode_every_bf16_pattern_matches_torch,
