@@ -262,6 +262,29 @@ int rpa_forward(const rpa_desc* desc, const rpa_options* opts, const void* queri
 int rpa_trace_format(const rpa_desc* desc, const rpa_options* opts, int with_update, char* buf,
                      size_t buf_bytes, size_t* text_bytes);
 
+/* Bytes of the library's own device scratch that rpa_forward_noalloc uses in
+ * place of a workspace (one copy per GPU, held until the process ends). */
+#define RPA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* rpa_forward without a workspace and without any allocation, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, and harnesses that forbid hipMalloc.  Same arguments and
+ * results as rpa_forward minus the workspace: the plan, work lists and split
+ * partials go to a device array of the library's, RPA_NOALLOC_SCRATCH_BYTES
+ * per GPU.  Calls whose rpa_workspace_bytes() exceeds that return
+ * RPA_ERR_WORKSPACE before touching the device.  The call allocates nothing
+ * and creates nothing: every kernel runs on `stream` (no side stream for
+ * prefill tiles, so mixed batches run their kernels one after another), no
+ * profile events are recorded, and RPA_TRACE prints no plan line.  All calls
+ * on one GPU share its scratch array, which keeps the last call's contents
+ * (every call rewrites what it reads): calls that overlap on one GPU, from
+ * different streams or threads, race and must be ordered by the caller. */
+int rpa_forward_noalloc(const rpa_desc* desc, const rpa_options* opts, const void* queries,
+                        const void* keys, const void* values, void* kv_cache,
+                        const int32_t* kv_lens, const int32_t* block_tables,
+                        const int32_t* query_start_loc, const int32_t* distribution,
+                        const float* attention_sink, void* out, void* stream);
+
 /* Bits of the device status word written by rpa_validate_metadata. */
 enum {
   RPA_META_QSL = 1,           /* qsl[0] != 0, qsl decreasing, or qsl[num_seqs] > total_tokens */

@@ -17,7 +17,8 @@ import torch
 from . import _lib
 from ._lib import RpaDesc, RpaError, RpaKernelStat, RpaOptions
 
-__all__ = ["rpa_update_kv_cache", "rpa_forward", "rpa_workspace_bytes", "rpa_slot_mapping",
+__all__ = ["rpa_update_kv_cache", "rpa_forward", "rpa_forward_noalloc", "rpa_workspace_bytes",
+           "rpa_slot_mapping",
            "rpa_reshape_and_cache", "rpa_copy_blocks", "rpa_swap_blocks",
            "rpa_validate_metadata", "rpa_trace_format", "profile_enable", "profile_read",
            "RpaError",
@@ -306,7 +307,7 @@ def _forward_args(queries, keys, values, kv_cache, kv_lens, block_tables, query_
                   distribution, attention_sink, out, workspace, softmax_scale, sliding_window,
                   logits_soft_cap, q_scale, k_scale, v_scale, chunk_prefill_size,
                   num_kv_pages_per_block, num_queries_per_block, vmem_limit_bytes):
-    """Checks and marshalling of rpa_forward's arguments:
+    """Checks and marshalling shared by rpa_forward and rpa_forward_noalloc:
     every size and dtype check runs before the device check (no launch on a
     mismatch).  Returns (device, desc, options, out)."""
     if (keys is None) != (values is None):
@@ -366,6 +367,35 @@ def rpa_forward(queries, keys, values, kv_cache, kv_lens, block_tables, query_st
             _ptr(distribution), _ptr(attention_sink), _ptr(out), _ptr(workspace),
             ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(dev)))
     return out, kv_cache
+
+
+def rpa_forward_noalloc(queries, keys, values, kv_cache, kv_lens, block_tables, query_start_loc,
+                        distribution, attention_sink=None, *, out, softmax_scale=1.0,
+                        sliding_window=None, logits_soft_cap=None, q_scale=None, k_scale=None,
+                        v_scale=None, chunk_prefill_size=None, num_kv_pages_per_block=None,
+                        num_queries_per_block=None, vmem_limit_bytes=None):
+    """rpa_forward with no workspace and no allocation: the library's own
+    device scratch (NOALLOC_SCRATCH_BYTES per GPU) holds the plan and split
+    partials, and every kernel runs on the current stream.  `out` must be
+    given (this call allocates nothing, here or in the library).  Calls that
+    overlap on one GPU share that scratch and race."""
+    if out is None:
+        raise ValueError("rpa_forward_noalloc needs a caller-allocated out")
+    dev, d, o, out = _forward_args(
+        queries, keys, values, kv_cache, kv_lens, block_tables, query_start_loc, distribution,
+        attention_sink, out, None, softmax_scale, sliding_window, logits_soft_cap, q_scale,
+        k_scale, v_scale, chunk_prefill_size, num_kv_pages_per_block, num_queries_per_block,
+        vmem_limit_bytes)
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        _lib.check(lib.rpa_forward_noalloc(
+            ctypes.byref(d), ctypes.byref(o), _ptr(queries), _ptr(keys), _ptr(values),
+            _ptr(kv_cache), _ptr(kv_lens), _ptr(block_tables), _ptr(query_start_loc),
+            _ptr(distribution), _ptr(attention_sink), _ptr(out), _stream(dev)))
+    return out, kv_cache
+
+
+NOALLOC_SCRATCH_BYTES = _lib.NOALLOC_SCRATCH_BYTES
 
 
 def rpa_trace_format(desc: RpaDesc, opts: RpaOptions, with_update: bool = True) -> str:

@@ -15,7 +15,8 @@ STATUS = {0: "RPA_OK", 1: "RPA_ERR_NULL_POINTER", 2: "RPA_ERR_INVALID_SHAPE",
 EXPORTS = ("rpa_update_kv_cache", "rpa_workspace_bytes", "rpa_forward", "rpa_error_string",
            "rpa_profile_enable", "rpa_profile_read", "rpa_slot_mapping",
            "rpa_reshape_and_cache", "rpa_copy_blocks", "rpa_swap_blocks",
-           "rpa_validate_metadata", "rpa_trace_format")
+           "rpa_validate_metadata", "rpa_trace_format", "rpa_forward_noalloc")
+NOALLOC_SCRATCH_BYTES = 32 << 20      # RPA_NOALLOC_SCRATCH_BYTES in include/rpa.h
 
 
 class RpaDesc(ctypes.Structure):
@@ -97,6 +98,9 @@ def load():
                                      ctypes.c_int, ctypes.c_char_p, ctypes.c_size_t,
                                      ctypes.POINTER(ctypes.c_size_t)]
     lib.rpa_trace_format.restype = ctypes.c_int
+    lib.rpa_forward_noalloc.argtypes = [ctypes.POINTER(RpaDesc), ctypes.POINTER(RpaOptions), P,
+                                        P, P, P, P, P, P, P, P, P, P]
+    lib.rpa_forward_noalloc.restype = ctypes.c_int
     del I32P
     _lib = lib
     return lib

@@ -98,6 +98,9 @@ std::vector<hipEvent_t> g_event_pool;
 // the pending record is per thread: concurrent callers pair their own events.
 thread_local ProfRec t_pending;
 thread_local bool t_have_pending = false;
+// Set during rpa_forward_noalloc: no profile events (creating one would
+// allocate) and no plan read-back in the trace.
+thread_local bool t_no_alloc = false;
 
 // ---- tracing (RPA_TRACE=1, or rpa_trace_format's dry run) ------------------
 // One call's trace: its sizes and options, the workspace layout, every launch
@@ -220,7 +223,7 @@ bool trace_launch(const char* kernel, unsigned grid, unsigned block, size_t lds,
 
 void prof_begin(const char* name, hipStream_t s) {
   t_have_pending = false;
-  if (t_trace.dry) return;
+  if (t_trace.dry || t_no_alloc) return;
   {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     if (!g_prof_on) return;
@@ -645,7 +648,7 @@ int forward_impl(const rpa_desc* desc, const rpa_options* opts, const void* quer
     if (e != hipSuccess) return hip_fail(e);
     if (!dry && (e = hipStreamWaitEvent(s, ss->join, 0)) != hipSuccess) return hip_fail(e);
   }
-  if (t_trace.on && !dry) {
+  if (t_trace.on && !dry && !t_no_alloc) {
     // the plan the device made (a synchronous read: tracing only, and never
     // while the stream is being captured)
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -679,6 +682,81 @@ int rpa_forward(const rpa_desc* desc, const rpa_options* opts, const void* queri
   return forward_impl(desc, opts, queries, keys, values, kv_cache, kv_lens, block_tables,
                       query_start_loc, distribution, attention_sink, out, workspace,
                       workspace_bytes, static_cast<hipStream_t>(stream), false, false);
+}
+
+}  // extern "C"
+
+namespace {
+
+// ---- allocation-free entry point ------------------------------------------
+// The workspace of rpa_forward_noalloc: a device array of the library's own,
+// one copy per GPU (its code object is loaded on each device it is used on
+// and holds the array until the process ends).  In host code `scratch` names
+// a host-side stand-in, not device memory: the device address of each GPU's
+// copy comes from hipGetSymbolAddress with that device current, and only that
+// address is ever passed to a kernel.
+constexpr size_t kNoAllocScratchBytes = RPA_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;   // device -> address of its copy of scratch
+
+// The device address of the scratch array on the device of `s` (NULL: the
+// current device), looked up once per device.
+hipError_t scratch_address(hipStream_t s, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (s) {
+    hipDevice_t d = 0;
+    if ((e = hipStreamGetDevice(s, &d)) != hipSuccess) return e;
+    dev = d;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it != g_scratch_ptr.end()) {
+    *out = it->second;
+    return hipSuccess;
+  }
+  if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (dev != cur) (void)hipSetDevice(cur);
+  if (e != hipSuccess) return e;
+  if (!ptr) return hipErrorInvalidSymbol;
+  g_scratch_ptr[dev] = ptr;
+  *out = ptr;
+  return hipSuccess;
+}
+
+struct NoAllocScope {
+  NoAllocScope() { t_no_alloc = true; }
+  ~NoAllocScope() { t_no_alloc = false; }
+};
+
+}  // namespace
+
+extern "C" {
+
+int rpa_forward_noalloc(const rpa_desc* desc, const rpa_options* opts, const void* queries,
+                        const void* keys, const void* values, void* kv_cache,
+                        const int32_t* kv_lens, const int32_t* block_tables,
+                        const int32_t* query_start_loc, const int32_t* distribution,
+                        const float* attention_sink, void* out, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if ((st = check_options(opts))) return st;
+  if (workspace_layout(*desc, *opts).total > kNoAllocScratchBytes) return RPA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(s, &ws);
+  if (e != hipSuccess) return hip_fail(e);
+  NoAllocScope na;
+  TraceScope ts(env_trace(), false, nullptr);
+  return forward_impl(desc, opts, queries, keys, values, kv_cache, kv_lens, block_tables,
+                      query_start_loc, distribution, attention_sink, out, ws,
+                      kNoAllocScratchBytes, s, true, false);
 }
 
 int rpa_trace_format(const rpa_desc* desc, const rpa_options* opts, int with_update, char* buf,

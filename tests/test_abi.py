@@ -305,3 +305,22 @@ def test_trace_format_reports_host_errors(lib):
     with pytest.raises(rpa.RpaError) as e:
         rpa.rpa_trace_format(good_desc(page_size=24), good_opts())
     assert e.value.code == 3
+
+
+def test_noalloc_checks_before_touching_the_device(lib):
+    """rpa_forward_noalloc makes rpa_forward's host checks, and refuses sizes
+    whose workspace exceeds its scratch array, before any device call."""
+    fake = ctypes.c_void_p(4096)   # never dereferenced: every call below fails host checks
+    o = good_opts()
+    args = [fake] * 4 + [fake] * 4 + [None, fake, None]
+    assert lib.rpa_forward_noalloc(None, ctypes.byref(o), *args) == 1
+    assert lib.rpa_forward_noalloc(ctypes.byref(good_desc(page_size=24)), ctypes.byref(o),
+                                   *args) == 3
+    assert lib.rpa_forward_noalloc(ctypes.byref(good_desc()),
+                                   ctypes.byref(good_opts(sliding_window=-1)), *args) == 4
+    big = good_desc(q_dtype=_lib.RPA_BF16, kv_in_dtype=_lib.RPA_BF16, cache_dtype=_lib.RPA_BF16,
+                    num_q_heads=128, num_kv_heads=8, head_dim=128, head_dim_padded=128,
+                    total_tokens=4096, max_num_seqs=4096)
+    st, need = ws_status(lib, big, o)
+    assert st == 0 and need > _lib.NOALLOC_SCRATCH_BYTES
+    assert lib.rpa_forward_noalloc(ctypes.byref(big), ctypes.byref(o), *args) == 5
