@@ -2,13 +2,25 @@
 
 A step is one rpa_forward call with the step's new keys/values: KV-cache
 update (scatter), device planning, attention and split merge, over one batch of
-synthetic input resident in HBM.  Default workload: bf16 decode (256
-sequences, kv_len ~ U{512..4096}, page_size 16, 32 q heads, 8 kv heads,
-head_dim 128).  Prints ONE JSON line.
+synthetic input resident in HBM.  The default run prints ONE JSON line whose
+`value` is the bf16 decode workload's KV GB/s (256 sequences, kv_len
+~ U{512..4096}, page_size 16, 32 q heads, 8 kv heads, head_dim 128) and whose
+nested `prefill` object is the bf16 long-prefill workload's TFLOP/s (2 x 8192
+tokens, no context, causal, 64 q heads, 8 kv heads, head_dim 128, page_size
+128): the two halves of the metric.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+Timing protocol: W untimed warm-up steps; then K timed steps, each preceded
+by a 1 GiB write that evicts L2 and the 256 MB MALL, each bracketed by
+hipEvents on the step's stream (profiling off); the whole loop sits between
+two device synchronisations.  Per-kernel times come from a second, profiled
+pass of K steps (the library's events around each launch).  Probes of the
+GPU (HBM read / copy streams, a dense bf16 MFMA burn with its shader clock,
+VALU issue rates) give measured ceilings beside the published peaks.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--op OP] [--no-cpu-baseline]
 """
 import argparse
+import contextlib
 import json
 import os
 import sys
@@ -65,58 +77,117 @@ def work_counts(w, split=False):
     return kvb, flops
 
 
-def cpu_baseline(w, budget_s=15.0, min_s=10.0, max_passes=8):
+def cpu_info():
+    """Host CPU model and logical CPU count (where the oracle baseline runs)."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    return dict(model=model, cpu_count=os.cpu_count(), affinity=affinity)
+
+
+def cpu_baseline(w, budget_s=10.0, threads=None, row_block=64, metric="kv"):
     """The oracle as it stands, timed on the host on a bounded sample of the
-    same workload: whole sequences drawn in a fixed order until ~budget_s of
-    CPU work (passes over the batch repeat while under min_s); reported in the
-    metric's unit scaled by the sample's share."""
+    same workload, with BLAS limited to `threads` (None: as configured).
+
+    The sample walks the sequences in a fixed random order; each sequence is
+    updated (its new tokens scattered into a compact copy of its pages) and
+    gathered once, then its query rows are attended to in blocks of
+    `row_block` in a fixed random order, until `budget_s` seconds of oracle
+    time.  metric "kv": KV bytes of the sequences done whole / time (decode);
+    "flops": 4 D FLOPs per visible (query, key, q head) of the rows done / time.
+    """
     import threadpoolctl
 
     from oracle import rpa_oracle as O
     from tests.helpers import bits, compact_pages
 
-    rng = np.random.default_rng(0)
-    order = rng.permutation(w.num_seqs)
-    q_bits = bits(w.queries, w.q_dtype)
-    k_bits = bits(w.keys, w.kv_in_dtype)
-    v_bits = bits(w.values, w.kv_in_dtype)
-    sink = None if w.attention_sink is None else w.attention_sink.cpu().numpy()
-    done, t_used, kvb, flops = 0, 0.0, 0, 0
-    tok_bytes = 2 * w.num_kv_heads * w.head_dim * ELEM[w.cache_dtype]
-    threads = threadpoolctl.threadpool_info()
-    nthreads = max([t.get("num_threads", 1) for t in threads] + [1])
-    schedule = [int(s) for _ in range(max_passes) for s in order]
-    for i, s in enumerate(schedule):
-        if i > 0 and i % len(order) == 0 and t_used >= min_s:
-            break                     # a whole pass done and enough CPU time
-        sub_cache, sub_bt = compact_pages(w, [s])
-        q0, ql, ctx, kvl = O.seq_bounds(w.query_start_loc, w.kv_lens, s)
+    limits = threadpoolctl.threadpool_limits(limits=threads) if threads else \
+        contextlib.nullcontext()
+    with limits:
+        info = threadpoolctl.threadpool_info()
+        used = max([t.get("num_threads", 1) for t in info] + [1])
+        rng = np.random.default_rng(0)
+        q_bits = bits(w.queries, w.q_dtype)
+        k_bits = bits(w.keys, w.kv_in_dtype)
+        v_bits = bits(w.values, w.kv_in_dtype)
+        sink = None if w.attention_sink is None else w.attention_sink.cpu().numpy()
+        tok_bytes = 2 * w.num_kv_heads * w.head_dim * ELEM[w.cache_dtype]
         pps = w.pages_per_seq
-        t0 = time.perf_counter()
-        cache = O.update_kv_cache(sub_cache, k_bits[q0:q0 + ql], v_bits[q0:q0 + ql],
-                                  np.array([kvl], np.int32), sub_bt[s * pps:(s + 1) * pps],
-                                  np.array([0, ql], np.int32), np.array([0, 0, 1], np.int32),
-                                  page_size=w.page_size, pages_per_seq=pps,
-                                  kv_in_dtype=w.kv_in_dtype, cache_dtype=w.cache_dtype,
-                                  k_scale=w.k_scale, v_scale=w.v_scale)
-        k, v = O.gather_kv(cache, 0, kvl, sub_bt[s * pps:(s + 1) * pps], page_size=w.page_size,
-                           pages_per_seq=pps, head_dim=w.head_dim, cache_dtype=w.cache_dtype,
-                           k_scale=w.k_scale, v_scale=w.v_scale)
-        q = O.to_f64(q_bits[q0:q0 + ql], w.q_dtype)
-        O.attend_sequence(q, k, v, ctx, softmax_scale=w.softmax_scale,
-                          sliding_window=w.sliding_window, logits_soft_cap=w.logits_soft_cap,
-                          q_scale=w.q_scale, sink=sink)
-        t_used += time.perf_counter() - t0
-        lo = max(0, ctx - w.sliding_window + 1) if w.sliding_window else 0
-        kvb += (kvl - lo) * tok_bytes
-        vis = ctx + np.arange(ql) + 1
-        if w.sliding_window:
-            vis = np.minimum(vis, w.sliding_window)
-        flops += 4 * w.head_dim * int(vis.sum()) * w.num_q_heads
-        done += 1
-        if t_used >= budget_s:
-            break
-    return dict(seconds=t_used, seqs=done, kv_bytes=kvb, flops=flops, threads=nthreads)
+        t_used, kvb, flops, rows_done, seqs_done = 0.0, 0, 0, 0, 0
+        for s in rng.permutation(w.num_seqs):
+            s = int(s)
+            q0, ql, ctx, kvl = O.seq_bounds(w.query_start_loc, w.kv_lens, s)
+            if ql == 0:
+                continue
+            sub_cache, sub_bt = compact_pages(w, [s])
+            t0 = time.perf_counter()
+            cache = O.update_kv_cache(sub_cache, k_bits[q0:q0 + ql], v_bits[q0:q0 + ql],
+                                      np.array([kvl], np.int32), sub_bt[s * pps:(s + 1) * pps],
+                                      np.array([0, ql], np.int32), np.array([0, 0, 1], np.int32),
+                                      page_size=w.page_size, pages_per_seq=pps,
+                                      kv_in_dtype=w.kv_in_dtype, cache_dtype=w.cache_dtype,
+                                      k_scale=w.k_scale, v_scale=w.v_scale)
+            k, v = O.gather_kv(cache, 0, kvl, sub_bt[s * pps:(s + 1) * pps],
+                               page_size=w.page_size, pages_per_seq=pps, head_dim=w.head_dim,
+                               cache_dtype=w.cache_dtype, k_scale=w.k_scale, v_scale=w.v_scale)
+            t_used += time.perf_counter() - t0
+            blocks = list(range(0, ql, row_block))
+            whole = True
+            for b in rng.permutation(len(blocks)):
+                t_lo = blocks[int(b)]
+                n = min(row_block, ql - t_lo)
+                q = O.to_f64(q_bits[q0 + t_lo:q0 + t_lo + n], w.q_dtype)
+                t0 = time.perf_counter()
+                O.attend_sequence(q, k, v, ctx + t_lo, softmax_scale=w.softmax_scale,
+                                  sliding_window=w.sliding_window,
+                                  logits_soft_cap=w.logits_soft_cap, q_scale=w.q_scale,
+                                  sink=sink)
+                t_used += time.perf_counter() - t0
+                vis = ctx + t_lo + np.arange(n) + 1
+                if w.sliding_window:
+                    vis = np.minimum(vis, w.sliding_window)
+                flops += 4 * w.head_dim * int(vis.sum()) * w.num_q_heads
+                rows_done += n
+                if t_used >= budget_s:
+                    whole = n + t_lo == ql and len(blocks) == 1
+                    break
+            if whole:
+                lo = max(0, ctx - w.sliding_window + 1) if w.sliding_window else 0
+                kvb += (kvl - lo) * tok_bytes
+                seqs_done += 1
+            if t_used >= budget_s:
+                break
+    value = (kvb / t_used / 1e9) if metric == "kv" else (flops / t_used / 1e12)
+    return dict(value=value, seconds=t_used, rows=rows_done, seqs=seqs_done, threads=used)
+
+
+def cpu_baseline_entry(w, budget_s, metric, unit):
+    """cpu_baseline at all of BLAS's threads and at one thread."""
+    host = cpu_info()
+    runs = {}
+    for label, threads in (("all", None), ("one", 1)):
+        progress(f"{w.name}: oracle baseline, {label} thread(s)")
+        runs[label] = cpu_baseline(w, budget_s, threads=threads, metric=metric)
+    a, o = runs["all"], runs["one"]
+    what = "sequences" if metric == "kv" else "query-row blocks of 64"
+    return dict(value=a["value"], unit=unit, cores=a["threads"], kind="oracle",
+                sample=f"{a['seqs']} sequences / {a['rows']} query rows of the {w.num_seqs}-"
+                       f"sequence batch ({what}, update + gather + float64 attention), "
+                       f"{a['seconds']:.1f} s of oracle time on the host",
+                one_thread=dict(value=o["value"], cores=o["threads"], seconds=o["seconds"],
+                                seqs=o["seqs"], rows=o["rows"]),
+                host_cpu=host["model"], host_cpu_count=host["cpu_count"],
+                host_cpu_affinity=host["affinity"])
 
 
 KERNEL_SOURCES = {  # kernel -> sources whose hash identifies a counter summary
@@ -135,8 +206,8 @@ def source_hash(kernel):
     return h.hexdigest()[:16]
 
 
-def traffic_file(workload):
-    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+def traffic_file(workload, kernel):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}_{kernel}.json")
 
 
 def read_counter_csv(path):
@@ -154,12 +225,15 @@ def read_counter_csv(path):
 def summarize_counters(workload, kernel, fetch_csv, write_csv, copy_bytes):
     """HBM traffic of one launch of `kernel` from a FETCH_SIZE run and a
     WRITE_SIZE run (KiB per dispatch), each scaled by what the same counter
-    reads for the calibration copy of `copy_bytes` (read once, written once)."""
+    reads for the calibration copy of `copy_bytes` (read once, written once).
+    The flush writes between timed steps are dispatches of their own and are
+    not counted."""
     sym = KERNEL_SYMBOL[kernel]
     res = {}
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         disp = read_counter_csv(path)
-        copies = [c[name] for k, c in disp.values() if "copy" in k.lower() and name in c]
+        copies = [c[name] for k, c in disp.values()
+                  if "copy" in k.lower() and "probe" not in k.lower() and name in c]
         ours = [c[name] for k, c in disp.values() if sym in k and name in c]
         if not copies or not ours:
             raise SystemExit(f"no copy or {sym} dispatch with {name} in {path}")
@@ -171,7 +245,7 @@ def summarize_counters(workload, kernel, fetch_csv, write_csv, copy_bytes):
     out = dict(workload=workload, kernel=kernel, source_hash=source_hash(kernel),
                copy_bytes=copy_bytes, fetch=res["FETCH_SIZE"], write=res["WRITE_SIZE"],
                traffic_bytes=res["FETCH_SIZE"]["bytes"] + res["WRITE_SIZE"]["bytes"])
-    with open(traffic_file(workload), "w") as fh:
+    with open(traffic_file(workload, kernel), "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
 
@@ -343,50 +417,137 @@ def bench_copy_blocks(args, w, dev, num_blocks=8192, num_pairs=2048):
     print(json.dumps(line), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode_bf16")
-    ap.add_argument("--op", default="forward",
-                    choices=["forward", "reshape_and_cache", "copy_blocks"],
-                    help="forward: the whole step (default); reshape_and_cache: the update's "
-                         "slot-mapping form into split K/V caches, at the workload's token "
-                         "count; copy_blocks: 2048 block copies in 8192-block split caches of "
-                         "the workload's block shape")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="skip timing the step replayed from a captured HIP graph")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="run one device copy of this size first (counter calibration)")
-    ap.add_argument("--summarize-counters", nargs=3, metavar=("KERNEL", "FETCH_CSV", "WRITE_CSV"),
-                    help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc runs")
-    args = ap.parse_args()
-    if args.summarize_counters:
-        k, f, wcsv = args.summarize_counters
-        summarize_counters(args.workload, k, f, wcsv, args.calib_copy_mib * 2 ** 20)
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path needs no "
-              "collective and shards by kv head or by sequence with no exchange.", file=sys.stderr)
-        sys.exit(2)
+FLUSH_BYTES = 1 << 30   # written before every timed step: evicts L2 (4 MB / XCD) and the 256 MB MALL
+
+
+class Flusher:
+    """A 1 GiB device buffer written (one fill kernel) before each timed step."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+        self.k = 0
+
+    def __call__(self):
+        self.k += 1
+        self.buf.fill_(self.k)
+
+
+def progress(msg):
+    """A progress line on stderr (the JSON line alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def timed_steps(step, steps, flush):
+    """K steps, each after a cache flush, each bracketed by events on the
+    current stream (rpa_forward joins all of its work back into it); returns
+    (per-step ms list, wall ms per step including the flushes)."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        flush()
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return [a.elapsed_time(b) for a, b in evs], wall
+
+
+def back_to_back(step, steps):
+    """K steps back to back between two synchronisations (no flush)."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def probe_ceilings(dev):
+    """Measured ceilings of this GPU from librpa_probes.so: HBM streaming read
+    and copy (GB/s), dense bf16 MFMA (TFLOP/s) with the shader clock it runs
+    at, and v_exp_f32 / v_rcp_f32 / v_fma_f32 issue rates (lane-ops/s)."""
+    import ctypes
 
     import torch
 
-    import ragged_paged_kv_scatter_amd as rpa
-    from ragged_paged_kv_scatter_amd import workloads as W
+    from ragged_paged_kv_scatter_amd import _probes
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    w = W.make(args.workload, device=dev)
-    if args.op == "reshape_and_cache":
-        bench_reshape_and_cache(args, w, dev)
-        return
-    if args.op == "copy_blocks":
-        bench_copy_blocks(args, w, dev)
-        return
+    lib = _probes.load()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    reps = 5
+
+    def time_it(launch, n=reps):
+        launch()                                   # warm-up
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(n):
+            a.record()
+            launch()
+            b.record()
+            b.synchronize()
+            best = min(best, a.elapsed_time(b))
+        return best
+
+    out = {}
+    nbytes = 2 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    half = nbytes // 2
+    dst = torch.empty(half // 4, dtype=torch.int32, device=dev)
+    # streaming rates depend on the grid: the best of 1 to 4 workgroups per CU
+    # (2 to 3 read fastest here, about 7 TB/s; 16 per CU reads about 6 TB/s)
+    read_ms, copy_ms = [], []
+    for per_cu in (1, 2, 3, 4):
+        blocks = cus * per_cu
+        sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+        read_ms.append(time_it(lambda: _probes.check(lib.rpa_probe_read(
+            ctypes.c_void_p(src.data_ptr()), nbytes // 16, ctypes.c_void_p(sink.data_ptr()),
+            blocks, stream), "read probe")))
+        copy_ms.append(time_it(lambda: _probes.check(lib.rpa_probe_copy(
+            ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), half // 16, blocks,
+            stream), "copy probe")))
+    out["hbm_read_gbs"] = nbytes / (min(read_ms) * 1e-3) / 1e9
+    out["hbm_copy_gbs"] = 2 * half / (min(copy_ms) * 1e-3) / 1e9
+    del src, dst, sink
+    # MFMA: 2 workgroups (8 waves) per CU, 4 chains per wave
+    mblocks, iters = cus * 2, 20000
+    msink = torch.empty(mblocks * 256 * 16, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(mblocks * 4 * 2, dtype=torch.int64, device=dev)
+    ms = time_it(lambda: _probes.check(lib.rpa_probe_mfma(
+        ctypes.c_void_p(msink.data_ptr()), ctypes.c_void_p(clocks.data_ptr()), iters, mblocks,
+        stream), "mfma probe"))
+    flops = mblocks * 4 * 4 * iters * 32 * 32 * 16 * 2
+    out["mfma_bf16_tflops"] = flops / (ms * 1e-3) / 1e12
+    c = clocks.view(-1, 2).double()
+    ok = c[:, 1] > 0
+    out["shader_clock_ghz_mfma"] = float((c[ok, 0] / c[ok, 1]).mean() * 0.1)
+    # VALU: 8 workgroups (32 waves) per CU, 8 chains per lane
+    vblocks, viters = cus * 8, 4096
+    vsink = torch.empty(vblocks * 256 * 8, dtype=torch.float32, device=dev)
+    for name, op in _probes.VALU_OPS.items():
+        ms = time_it(lambda: _probes.check(lib.rpa_probe_valu(
+            ctypes.c_void_p(vsink.data_ptr()), op, viters, vblocks, stream), "valu probe"))
+        out[f"{name}_per_s"] = vblocks * 256 * 8 * viters / (ms * 1e-3)
+    torch.cuda.synchronize()
+    return out
+
+
+def measure_forward(args, w, dev, flush, ceilings, with_graph=True):
+    """One workload's measurement: timed steps (flushed, events, profiling
+    off), a profiled pass for per-kernel times, the dominant kernel's
+    roofline, and optionally a HIP-graph replay timing.  Returns the dict of
+    the workload's JSON fields."""
+    import torch
+
+    import ragged_paged_kv_scatter_amd as rpa
+
     meta = {k: torch.from_numpy(np.ascontiguousarray(getattr(w, k))).to(dev)
             for k in ("kv_lens", "block_tables", "query_start_loc", "distribution")}
     out = torch.empty(w.queries.shape, dtype=w.queries.dtype, device=dev)
@@ -403,34 +564,28 @@ def main():
                         meta["block_tables"], meta["query_start_loc"], meta["distribution"],
                         w.attention_sink, out=out, workspace=workspace, **opts)
 
-    if args.calib_copy_mib:
-        src = torch.ones(args.calib_copy_mib * 2 ** 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    progress(f"{w.name}: warm-up")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    rpa.profile_enable(False)
+    progress(f"{w.name}: {args.steps} timed steps")
+    step_ms, wall_ms = timed_steps(step, args.steps, flush)
+    ms = float(np.mean(step_ms))
+    nf_ms = back_to_back(step, args.steps)
+    # per-kernel times: a second pass with the library's launch events
     rpa.profile_enable(True)
     rpa.profile_read()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    timed_steps(step, args.steps, flush)
     rpa.profile_enable(False)
     kstats = rpa.profile_read()
-    ms = (t1 - t0) * 1e3 / args.steps
 
     kvb, flops, row_kvb, pf_flops = work_counts(w, split=True)
-    decode_like = args.workload != "prefill_bf16"   # prefill reports TFLOP/s, the rest KV GB/s
-    if decode_like:
-        value, unit = kvb / (ms * 1e-3) / 1e9, "GB/s"
-    else:
-        value, unit = flops / (ms * 1e-3) / 1e12, "TFLOP/s"
+    decode_like = w.name != "prefill_bf16"   # long prefill reports TFLOP/s, the rest KV GB/s
+    work = kvb if decode_like else flops
+    scale = 1e9 if decode_like else 1e12
+    unit = "GB/s" if decode_like else "TFLOP/s"
+    value = work / (ms * 1e-3) / scale
     # dominant kernel: of the two attention kernels, the one with the larger
     # summed time among those with work in this batch (on the side-stream path
     # a kernel with no work still spans the other's run while it waits for
@@ -438,32 +593,38 @@ def main():
     # algorithmic work: the row kernel's KV bytes, the prefill tiles' FLOPs
     cands = {k: v for k, v in kstats.items()
              if (k == "decode" and row_kvb > 0) or (k == "prefill" and pf_flops > 0)}
-    dom = max(cands.items(), key=lambda kv: kv[1][1]) if cands else ("none", (1, 0.0))
-    dom_name, (dom_n, dom_ms) = dom
+    dom_name, (dom_n, dom_ms) = max(cands.items(), key=lambda kv: kv[1][1]) if cands else \
+        ("none", (1, 0.0))
     dom_avg_ms = dom_ms / max(dom_n, 1)
     if dom_name == "prefill":
         achieved = pf_flops / (dom_avg_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=achieved, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=achieved / BF16_PEAK_TFLOPS, traffic=None)
+        meas = ceilings.get("mfma_bf16_tflops") if ceilings else None
     else:
         achieved = row_kvb / (dom_avg_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=achieved / HBM_PEAK_GBS, traffic=None)
+        meas = ceilings.get("hbm_read_gbs") if ceilings else None
     roof["kernel"] = dom_name
     roof["kernel_avg_ms"] = dom_avg_ms
+    if meas:
+        roof["measured_ceiling"] = meas
+        roof["frac_of_measured"] = achieved / meas
     # HBM traffic per launch from a committed counter summary, only while the
     # kernel's sources are the ones the counters were taken on
-    tf = traffic_file(w.name)
+    tf = traffic_file(w.name, dom_name)
     if os.path.exists(tf) and dom_name in KERNEL_SOURCES:
         with open(tf) as fh:
             t = json.load(fh)
         if t.get("kernel") == dom_name and t.get("source_hash") == source_hash(dom_name):
             roof["traffic"] = t["traffic_bytes"]
-
-    line = {
-        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": w.q_dtype, "data": "synthetic",
+    res = {
+        "value": value, "unit": unit, "ms_per_step": ms,
+        "ms_per_step_min": float(np.min(step_ms)),
+        "wall_ms_per_step_with_flush": wall_ms,
+        "no_flush": {"ms_per_step": nf_ms, "value": work / (nf_ms * 1e-3) / scale},
+        "dtype": w.q_dtype,
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "total_tokens": w.total_tokens,
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "page_size": w.page_size,
@@ -472,22 +633,115 @@ def main():
         "roofline": roof,
         "kernels_ms": {k: v[1] / max(v[0], 1) for k, v in kstats.items()},
     }
-    if not args.no_graph:
+    if ceilings and pf_flops > 0 and "prefill" in kstats:
+        # VALU roof of the prefill kernel: its transcendental count at the
+        # measured issue rates (one exp2 per visible logit; with a soft cap
+        # also an exp2 and a reciprocal for tanh)
+        n_logit = pf_flops / (4 * w.head_dim)
+        t_tr = n_logit / ceilings["exp_per_s"]
+        if w.logits_soft_cap:
+            t_tr += n_logit / ceilings["exp_per_s"] + n_logit / ceilings["rcp_per_s"]
+        pk = kstats["prefill"][1] / max(kstats["prefill"][0], 1)
+        res["valu_roof"] = {"logits": n_logit,
+                            "transcendentals_per_logit": 3 if w.logits_soft_cap else 1,
+                            "t_transcendental_ms": t_tr * 1e3,
+                            "share_of_prefill_kernel": t_tr * 1e3 / pk if pk else None}
+    progress(f"{w.name}: {ms:.4f} ms per step, kernels {res['kernels_ms']}")
+    if with_graph and not args.no_graph:
         try:
-            line["graph"] = graph_timing(args, step, dev, kvb if decode_like else flops,
-                                         decode_like, unit)
+            res["graph"] = graph_timing(args, step, dev, work, decode_like, unit)
         except Exception as e:  # reported, never fatal: `value` is the eager step
-            line["graph"] = dict(error=str(e)[:200])
+            res["graph"] = dict(error=str(e)[:200])
     if not args.no_cpu_baseline:
-        cb = cpu_baseline(w, args.cpu_budget)
-        if unit == "GB/s":
-            cv = cb["kv_bytes"] / cb["seconds"] / 1e9
+        res["cpu_baseline"] = cpu_baseline_entry(w, args.cpu_budget,
+                                                 "kv" if decode_like else "flops", unit)
+    del workspace, out
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_bf16")
+    ap.add_argument("--op", default="forward",
+                    choices=["forward", "reshape_and_cache", "copy_blocks", "probes"],
+                    help="forward: the whole step (default; with the default workload the line "
+                         "also carries the long-prefill measurement); reshape_and_cache: the "
+                         "update's slot-mapping form into split K/V caches, at the workload's "
+                         "token count; copy_blocks: 2048 block copies in 8192-block split "
+                         "caches of the workload's block shape; probes: the measured ceilings "
+                         "(HBM read / copy, bf16 MFMA and shader clock, VALU issue rates)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the step replayed from a captured HIP graph")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="default workload only: skip the nested long-prefill measurement")
+    ap.add_argument("--no-probes", action="store_true", help="skip the probe ceilings")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle time per CPU-baseline run (two runs per workload)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one device copy of this size first (counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("KERNEL", "FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>_<kernel>.json from two rocprofv3 "
+                         "--pmc runs")
+    args = ap.parse_args()
+    if args.summarize_counters:
+        k, f, wcsv = args.summarize_counters
+        summarize_counters(args.workload, k, f, wcsv, args.calib_copy_mib * 2 ** 20)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path needs no "
+              "collective and shards by kv head or by sequence with no exchange.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from ragged_paged_kv_scatter_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.op == "probes":
+        line = {"metric": "GPU ceilings (probes)", "n_gpus": 1, "data": "synthetic",
+                "ceilings": probe_ceilings(dev)}
+        print(json.dumps(line), flush=True)
+        return
+    if args.calib_copy_mib:
+        src = torch.ones(args.calib_copy_mib * 2 ** 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.op in ("reshape_and_cache", "copy_blocks"):
+        w = W.make(args.workload, device=dev)
+        if args.op == "reshape_and_cache":
+            bench_reshape_and_cache(args, w, dev)
         else:
-            cv = cb["flops"] / cb["seconds"] / 1e12
-        line["cpu_baseline"] = dict(
-            value=cv, unit=unit, cores=cb["threads"], kind="oracle",
-            sample=f"{cb['seqs']} sequence evaluations over a {w.num_seqs}-sequence batch "
-                   f"(update + gather + float64 attention), {cb['seconds']:.1f} s on the host")
+            bench_copy_blocks(args, w, dev)
+        return
+    if not args.no_probes:
+        progress("probes")
+    ceilings = None if args.no_probes else probe_ceilings(dev)
+    flush = Flusher(dev)
+    w = W.make(args.workload, device=dev)
+    res = measure_forward(args, w, dev, flush, ceilings)
+    del w
+    torch.cuda.empty_cache()
+    line = {"metric": METRIC, "value": res.pop("value"), "unit": res.pop("unit"), "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": res.pop("ms_per_step"),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": res.pop("dtype"), "data": "synthetic"}
+    line.update(res)
+    if args.workload == "decode_bf16" and not args.no_prefill:
+        wp = W.make("prefill_bf16", device=dev)
+        pf = measure_forward(args, wp, dev, flush, ceilings)
+        pf["metric"] = "ragged paged attn: long prefill TFLOP/s, % of bf16 MFMA roofline"
+        line["prefill"] = pf
+        del wp
+    if ceilings:
+        line["ceilings"] = ceilings
     print(json.dumps(line), flush=True)
 
 

@@ -1,4 +1,5 @@
-"""Builds librpa.so (the HIP kernels and the C ABI) in-tree with hipcc for gfx950.
+"""Builds librpa.so (the HIP kernels and the C ABI) and librpa_probes.so (the
+measurement probes) in-tree with hipcc for gfx950.
 
 Run as ``python -m ragged_paged_kv_scatter_amd.build``, or call :func:`build`.
 Every call recompiles."""
@@ -14,6 +15,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "librpa.so")
 SOURCES = ["rpa_api.cpp", "scatter.hip", "plan.hip", "decode.hip", "prefill.hip", "slots.hip",
            "validate.hip"]
+# measurement probes (include/rpa_probes.h), a library of their own
+PROBES_LIB = os.path.join(HERE, "librpa_probes.so")
+PROBES_SOURCES = ["probes.hip"]
 ARCH = os.environ.get("RPA_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
@@ -32,13 +36,9 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    obj_dir = os.path.join(HERE, "_build")
-    os.makedirs(obj_dir, exist_ok=True)
-    t0 = time.time()
-    procs = []
-    objs = []
-    for src in SOURCES:
+def _compile(sources, obj_dir, jobs, verbose):
+    procs, objs = [], []
+    for src in sources:
         obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
@@ -58,14 +58,28 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     if failed:
         msg = "\n".join(f"--- {s} ---\n{o}" for s, o in failed)
         raise RuntimeError(f"hipcc failed:\n{msg}")
-    tmp = LIB + ".tmp"
+    return objs
+
+
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    """Compile and link librpa.so and librpa_probes.so; returns librpa.so's path."""
+    obj_dir = os.path.join(HERE, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    t0 = time.time()
+    objs = _compile(SOURCES + PROBES_SOURCES, obj_dir, jobs, verbose)
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBES_LIB)
     if verbose:
-        print(f"built {LIB} in {time.time() - t0:.1f}s")
+        print(f"built {LIB} and {PROBES_LIB} in {time.time() - t0:.1f}s")
     return LIB
 
 

@@ -12,8 +12,8 @@ from ragged_paged_kv_scatter_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def declared_functions():
-    src = open(os.path.join(ROOT, "include", "rpa.h")).read()
+def declared_functions(header="rpa.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(rpa_\w+)\s*\(", src, flags=re.M)))
 
@@ -30,6 +30,20 @@ def test_exports_every_declared_symbol(lib):
                           "rpa_copy_blocks", "rpa_swap_blocks"}
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_probe_library_exports_every_declared_symbol():
+    from ragged_paged_kv_scatter_amd import _probes
+    lib = _probes.load()
+    names = declared_functions("rpa_probes.h")
+    assert set(names) == set(_probes.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_every_header_is_covered():
+    """Each header under include/ belongs to one of the two libraries."""
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["rpa.h", "rpa_probes.h"]
 
 
 def good_desc(**kw):

@@ -67,3 +67,18 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_cpu_baseline_fields():
+    """The oracle baseline on a tiny batch: positive rate, sequences done
+    whole, and the one-thread run really limited to one BLAS thread."""
+    w = W.make("tiny_fp32")
+    a = bench.cpu_baseline(w, budget_s=0.01)
+    assert a["value"] > 0 and a["seqs"] >= 1 and a["rows"] >= 1
+    one = bench.cpu_baseline(w, budget_s=0.01, threads=1)
+    assert one["threads"] == 1
+    p = W.make("prefill_bf16", small=True)
+    f = bench.cpu_baseline(p, budget_s=0.01, metric="flops")
+    assert f["value"] > 0 and f["rows"] >= 1
+    info = bench.cpu_info()
+    assert info["cpu_count"] >= 1
