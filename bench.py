@@ -34,6 +34,9 @@ sys.path.insert(0, ROOT)
 METRIC = "ragged paged attn: decode KV GB/s + prefill TFLOP/s, % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+# Long-prefill workloads report TFLOP/s; the others KV GB/s.
+PREFILL_WORKLOADS = ("prefill_bf16", "prefill_fp8q")
 ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
 
 
@@ -51,7 +54,7 @@ def work_counts(w, split=False):
     pairs = 0
     row_kvb = 0
     pf_pairs = 0
-    has_prefill_kernel = w.q_dtype == "bf16"
+    has_prefill_kernel = w.q_dtype in ("bf16", "fp8")
     tok_bytes = 2 * w.num_kv_heads * w.head_dim * ELEM[w.cache_dtype]
     W = w.sliding_window
     for s in range(w.num_seqs):
@@ -550,7 +553,7 @@ def measure_forward(args, w, dev, flush, ceilings, with_graph=True):
 
     meta = {k: torch.from_numpy(np.ascontiguousarray(getattr(w, k))).to(dev)
             for k in ("kv_lens", "block_tables", "query_start_loc", "distribution")}
-    out = torch.empty(w.queries.shape, dtype=w.queries.dtype, device=dev)
+    out = torch.empty(w.queries.shape, dtype=rpa.out_dtype_for(w.queries.dtype), device=dev)
     opts = w.options()
     ws_bytes = rpa.rpa_workspace_bytes(
         rpa._desc(w.queries, rpa._dtype(w.keys), w.kv_cache, meta["kv_lens"],
@@ -581,7 +584,7 @@ def measure_forward(args, w, dev, flush, ceilings, with_graph=True):
     kstats = rpa.profile_read()
 
     kvb, flops, row_kvb, pf_flops = work_counts(w, split=True)
-    decode_like = w.name != "prefill_bf16"   # long prefill reports TFLOP/s, the rest KV GB/s
+    decode_like = w.name not in PREFILL_WORKLOADS
     work = kvb if decode_like else flops
     scale = 1e9 if decode_like else 1e12
     unit = "GB/s" if decode_like else "TFLOP/s"
@@ -598,8 +601,14 @@ def measure_forward(args, w, dev, flush, ceilings, with_graph=True):
     dom_avg_ms = dom_ms / max(dom_n, 1)
     if dom_name == "prefill":
         achieved = pf_flops / (dom_avg_ms * 1e-3) / 1e12
-        roof = dict(bound="mfma", achieved=achieved, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=achieved / BF16_PEAK_TFLOPS, traffic=None)
+        # e4m3 queries: q.k on fp8 MFMA, p.v on bf16 MFMA (half the FLOPs each)
+        peak = FP8_PEAK_TFLOPS if w.q_dtype == "fp8" else BF16_PEAK_TFLOPS
+        roof = dict(bound="mfma", achieved=achieved, peak=peak, unit="TFLOP/s",
+                    frac=achieved / peak, traffic=None)
+        if w.q_dtype == "fp8":
+            mixed = 1.0 / (0.5 / FP8_PEAK_TFLOPS + 0.5 / BF16_PEAK_TFLOPS)
+            roof["peak_fp8_qk_bf16_pv"] = mixed
+            roof["frac_of_fp8_qk_bf16_pv"] = achieved / mixed
         meas = ceilings.get("mfma_bf16_tflops") if ceilings else None
     else:
         achieved = row_kvb / (dom_avg_ms * 1e-3) / 1e9

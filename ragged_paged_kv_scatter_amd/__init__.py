@@ -18,6 +18,7 @@ from . import _lib
 from ._lib import RpaDesc, RpaError, RpaKernelStat, RpaOptions
 
 __all__ = ["rpa_update_kv_cache", "rpa_forward", "rpa_forward_noalloc", "rpa_workspace_bytes",
+           "out_dtype_for",
            "rpa_slot_mapping",
            "rpa_reshape_and_cache", "rpa_copy_blocks", "rpa_swap_blocks",
            "rpa_validate_metadata", "rpa_trace_format", "profile_enable", "profile_read",
@@ -29,6 +30,12 @@ META_QSL, META_LENS, META_BLOCK_TABLE, META_SLOTS, META_DISTRIBUTION = 1, 2, 4, 
 
 _DT = {torch.float32: _lib.RPA_F32, torch.bfloat16: _lib.RPA_BF16, torch.uint8: _lib.RPA_FP8_E4M3,
        torch.float8_e4m3fn: _lib.RPA_FP8_E4M3}
+
+
+def out_dtype_for(q_dtype: torch.dtype) -> torch.dtype:
+    """dtype of the attention output: the queries' own, or bf16 for e4m3
+    queries (uint8 codes or float8_e4m3fn)."""
+    return torch.bfloat16 if q_dtype in (torch.uint8, torch.float8_e4m3fn) else q_dtype
 
 
 def _dtype(t: torch.Tensor) -> int:
@@ -325,9 +332,10 @@ def _forward_args(queries, keys, values, kv_cache, kv_lens, block_tables, query_
         if attention_sink.numel() != Hq:
             raise ValueError(f"attention_sink must hold num_q_heads = {Hq} values, got "
                              f"{attention_sink.numel()}")
+    out_dtype = out_dtype_for(queries.dtype)
     if out is not None:
-        if tuple(out.shape) != tuple(queries.shape) or out.dtype != queries.dtype:
-            raise ValueError(f"out must be {tuple(queries.shape)} {queries.dtype}, got "
+        if tuple(out.shape) != tuple(queries.shape) or out.dtype != out_dtype:
+            raise ValueError(f"out must be {tuple(queries.shape)} {out_dtype}, got "
                              f"{tuple(out.shape)} {out.dtype}")
         if not out.is_contiguous():
             raise ValueError("out must be contiguous")
@@ -339,7 +347,7 @@ def _forward_args(queries, keys, values, kv_cache, kv_lens, block_tables, query_
                  chunk_prefill_size, num_kv_pages_per_block, num_queries_per_block,
                  vmem_limit_bytes)
     if out is None:
-        out = torch.empty(queries.shape, dtype=queries.dtype, device=dev)
+        out = torch.empty(queries.shape, dtype=out_dtype, device=dev)
     return dev, d, o, out
 
 

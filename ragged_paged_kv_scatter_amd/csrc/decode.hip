@@ -24,6 +24,7 @@
 #include <math.h>
 
 #include <cstdio>
+#include <type_traits>
 #include <utility>
 
 #include "device_common.h"
@@ -260,8 +261,11 @@ __device__ __forceinline__ void store_slice(QT* o, long long base, const float* 
   }
 }
 
+// QT: query type (float, uint16_t = bf16, or uint8_t = e4m3 codes, widened
+// exactly to bf16 on load); the output is QT, or bf16 for e4m3 queries.
 template <typename QT, typename CT, int D, int G, int EPL, int NR, bool CAP>
 __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
+  using OT = std::conditional_t<sizeof(QT) == 1, uint16_t, QT>;
   constexpr bool F32 = sizeof(CT) == 4;
   constexpr int LPT = D / EPL;          // lanes per token
   constexpr int TPR = 64 / LPT;         // tokens per load row
@@ -317,7 +321,8 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
     r.g = g;
     return r;
   };
-  // q of the G heads of item `it`, this lane's d-slice: fp32 values or raw bf16 pairs
+  // q of the G heads of item `it`, this lane's d-slice: fp32 values or bf16
+  // pairs (e4m3 codes widened exactly, four per loaded word)
   auto load_q = [&](const Item& it, uint32_t (*qw)[NP]) __attribute__((always_inline)) {
     const QT* qp =
         static_cast<const QT*>(p.q) + ((long long)it.token * p.Hq + it.g * G) * D + dl * EPL;
@@ -326,6 +331,14 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
       if constexpr (sizeof(QT) == 4) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) qw[i][e] = __float_as_uint(qp[i * D + e]);
+      } else if constexpr (sizeof(QT) == 1) {
+        static_assert(EPL % 4 == 0, "whole words of e4m3 codes");
+#pragma unroll
+        for (int e = 0; e < EPL / 4; ++e) {
+          const uint32_t w = reinterpret_cast<const uint32_t*>(qp + i * D)[e];
+          qw[i][2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.f, false));
+          qw[i][2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.f, true));
+        }
       } else {
 #pragma unroll
         for (int e = 0; e < NP; ++e) qw[i][e] = reinterpret_cast<const uint32_t*>(qp + i * D)[e];
@@ -564,7 +577,7 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
     if (slot == 0) {
       const float vs = p.v_scale;
       if (cur.part < 0) {
-        QT* op = static_cast<QT*>(p.out);
+        OT* op = static_cast<OT*>(p.out);
 #pragma unroll
         for (int i = 0; i < G; ++i) {
           const int h = cur.g * G + i;
@@ -577,7 +590,7 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
           }
           const float scale = f * vs / ll;
           const long long base = ((long long)cur.token * p.Hq + h) * D + dl * EPL;
-          store_slice<QT, EPL>(op, base, acc[i], scale);
+          store_slice<OT, EPL>(op, base, acc[i], scale);
         }
       } else if (cur.part < p.lay.max_parts) {
 #pragma unroll
@@ -657,7 +670,7 @@ __device__ __forceinline__ u32x4 nt_load16(const char* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-template <typename CT, int D, int G, bool CAP>
+template <typename CT, int D, int G, bool CAP, bool QF8>
 __global__ __launch_bounds__(64 * kWavesPerWG) void mfma_row_kernel(AttnParams p) {
   using Cfg = MfCfg<CT, D>;
   constexpr int ESZ = Cfg::ESZ, E = Cfg::E, LPTK = Cfg::LPTK, TPI = Cfg::TPI, NLI = Cfg::NLI,
@@ -708,15 +721,26 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void mfma_row_kernel(AttnParams p
     const int part = __builtin_amdgcn_readfirstlane(dsc.part);
     const int* bt = p.block_tables + (long long)seq * p.pps;
 
-    // q^T operands: lane (head c16, d slots of g4) per MFMA
+    // q^T operands: lane (head c16, d slots of g4) per MFMA (e4m3 queries
+    // widened exactly to bf16)
     bf16x8 qb[NMQ];
     {
-      const uint16_t* qp = static_cast<const uint16_t*>(p.q) +
-                           ((long long)token * p.Hq + g * G + (c16 < G ? c16 : 0)) * D;
+      const long long qrow = (long long)token * p.Hq + g * G + (c16 < G ? c16 : 0);
 #pragma unroll
       for (int m = 0; m < NMQ; ++m) {
         const int d0 = 32 * m + 8 * g4;
-        const uint4 v = (c16 < G) ? *reinterpret_cast<const uint4*>(qp + d0) : make_uint4(0, 0, 0, 0);
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if constexpr (QF8) {
+          if (c16 < G) {
+            const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(p.q) + qrow * D + d0);
+            v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, 1.f, false));
+            v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, 1.f, true));
+            v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, 1.f, false));
+            v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, 1.f, true));
+          }
+        } else {
+          if (c16 < G) v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + qrow * D + d0);
+        }
         qb[m] = __builtin_bit_cast(bf16x8, v);
       }
     }
@@ -928,10 +952,11 @@ struct RowCfg {
   // load rows per step: 4, or 2 where G x EPL = 64 accumulators leave no room
   // for two 4-row buffers at two waves per SIMD
   static constexpr int NR = (G * EPL >= 64 && (sizeof(CT) >= 2 || G >= 16)) ? 2 : 4;
-  // bf16 queries with G >= 8 q heads per kv head: the MFMA kernel
-  static constexpr bool MF = sizeof(QT) == 2 && G >= 8;
+  // bf16 or e4m3 queries with G >= 8 q heads per kv head: the MFMA kernel
+  static constexpr bool MF = sizeof(QT) <= 2 && G >= 8;
+  static constexpr bool QF8 = sizeof(QT) == 1;
   static const void* kernel() {
-    if constexpr (MF) return reinterpret_cast<const void*>(&mfma_row_kernel<CT, D, (MF ? G : 8), CAP>);
+    if constexpr (MF) return reinterpret_cast<const void*>(&mfma_row_kernel<CT, D, (MF ? G : 8), CAP, QF8>);
     else return reinterpret_cast<const void*>(&row_kernel<QT, CT, D, G, EPL, NR, CAP>);
   }
   static int resident() {
@@ -950,14 +975,14 @@ hipError_t launch_rows_t(const AttnParams& p, hipStream_t s) {
   if (trace_active()) {
     char nm[96];
     if constexpr (Cfg::MF)
-      std::snprintf(nm, sizeof nm, "mfma_row_kernel<%s,D%d,G%d%s>", elem_name<CT>(), D, G,
-                    CAP ? ",cap" : "");
+      std::snprintf(nm, sizeof nm, "mfma_row_kernel<%s%s,D%d,G%d%s>", elem_name<CT>(),
+                    Cfg::QF8 ? ",q_fp8" : "", D, G, CAP ? ",cap" : "");
     else
       std::snprintf(nm, sizeof nm, "row_kernel<%s,%s,D%d,G%d,EPL%d,NR%d%s>", elem_name<QT>(),
                     elem_name<CT>(), D, G, Cfg::EPL, Cfg::NR, CAP ? ",cap" : "");
     if (trace_launch(nm, grid.x, 64 * kWavesPerWG, 0, s)) return hipSuccess;
   }
-  if constexpr (Cfg::MF) mfma_row_kernel<CT, D, (Cfg::MF ? G : 8), CAP><<<grid, 64 * kWavesPerWG, 0, s>>>(p);
+  if constexpr (Cfg::MF) mfma_row_kernel<CT, D, (Cfg::MF ? G : 8), CAP, Cfg::QF8><<<grid, 64 * kWavesPerWG, 0, s>>>(p);
   else row_kernel<QT, CT, D, G, Cfg::EPL, Cfg::NR, CAP><<<grid, 64 * kWavesPerWG, 0, s>>>(p);
   return hipGetLastError();
 }
@@ -1005,6 +1030,7 @@ int row_waves_c(rpa_dtype q_dt, rpa_dtype cache_dt, int D, int G) {
   if (q_dt == RPA_F32 && cache_dt == RPA_F32) return row_waves_d<float, float, CAP>(D, G);
   if (q_dt == RPA_BF16 && cache_dt == RPA_BF16) return row_waves_d<uint16_t, uint16_t, CAP>(D, G);
   if (q_dt == RPA_BF16 && cache_dt == RPA_FP8_E4M3) return row_waves_d<uint16_t, uint8_t, CAP>(D, G);
+  if (q_dt == RPA_FP8_E4M3 && cache_dt == RPA_FP8_E4M3) return row_waves_d<uint8_t, uint8_t, CAP>(D, G);
   return 0;
 }
 
@@ -1013,6 +1039,7 @@ hipError_t launch_rows_c(const AttnParams& p, rpa_dtype q_dt, rpa_dtype cache_dt
   if (q_dt == RPA_F32 && cache_dt == RPA_F32) return launch_rows_d<float, float, CAP>(p, s);
   if (q_dt == RPA_BF16 && cache_dt == RPA_BF16) return launch_rows_d<uint16_t, uint16_t, CAP>(p, s);
   if (q_dt == RPA_BF16 && cache_dt == RPA_FP8_E4M3) return launch_rows_d<uint16_t, uint8_t, CAP>(p, s);
+  if (q_dt == RPA_FP8_E4M3 && cache_dt == RPA_FP8_E4M3) return launch_rows_d<uint8_t, uint8_t, CAP>(p, s);
   return hipErrorInvalidValue;
 }
 

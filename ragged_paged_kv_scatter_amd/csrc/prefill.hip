@@ -44,6 +44,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef i16x4 __attribute__((address_space(3))) * lds_i16x4_ptr;
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int BK = 64;          // keys per block
 constexpr int NT = 256;         // threads per workgroup
@@ -90,6 +91,17 @@ __device__ __forceinline__ int swz_f(int r) {
 template <int D>
 __device__ __forceinline__ int swz_chunk(int r, int c) {
   return c ^ swz_f<D>(r);
+}
+
+// Chunk swizzle of an e4m3 K row (D bytes) in LDS, for the fp8-query kernel:
+// the 16 rows a ds_read_b128 serves at one logical chunk land on 16 distinct
+// 16-byte bank groups.  D = 128: two rows per 256 B, f(r) = (r >> 1) & 7
+// spreads the 8 rows of one parity; D = 64: four rows per 256 B,
+// f(r) = (r >> 2) & 3 spreads the 4 rows of one residue.
+template <int D>
+__device__ __forceinline__ int swz8_f(int r) {
+  if constexpr (D == 128) return (r >> 1) & 7;
+  else return (r >> 2) & 3;
 }
 
 __device__ __forceinline__ void wait_vmem_all() {
@@ -141,22 +153,39 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 //   - multiplies P(b) V(b) while the row max of S(b+1) is formed.
 // So MFMA and VALU work of one wave overlap, and every buffer is rewritten
 // only after the barrier that follows its last reader.
-template <typename CT, int D, bool CAP>
+//
+// QF8 (e4m3 queries over an e4m3 cache): S^T = K Q^T runs on
+// v_mfma_f32_32x32x64_f8f6f4 with the cached K codes copied global -> LDS as
+// they are (no widening), and Q codes in registers; its 32x32 accumulator
+// has the layout of the bf16 one, so the softmax and the bf16 O^T += V^T P^T
+// steps are shared.  The fp8 A and B operands hold, in lane group kg of
+// k-step s, the 32 bytes d = 64 s + 32 kg .. + 31 of their K row / Q row in
+// the same order, so every product pairs the same d.
+template <typename CT, int D, bool CAP, bool QF8>
 __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
-  constexpr bool DIRECT = sizeof(CT) == 2;         // bf16 cache: global -> LDS directly
-  constexpr int RB = D * 2;                        // LDS row bytes (bf16)
-  constexpr int CPR = RB / 16;                     // 16-byte LDS chunks per row
-  constexpr int BLKB = BK * RB;                    // bytes of one K (or V) block
-  constexpr int KS = D / 16;                       // MFMA k-steps of q.k
+  static_assert(!QF8 || sizeof(CT) == 1, "e4m3 queries go with an e4m3 cache");
+  constexpr bool VDIRECT = sizeof(CT) == 2;        // bf16 cache: V global -> LDS directly
+  constexpr bool KDIRECT = VDIRECT || QF8;         // K rows copied as stored
+  constexpr int RB = D * 2;                        // LDS row bytes of V (and of bf16 K)
+  constexpr int RBK = QF8 ? D : RB;                // LDS row bytes of K
+  constexpr int CPR = RB / 16;                     // 16-byte LDS chunks per V row
+  constexpr int CPRK = RBK / 16;                   // 16-byte LDS chunks per K row
+  constexpr int BLKB = BK * RB;                    // bytes of one V block
+  constexpr int BLKBK = BK * RBK;                  // bytes of one K block
+  constexpr int KS = D / 16;                       // bf16 MFMA k-steps of q.k
+  constexpr int KS8 = D / 64;                      // fp8 MFMA k-steps of q.k
   constexpr int DT = D / 32;                       // 32-row d tiles of O^T
-  constexpr int IPW = BLKB / 1024 / 4;             // direct loads per wave per K (or V) block
-  constexpr int RPI = 1024 / RB;                   // rows per direct load instruction
+  constexpr int IPW = BLKB / 1024 / 4;             // direct loads per wave per V block
+  constexpr int RPI = 1024 / RB;                   // V rows per direct load instruction
+  constexpr int IPWK = BLKBK / 1024 / 4;           // direct loads per wave per K block
+  constexpr int RPIK = 1024 / RBK;                 // K rows per direct load instruction
   constexpr int ESZ = CacheElem<CT>::size;
   constexpr int GCPR = D * ESZ / 16;               // 16-byte chunks of a cached head row
   constexpr int PER = BK * GCPR / NT;              // staged chunks per thread (e4m3 path)
-  static_assert(!DIRECT || IPW * RPI == 16, "a wave loads 16 consecutive rows");
-  static_assert(DIRECT || (PER >= 1 && BK * GCPR % NT == 0), "staged split");
-  __shared__ __attribute__((aligned(1024))) char s_k[2 * BLKB];
+  static_assert(!VDIRECT || IPW * RPI == 16, "a wave loads 16 consecutive rows");
+  static_assert(!KDIRECT || IPWK * RPIK == 16, "a wave loads 16 consecutive rows");
+  static_assert(VDIRECT || (PER >= 1 && BK * GCPR % NT == 0), "staged split");
+  __shared__ __attribute__((aligned(1024))) char s_k[2 * BLKBK];
   __shared__ __attribute__((aligned(1024))) char s_v[2 * BLKB];
   __shared__ int s_pt[kPT];
 
@@ -180,7 +209,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
   // visible logit is exactly 0, as the definition gives.
   const bool q_zero = p.qk_scale == 0.f;
   const uint32_t q_and = q_zero ? 0u : 0xFFFFFFFFu;
-  const uint32_t q_xor = p.qk_scale < 0.f ? 0x80008000u : 0u;
+  const uint32_t q_xor = p.qk_scale < 0.f ? (QF8 ? 0x80808080u : 0x80008000u) : 0u;
   const float scale_pos = q_zero ? 1.f : fabsf(p.qk_scale);
   const float c_scale = CAP ? scale_pos : scale_pos * kLog2e;
   const float c_eff = CAP ? 1.f : c_scale;       // stored logits -> log2 units
@@ -201,11 +230,18 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
   // lane / CPR, physical chunk lane % CPR, which holds logical chunk
   // (lane % CPR) ^ swz(row); the rows' source offsets from the wave's first
   // token row are fixed per lane.
-  uint32_t dma_off[DIRECT ? IPW : 1];
+  // Physical chunk -> logical chunk of LDS row r: K (e4m3 rows when QF8) or V.
+  auto kchunk = [](int r, int c) { return QF8 ? (c ^ swz8_f<D>(r)) : swz_chunk<D>(r, c); };
+  uint32_t dma_off[VDIRECT ? IPW : 1], dma_off_k[KDIRECT ? IPWK : 1];
 #pragma unroll
-  for (int j = 0; j < (DIRECT ? IPW : 1); ++j) {
+  for (int j = 0; j < (VDIRECT ? IPW : 1); ++j) {
     const int r = RPI * j + lane / CPR;
     dma_off[j] = r * row_bytes + (swz_chunk<D>(r, lane % CPR) << 4);
+  }
+#pragma unroll
+  for (int j = 0; j < (KDIRECT ? IPWK : 1); ++j) {
+    const int r = RPIK * j + lane / CPRK;
+    dma_off_k[j] = r * row_bytes + (kchunk(r, lane % CPRK) << 4);
   }
 
   // LDS byte offsets inside a K / V buffer (fixed per lane):
@@ -225,6 +261,21 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
     const char* a = kb + ((k_off ^ (uint32_t)(ks << 5)) + hf * 32 * RB);
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(a));
   };
+  // fp8 A operand (QF8): key row hf * 32 + col, bytes 64 ks + 32 kg .. + 31,
+  // i.e. logical chunks 4 ks + 2 kg and 4 ks + 2 kg + 1 of the e4m3 row
+  const int f8 = swz8_f<D>(col);
+  auto ld_k8 = [&](const char* kb, int ks, int hf) -> i32x8 {
+    const char* row = kb + (hf * 32 + col) * RBK;
+    const int c0 = 4 * ks + 2 * kg;
+    const uint4 lo = *reinterpret_cast<const uint4*>(row + ((c0 ^ f8) << 4));
+    const uint4 hi = *reinterpret_cast<const uint4*>(row + (((c0 + 1) ^ f8) << 4));
+    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
+                 (int)hi.w};
+  };
+  // S^T accumulation step of one 32-key half: bf16 (16 d) or e4m3 (64 d)
+  auto mfma_qk8 = [](i32x8 a, i32x8 b, f32x16 c) -> f32x16 {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  };
   auto ld_vt = [&](const char* vb, int ks, int dt) -> bf16x8 {
     const char* a1 = vb + ((v_off1 ^ (uint32_t)(dt << 6)) + ks * 16 * RB);
     const char* a2 = vb + ((v_off2 ^ (uint32_t)(dt << 6)) + (ks * 16 + 8) * RB);
@@ -238,9 +289,9 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
   // kv head); they touch rows this kernel does not write.  Rows with many
   // parts are merged by the whole workgroup in s_k, before any copy into it.
   static_assert(NT == 256, "the workgroup merge takes 4 waves");
-  static_assert(merge_wg_floats<D, 16>() * 4 <= 2 * BLKB, "merge scratch fits in s_k");
+  static_assert(merge_wg_floats<D, 16>() * 4 <= 2 * BLKB, "merge scratch fits in s_v");
   if (p.fuse_merge)
-    merge_all_g<uint16_t, D>(p, (long long)hdr->n_merge_rows * Hkv, reinterpret_cast<float*>(s_k));
+    merge_all_g<uint16_t, D>(p, (long long)hdr->n_merge_rows * Hkv, reinterpret_cast<float*>(s_v));
 
   // Persistent grid: in round k block b takes unit k * grid + b, except that
   // odd rounds reverse the order of the groups of 8 blocks (when the grid is
@@ -316,36 +367,41 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
     };
 
     // ---- loads of one K or V block (vofs = 0: K rows, v_bytes: V rows) ----
-    auto issue_direct = [&](int blk, char* buf, uint32_t vofs) __attribute__((always_inline)) {
+    // ISK: K rows (RBK bytes in LDS), else V rows (RB bytes)
+    auto issue_direct = [&](auto isk, int blk, char* buf, uint32_t vofs)
+                            __attribute__((always_inline)) {
+      constexpr bool K_ = decltype(isk)::value;
+      constexpr int IPW_ = K_ ? IPWK : IPW, RPI_ = K_ ? RPIK : RPI, CPR_ = K_ ? CPRK : CPR;
       const int t0 = blk * BK + 16 * wave;           // the wave's first token
-      const uint32_t lds0 = lds_addr(buf + wave * IPW * 1024);
+      const uint32_t lds0 = lds_addr(buf + wave * IPW_ * 1024);
       if (t0 >= kv_lo && t0 + 16 <= kv_hi) {
         // 16 tokens of one page (page_size >= 16): uniform base + lane offsets
         const int page = __builtin_amdgcn_readfirstlane(s_pt[(t0 >> sh) - pt_base]);
         const uint32_t crow = ((uint32_t)page << sh) | (uint32_t)(t0 & pmask);
         const char* base = uniform_ptr(kv_head + vofs + (uint64_t)crow * row_bytes);
 #pragma unroll
-        for (int j = 0; j < IPW; ++j) dma16_s(base, dma_off[j], lds0 + j * 1024);
+        for (int j = 0; j < IPW_; ++j) dma16_s(base, K_ ? dma_off_k[j] : dma_off[j], lds0 + j * 1024);
       } else {
         // range edge: rows outside [kv_lo, kv_hi) come from the zero row
 #pragma unroll
-        for (int j = 0; j < IPW; ++j) {
-          const int r = RPI * j + lane / CPR;
+        for (int j = 0; j < IPW_; ++j) {
+          const int r = RPI_ * j + lane / CPR_;
           const int tok = t0 + r;
-          const char* src = zero_row + (swz_chunk<D>(r, lane % CPR) << 4);
+          const int lc = K_ ? kchunk(r, lane % CPR_) : swz_chunk<D>(r, lane % CPR_);
+          const char* src = zero_row + (lc << 4);
           if (tok >= kv_lo && tok < kv_hi) {
             const int page = s_pt[(tok >> sh) - pt_base];
             const uint32_t crow = ((uint32_t)page << sh) | (uint32_t)(tok & pmask);
-            src = kv_head + vofs + (uint64_t)crow * row_bytes + (swz_chunk<D>(r, lane % CPR) << 4);
+            src = kv_head + vofs + (uint64_t)crow * row_bytes + (lc << 4);
           }
           dma16(src, lds0 + j * 1024);
         }
       }
     };
-    uint4 kr[DIRECT ? 1 : PER], vr[DIRECT ? 1 : PER];
+    uint4 kr[KDIRECT ? 1 : PER], vr[VDIRECT ? 1 : PER];
     auto fetch_staged = [&](int blk, uint4* regs, uint32_t vofs) {   // e4m3: global -> registers
 #pragma unroll
-      for (int i = 0; i < (DIRECT ? 0 : PER); ++i) {
+      for (int i = 0; i < (VDIRECT ? 0 : PER); ++i) {
         const int cidx = tid + NT * i;
         const int tok = blk * BK + cidx / GCPR, cc = cidx % GCPR;
         uint4 a = make_uint4(0, 0, 0, 0);
@@ -359,7 +415,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
     };
     auto stage_staged = [&](const uint4* regs, char* buf) {  // e4m3 -> bf16 into swizzled rows
 #pragma unroll
-      for (int i = 0; i < (DIRECT ? 0 : PER); ++i) {
+      for (int i = 0; i < (VDIRECT ? 0 : PER); ++i) {
         const int cidx = tid + NT * i;
         const int row = cidx / GCPR, cc = cidx % GCPR;
         const uint32_t w[4] = {regs[i].x, regs[i].y, regs[i].z, regs[i].w};
@@ -376,19 +432,19 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
             make_uint4(o[4], o[5], o[6], o[7]);
       }
     };
-    auto kbuf = [&](int blk) -> char* { return s_k + (blk & 1) * BLKB; };
+    auto kbuf = [&](int blk) -> char* { return s_k + (blk & 1) * BLKBK; };
     auto vbuf = [&](int blk) -> char* { return s_v + (blk & 1) * BLKB; };
     auto load_k = [&](int blk) {
-      if constexpr (DIRECT) issue_direct(blk, kbuf(blk), 0);
+      if constexpr (KDIRECT) issue_direct(std::true_type{}, blk, kbuf(blk), 0);
       else fetch_staged(blk, kr, 0);
     };
     auto load_v = [&](int blk) {
-      if constexpr (DIRECT) issue_direct(blk, vbuf(blk), v_bytes);
+      if constexpr (VDIRECT) issue_direct(std::false_type{}, blk, vbuf(blk), v_bytes);
       else fetch_staged(blk, vr, v_bytes);
     };
     // step b, first part: K(b+1), V(b) are in LDS; start K(b+2), V(b+1)
     auto begin_step = [&](int blk) __attribute__((always_inline)) {
-      if constexpr (DIRECT) wait_vmem_all();      // this wave's loads have landed
+      if constexpr (KDIRECT) wait_vmem_all();     // this wave's loads have landed
       __syncthreads();                            // everyone's; last readers are done
       if (blk + 1 < blk_end) load_v(blk + 1);     // its pages are in the table already
       if (blk + 2 < blk_end) {
@@ -398,23 +454,41 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
     };
     // step b, last part (e4m3): widen the fetched rows into their buffers
     auto end_step = [&](int blk) __attribute__((always_inline)) {
-      if constexpr (!DIRECT) {
+      if constexpr (!VDIRECT) {
         if (blk + 1 < blk_end) stage_staged(vr, vbuf(blk + 1));
+      }
+      if constexpr (!KDIRECT) {
         if (blk + 2 < blk_end) stage_staged(kr, kbuf(blk + 2));
       }
     };
 
     // ---- per-lane state: Q^T operand, O^T accumulators, softmax state ----
-    bf16x8 qreg[KS];   // 8 bf16 of row row_q, d = 16 ks + 8 kg .. +7
+    bf16x8 qreg[QF8 ? 1 : KS];   // 8 bf16 of row row_q, d = 16 ks + 8 kg .. +7
+    i32x8 qreg8[QF8 ? KS8 : 1];   // QF8: 32 e4m3 of row row_q, d = 64 ks + 32 kg .. +31
     {
-      const uint16_t* qp = static_cast<const uint16_t*>(p.q) +
-                           ((long long)(q0 + (row_ok ? row_q : it.q_begin)) * Hq + h) * D + 8 * kg;
+      const long long qrow = (long long)(q0 + (row_ok ? row_q : it.q_begin)) * Hq + h;
+      auto fix = [&](uint4 v) {
+        return make_uint4((v.x & q_and) ^ q_xor, (v.y & q_and) ^ q_xor, (v.z & q_and) ^ q_xor,
+                          (v.w & q_and) ^ q_xor);
+      };
+      if constexpr (QF8) {
+        const uint8_t* qp = static_cast<const uint8_t*>(p.q) + qrow * D + 32 * kg;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qp + 16 * ks) : make_uint4(0, 0, 0, 0);
-        v = make_uint4((v.x & q_and) ^ q_xor, (v.y & q_and) ^ q_xor, (v.z & q_and) ^ q_xor,
-                       (v.w & q_and) ^ q_xor);
-        qreg[ks] = __builtin_bit_cast(bf16x8, v);
+        for (int ks = 0; ks < KS8; ++ks) {
+          const uint4 z = make_uint4(0, 0, 0, 0);
+          const uint4 lo = fix(row_ok ? *reinterpret_cast<const uint4*>(qp + 64 * ks) : z);
+          const uint4 hi = fix(row_ok ? *reinterpret_cast<const uint4*>(qp + 64 * ks + 16) : z);
+          qreg8[ks] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y,
+                            (int)hi.z, (int)hi.w};
+        }
+      } else {
+        const uint16_t* qp = static_cast<const uint16_t*>(p.q) + qrow * D + 8 * kg;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 v = fix(row_ok ? *reinterpret_cast<const uint4*>(qp + 16 * ks)
+                                     : make_uint4(0, 0, 0, 0));
+          qreg[ks] = __builtin_bit_cast(bf16x8, v);
+        }
       }
     }
     f32x16 oacc[DT];
@@ -496,32 +570,55 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
       // ahead of their MFMAs.  The q.k MFMAs carry the p of logits 0..15, the
       // first half of the p.v MFMAs (k-steps 0, 1, which use only those) the
       // p of logits 16..31, the second half the mask / cap / max of S(b+1).
-      constexpr int XA = 8 / KS;          // logits exponentiated per q.k MFMA
+      constexpr int XA = QF8 ? 8 / KS8 : 8 / KS;   // logits exponentiated per q.k MFMA
       constexpr int XB = 8 / DT;          // per p.v MFMA of k-steps 0, 1
       constexpr int MB = 16 / DT;         // logits max-reduced per p.v MFMA of k-steps 2, 3
       // The two waves of a SIMD take turns: a wave in its compute part
       // outranks one at its barrier / copy part, which keeps the MFMA pipe
       // fed while the other wave catches up (measured 2-3% on long prefill).
       __builtin_amdgcn_s_setprio(1);
-      bf16x8 a0 = ld_k(kn, 0, 0), a1 = ld_k(kn, 0, 1);
+      if constexpr (QF8) {
+        i32x8 a0 = ld_k8(kn, 0, 0), a1 = ld_k8(kn, 0, 1);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 n0 = a0, n1 = a1;
-        if (ks + 1 < KS) {
-          n0 = ld_k(kn, ks + 1, 0);
-          n1 = ld_k(kn, ks + 1, 1);
+        for (int ks = 0; ks < KS8; ++ks) {
+          i32x8 n0 = a0, n1 = a1;
+          if (ks + 1 < KS8) {
+            n0 = ld_k8(kn, ks + 1, 0);
+            n1 = ld_k8(kn, ks + 1, 1);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          s2[0] = mfma_qk8(a0, qreg8[ks], s2[0]);
+#pragma unroll
+          for (int x = 0; x < XA; ++x) expo((2 * ks) * XA + x);
+          __builtin_amdgcn_sched_barrier(0);
+          s2[1] = mfma_qk8(a1, qreg8[ks], s2[1]);
+#pragma unroll
+          for (int x = 0; x < XA; ++x) expo((2 * ks + 1) * XA + x);
+          __builtin_amdgcn_sched_barrier(0);
+          a0 = n0;
+          a1 = n1;
         }
-        __builtin_amdgcn_sched_barrier(0);
-        s2[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], s2[0], 0, 0, 0);
+      } else {
+        bf16x8 a0 = ld_k(kn, 0, 0), a1 = ld_k(kn, 0, 1);
 #pragma unroll
-        for (int x = 0; x < XA; ++x) expo((2 * ks) * XA + x);
-        __builtin_amdgcn_sched_barrier(0);
-        s2[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s2[1], 0, 0, 0);
+        for (int ks = 0; ks < KS; ++ks) {
+          bf16x8 n0 = a0, n1 = a1;
+          if (ks + 1 < KS) {
+            n0 = ld_k(kn, ks + 1, 0);
+            n1 = ld_k(kn, ks + 1, 1);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          s2[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], s2[0], 0, 0, 0);
 #pragma unroll
-        for (int x = 0; x < XA; ++x) expo((2 * ks + 1) * XA + x);
-        __builtin_amdgcn_sched_barrier(0);
-        a0 = n0;
-        a1 = n1;
+          for (int x = 0; x < XA; ++x) expo((2 * ks) * XA + x);
+          __builtin_amdgcn_sched_barrier(0);
+          s2[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s2[1], 0, 0, 0);
+#pragma unroll
+          for (int x = 0; x < XA; ++x) expo((2 * ks + 1) * XA + x);
+          __builtin_amdgcn_sched_barrier(0);
+          a0 = n0;
+          a1 = n1;
+        }
       }
 
       // (2) O^T += V^T(b) P^T(b)
@@ -581,8 +678,8 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
     const int b0 = blk_first;
     ensure_pages(b0);
     load_k(b0);
-    if constexpr (!DIRECT) stage_staged(kr, kbuf(b0));
-    if constexpr (DIRECT) wait_vmem_all();
+    if constexpr (!KDIRECT) stage_staged(kr, kbuf(b0));
+    if constexpr (KDIRECT) wait_vmem_all();
     __syncthreads();
     load_v(b0);
     if (b0 + 1 < blk_end) {
@@ -595,10 +692,18 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sa[hf][i] = 0.f;
+      if constexpr (QF8) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        sa[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_k(kb, ks, 0), qreg[ks], sa[0], 0, 0, 0);
-        sa[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_k(kb, ks, 1), qreg[ks], sa[1], 0, 0, 0);
+        for (int ks = 0; ks < KS8; ++ks) {
+          sa[0] = mfma_qk8(ld_k8(kb, ks, 0), qreg8[ks], sa[0]);
+          sa[1] = mfma_qk8(ld_k8(kb, ks, 1), qreg8[ks], sa[1]);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          sa[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_k(kb, ks, 0), qreg[ks], sa[0], 0, 0, 0);
+          sa[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_k(kb, ks, 1), qreg[ks], sa[1], 0, 0, 0);
+        }
       }
       float t = kRedInit;
 #pragma unroll
@@ -609,8 +714,8 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
       }
       mx = to_mx(red(t, __shfl_xor(t, 32)));
     }
-    if constexpr (!DIRECT) {
-      stage_staged(vr, vbuf(b0));
+    if constexpr (!VDIRECT) stage_staged(vr, vbuf(b0));
+    if constexpr (!KDIRECT) {
       if (b0 + 1 < blk_end) stage_staged(kr, kbuf(b0 + 1));
     }
 
@@ -668,46 +773,50 @@ long long resident_grid(const void* kernel) {
   return (long long)(per_cu * cus) / 8 * 8;
 }
 
-template <typename CT, int D, bool CAP>
+template <typename CT, int D, bool CAP, bool QF8>
 hipError_t launch_d(const AttnParams& p, long long blocks, hipStream_t s) {
   // persistent grid: the resident workgroups, rounded down to a multiple of 8
   // so that block b and its later units b + grid sit on the same XCD
   static const long long resident =
-      resident_grid(reinterpret_cast<const void*>(&prefill_kernel<CT, D, CAP>));
+      resident_grid(reinterpret_cast<const void*>(&prefill_kernel<CT, D, CAP, QF8>));
   if (blocks > resident) blocks = resident;
   if (trace_active()) {
     char nm[80];
-    std::snprintf(nm, sizeof nm, "prefill_kernel<%s,D%d%s>(%s)", elem_name<CT>(), D,
-                  CAP ? ",cap" : "", p.fuse_merge ? "merge+tiles" : "tiles");
+    std::snprintf(nm, sizeof nm, "prefill_kernel<%s%s,D%d%s>(%s)", elem_name<CT>(),
+                  QF8 ? ",q_fp8" : "", D, CAP ? ",cap" : "",
+                  p.fuse_merge ? "merge+tiles" : "tiles");
     if (trace_launch(nm, (unsigned)blocks, NT, 0, s)) return hipSuccess;
   }
-  prefill_kernel<CT, D, CAP><<<dim3((unsigned)blocks), NT, 0, s>>>(p);
+  prefill_kernel<CT, D, CAP, QF8><<<dim3((unsigned)blocks), NT, 0, s>>>(p);
   return hipGetLastError();
 }
 
-template <typename CT>
+template <typename CT, bool QF8>
 hipError_t launch_t(const AttnParams& p, hipStream_t s) {
   const long long merge_blocks =
       p.fuse_merge ? ((long long)p.lay.max_merge_rows * p.Hkv + 3) / 4 : 0;
   const long long blocks = std::max((long long)p.lay.max_pf_items * p.Hq, merge_blocks);
   if (blocks <= 0) return hipSuccess;
   const bool cap = p.cap > 0.f;
-  if (p.D == 64) return cap ? launch_d<CT, 64, true>(p, blocks, s) : launch_d<CT, 64, false>(p, blocks, s);
-  return cap ? launch_d<CT, 128, true>(p, blocks, s) : launch_d<CT, 128, false>(p, blocks, s);
+  if (p.D == 64)
+    return cap ? launch_d<CT, 64, true, QF8>(p, blocks, s) : launch_d<CT, 64, false, QF8>(p, blocks, s);
+  return cap ? launch_d<CT, 128, true, QF8>(p, blocks, s) : launch_d<CT, 128, false, QF8>(p, blocks, s);
 }
 
 }  // namespace
 
 bool prefill_supported(const rpa_desc& d) {
-  return d.q_dtype == RPA_BF16 && (d.cache_dtype == RPA_BF16 || d.cache_dtype == RPA_FP8_E4M3) &&
-         (d.head_dim == 64 || d.head_dim == 128);
+  const bool bf16_q =
+      d.q_dtype == RPA_BF16 && (d.cache_dtype == RPA_BF16 || d.cache_dtype == RPA_FP8_E4M3);
+  const bool fp8_q = d.q_dtype == RPA_FP8_E4M3 && d.cache_dtype == RPA_FP8_E4M3;
+  return (bf16_q || fp8_q) && (d.head_dim == 64 || d.head_dim == 128);
 }
 
 hipError_t launch_prefill(const AttnParams& p, rpa_dtype q_dt, rpa_dtype cache_dt,
                           hipStream_t s) {
-  if (q_dt != RPA_BF16) return hipErrorInvalidValue;
-  if (cache_dt == RPA_BF16) return launch_t<uint16_t>(p, s);
-  if (cache_dt == RPA_FP8_E4M3) return launch_t<uint8_t>(p, s);
+  if (q_dt == RPA_BF16 && cache_dt == RPA_BF16) return launch_t<uint16_t, false>(p, s);
+  if (q_dt == RPA_BF16 && cache_dt == RPA_FP8_E4M3) return launch_t<uint8_t, false>(p, s);
+  if (q_dt == RPA_FP8_E4M3 && cache_dt == RPA_FP8_E4M3) return launch_t<uint8_t, true>(p, s);
   return hipErrorInvalidValue;
 }
 

@@ -30,7 +30,9 @@ bool supported_triple(int q, int in, int c) {
   return (q == RPA_F32 && in == RPA_F32 && c == RPA_F32) ||
          (q == RPA_BF16 && in == RPA_BF16 && c == RPA_BF16) ||
          (q == RPA_BF16 && in == RPA_BF16 && c == RPA_FP8_E4M3) ||
-         (q == RPA_BF16 && in == RPA_FP8_E4M3 && c == RPA_FP8_E4M3);
+         (q == RPA_BF16 && in == RPA_FP8_E4M3 && c == RPA_FP8_E4M3) ||
+         (q == RPA_FP8_E4M3 && in == RPA_BF16 && c == RPA_FP8_E4M3) ||
+         (q == RPA_FP8_E4M3 && in == RPA_FP8_E4M3 && c == RPA_FP8_E4M3);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -152,7 +152,8 @@ def build(name: str, *, q_lens, kv_lens, distribution, num_q_heads, num_kv_heads
     gen = torch.Generator(device=device)
     gen.manual_seed(int(seed))
     two_h = 2 * num_kv_heads
-    queries = _rand_tensor((T, num_q_heads, head_dim), q_dtype, gen, device)
+    queries = _rand_tensor((T, num_q_heads, head_dim), q_dtype, gen, device,
+                           scale=q_scale if q_scale else 1.0)
     cache_scale = k_scale if k_scale else 1.0
     kv_cache = _rand_tensor((num_pages, page_size, two_h, hdp), cache_dtype, gen, device,
                             scale=cache_scale)
@@ -264,6 +265,40 @@ def long_decode_bf16(device="cpu", seed=1005, kv_len=131072, **kw) -> Workload:
                  rng=rng, **args)
 
 
+def prefill_fp8q(device="cpu", seed=1006, n_seqs=2, seq_len=8192, q_scale=0.05, **kw) -> Workload:
+    """The long-prefill shape with 8-bit queries and cache ("w8a8"): 2 seqs
+    with q_len = kv_len = 8192, causal; Hq 64, Hkv 8, D 128, page_size 128;
+    queries are e4m3 codes of N(0,1) / q_scale, the cache e4m3 with k_scale =
+    v_scale = 0.05 (new K/V bf16 N(0,1), quantised by the update)."""
+    rng = np.random.default_rng(seed)
+    args = dict(num_q_heads=64, num_kv_heads=8, head_dim=128, page_size=128)
+    args.update(kw)
+    return build("prefill_fp8q", q_lens=[seq_len] * n_seqs, kv_lens=[seq_len] * n_seqs,
+                 distribution=(0, n_seqs, 0), q_dtype="fp8", kv_in_dtype="bf16",
+                 cache_dtype="fp8", softmax_scale=1 / math.sqrt(args["head_dim"]),
+                 q_scale=q_scale, k_scale=0.05, v_scale=0.05, seed=seed, device=device,
+                 rng=rng, **args)
+
+
+def mixed_fp8q(device="cpu", seed=1007, n_decode=64, decode_kv=(512, 4096), n_prefill=4,
+               chunk=384, ctx_max=2048, q_scale=0.05, **kw) -> Workload:
+    """8-bit queries and cache over a mixed batch: 64 decode rows (kv ~
+    U{512..4096}) + 4 prefill chunks of 384 tokens with context ~ U{0..2048};
+    Hq 64, Hkv 8, D 128, page_size 32; window 1024, soft cap 30, sinks."""
+    rng = np.random.default_rng(seed)
+    dkv = rng.integers(decode_kv[0], decode_kv[1], size=n_decode, endpoint=True)
+    ctx = rng.integers(0, ctx_max, size=n_prefill, endpoint=True)
+    q = np.concatenate([np.ones(n_decode, np.int64), np.full(n_prefill, chunk, np.int64)])
+    kv = np.concatenate([dkv, ctx + chunk])
+    args = dict(num_q_heads=64, num_kv_heads=8, head_dim=128, page_size=32)
+    args.update(kw)
+    return build("mixed_fp8q", q_lens=q, kv_lens=kv, distribution=(n_decode, n_prefill, 0),
+                 q_dtype="fp8", kv_in_dtype="bf16", cache_dtype="fp8",
+                 softmax_scale=1 / math.sqrt(args["head_dim"]), q_scale=q_scale, k_scale=0.05,
+                 v_scale=0.05, sliding_window=1024, logits_soft_cap=30.0, with_sink=True,
+                 seed=seed, device=device, rng=rng, **args)
+
+
 RECIPES = {
     "tiny_fp32": tiny_fp32,
     "decode_bf16": decode_bf16,
@@ -271,6 +306,8 @@ RECIPES = {
     "prefill_bf16": prefill_bf16,
     "fp8_full": fp8_full,
     "long_decode_bf16": long_decode_bf16,
+    "prefill_fp8q": prefill_fp8q,
+    "mixed_fp8q": mixed_fp8q,
 }
 
 # Scaled-down variants with the same structure, for CPU oracle runs and fast
@@ -283,6 +320,8 @@ SMALL = {
     "fp8_full": dict(n_decode=8, decode_kv=(40, 600), n_prefill=2, chunk=100, ctx=150,
                      sliding_window=128),
     "long_decode_bf16": dict(kv_len=5000),
+    "prefill_fp8q": dict(n_seqs=2, seq_len=300),
+    "mixed_fp8q": dict(n_decode=8, decode_kv=(40, 600), n_prefill=3, chunk=77, ctx_max=200),
 }
 
 

@@ -103,7 +103,8 @@ def gpu_forward(w, update=True, out=None, **kw):
     meta = {k: torch.from_numpy(np.ascontiguousarray(getattr(w, k))).to(dev)
             for k in ("kv_lens", "block_tables", "query_start_loc", "distribution")}
     if out is None:
-        out = torch.full(w.queries.shape, float("nan"), dtype=w.queries.dtype, device=dev)
+        out = torch.full(w.queries.shape, float("nan"), dtype=rpa.out_dtype_for(w.queries.dtype),
+                         device=dev)
     opts = w.options()
     opts.update(kw)
     rpa.rpa_forward(w.queries, w.keys if update else None, w.values if update else None,

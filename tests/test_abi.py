@@ -73,6 +73,9 @@ def ws_status(lib, d, o):
 def test_workspace_query_ok(lib):
     st, n = ws_status(lib, good_desc(), good_opts())
     assert st == 0 and n > 0
+    for kv_in in (_lib.RPA_BF16, _lib.RPA_FP8_E4M3):   # e4m3 queries over an e4m3 cache
+        d = good_desc(q_dtype=_lib.RPA_FP8_E4M3, kv_in_dtype=kv_in, cache_dtype=_lib.RPA_FP8_E4M3)
+        assert ws_status(lib, d, good_opts(q_scale=0.05))[0] == 0
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -87,6 +90,8 @@ def test_workspace_query_ok(lib):
     (dict(q_dtype=7), 3),
     (dict(cache_dtype=_lib.RPA_FP8_E4M3, kv_in_dtype=_lib.RPA_F32), 3),
     (dict(max_num_seqs=20000), 3),
+    (dict(q_dtype=_lib.RPA_FP8_E4M3, kv_in_dtype=_lib.RPA_BF16, cache_dtype=_lib.RPA_BF16), 3),
+    (dict(q_dtype=_lib.RPA_FP8_E4M3), 3),     # e4m3 queries need an e4m3 cache
 ])
 def test_invalid_desc_codes(lib, kw, code):
     st, _ = ws_status(lib, good_desc(**kw), good_opts())

@@ -17,7 +17,8 @@ from tests.helpers import (bits, check_output, compact_pages, gpu_forward, oracl
                            poison_unused)
 
 pytestmark = pytest.mark.gpu
-NAMES = ["tiny_fp32", "decode_bf16", "mixed_bf16", "prefill_bf16", "fp8_full", "long_decode_bf16"]
+NAMES = ["tiny_fp32", "decode_bf16", "mixed_bf16", "prefill_bf16", "fp8_full", "long_decode_bf16",
+         "prefill_fp8q", "mixed_fp8q"]
 
 
 @pytest.mark.parametrize("name", NAMES)
@@ -163,7 +164,8 @@ def _with(w, **kw):
 
 
 FULL = [("tiny_fp32", 3, 8), ("decode_bf16", 24, 1), ("mixed_bf16", 12, 24),
-        ("prefill_bf16", 2, 24), ("fp8_full", 12, 24), ("long_decode_bf16", 1, 1)]
+        ("prefill_bf16", 2, 24), ("fp8_full", 12, 24), ("long_decode_bf16", 1, 1),
+        ("prefill_fp8q", 2, 24), ("mixed_fp8q", 12, 24)]
 
 
 @pytest.mark.parametrize("name,n_seqs,rows_per_seq", FULL)
@@ -177,7 +179,7 @@ def test_full_size_sampled(name, n_seqs, rows_per_seq):
     assert not torch.isnan(out[:n_valid].float()).any()
 
 
-@pytest.mark.parametrize("name", ["decode_bf16", "mixed_bf16", "fp8_full"])
+@pytest.mark.parametrize("name", ["decode_bf16", "mixed_bf16", "fp8_full", "mixed_fp8q"])
 def test_page_permutation_bitwise_invariance(name):
     """Same logical cache on two different page permutations: identical
     output bits (the plan depends only on lengths, not on page ids)."""
@@ -200,7 +202,7 @@ def test_page_permutation_bitwise_invariance(name):
                                            else torch.int32))
 
 
-@pytest.mark.parametrize("name", ["mixed_bf16", "fp8_full"])
+@pytest.mark.parametrize("name", ["mixed_bf16", "fp8_full", "mixed_fp8q"])
 def test_value_sensitivity_one_hot_positions(name):
     """V rows set to one-hot codes of their absolute position: a misread page
     moves weight to the wrong position and shows as an O(1) error."""

@@ -36,6 +36,17 @@ CASES = {
                                    (0, 0.05, 0.05)),
     "fp8in_g2_d128_ps32": ("bf16", "fp8", "fp8", 128, 128, 4, 2, 32, 0, 0.0, False,
                            (0, 0.1, 0.2)),
+    # e4m3 queries (q_scale dequantises them) over an e4m3 cache
+    "fp8q_g8_d128_ps32_all": ("fp8", "bf16", "fp8", 128, 128, 16, 2, 32, 100, 20.0, True,
+                              (0.05, 0.05, 0.05)),
+    "fp8q_g2_d64_ps16": ("fp8", "fp8", "fp8", 64, 64, 4, 2, 16, 0, 0.0, False,
+                         (0.05, 0.1, 0.2)),
+    "fp8q_g16_d64_ps64_padded_cap": ("fp8", "bf16", "fp8", 64, 80, 16, 1, 64, 0, 5.0, False,
+                                     (0.03, 0.05, 0.05)),
+    "fp8q_g4_d128_ps128_window_sink": ("fp8", "bf16", "fp8", 128, 128, 8, 2, 128, 37, 0.0, True,
+                                       (0.02, 0.04, 0.06)),
+    "fp8q_g1_d128_ps16": ("fp8", "fp8", "fp8", 128, 128, 2, 2, 16, 0, 0.0, False,
+                          (0.05, 0.05, 0.05)),
 }
 
 
@@ -118,6 +129,8 @@ SCALE_CASES = {
     "bf16_g8_cap": ("bf16", "bf16", 64, 16, 2, 16, 5.0, 40, False),
     "fp8_g8": ("bf16", "fp8", 64, 16, 2, 32, 0.0, 0, False),
     "fp8_g4_cap": ("bf16", "fp8", 128, 8, 2, 64, 8.0, 0, True),
+    "fp8q_g8": ("fp8", "fp8", 128, 16, 2, 32, 0.0, 0, False),
+    "fp8q_g2_cap": ("fp8", "fp8", 64, 4, 2, 16, 4.0, 0, True),
 }
 
 

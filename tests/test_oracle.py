@@ -425,6 +425,23 @@ def test_fp8_prefill_equals_sdpa_on_library_dequant():
     np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
 
 
+def test_fp8_queries_equal_sdpa_on_torch_dequant():
+    """e4m3 query codes with q_scale ("w8a8" queries) over an e4m3 cache: the
+    oracle (its own e4m3 table, q_scale on the logits) equals torch SDPA on
+    torch's float8_e4m3fn decoding of the same codes times their scales."""
+    L, Hq, Hkv, D, qs, ks, vs = 29, 4, 2, 32, 0.04, 0.05, 0.08
+    w = W.build("fp8q", q_lens=[L], kv_lens=[L], distribution=(0, 1, 0), num_q_heads=Hq,
+                num_kv_heads=Hkv, head_dim=D, page_size=8, q_dtype="fp8", kv_in_dtype="fp8",
+                cache_dtype="fp8", softmax_scale=0.2, q_scale=qs, k_scale=ks, v_scale=vs,
+                seed=12)
+    out, _ = oracle_forward(w)
+
+    def deq(codes, sc):
+        return (codes.view(torch.float8_e4m3fn).to(torch.float64) * sc).numpy()
+    ref = sdpa_causal(deq(w.queries, qs), deq(w.keys, ks), deq(w.values, vs), 0.2)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
 def test_q_scale_multiplies_logits():
     q, k, v = rand((5, 4, 8), 40), rand((9, 2, 8), 41), rand((9, 2, 8), 42)
     a = O.attend_sequence(q, k, v, 4, softmax_scale=0.2, q_scale=3.0)

@@ -84,6 +84,7 @@ PINS = [
     T.test_tiny_config_bruteforce_end_to_end,
     T.test_fp8_prefill_equals_sdpa_on_library_dequant,
     T.test_q_scale_multiplies_logits,
+    T.test_fp8_queries_equal_sdpa_on_torch_dequant,
     T.test_masked_slots_may_hold_nan,
     lambda: T.test_visible_slots_match_hand_derived_slots(0),
     lambda: T.test_visible_slots_match_hand_derived_slots(4),
