@@ -21,7 +21,9 @@
  * - All shape checks happen on the host before anything is enqueued: a call
  *   that returns an error has no side effect.
  * - Layouts (row-major, contiguous):
- *     queries, out       [total_tokens, num_q_heads, head_dim]      in q_dtype
+ *     queries            [total_tokens, num_q_heads, head_dim]      in q_dtype
+ *     out                [total_tokens, num_q_heads, head_dim]      in q_dtype, or BF16
+ *                        when q_dtype is FP8_E4M3
  *     keys, values       [total_tokens, num_kv_heads, head_dim]     in kv_in_dtype
  *     kv_cache           [num_pages, page_size, 2*num_kv_heads, head_dim_padded]
  *                        in cache_dtype.  This is the same memory as the v3
@@ -95,7 +97,11 @@ typedef struct rpa_desc {
   int32_t cache_dtype;      /* rpa_dtype of kv_cache */
 } rpa_desc;
 /* Supported (q, kv_in, cache) dtype triples: (F32, F32, F32),
- * (BF16, BF16, BF16), (BF16, BF16, FP8_E4M3), (BF16, FP8_E4M3, FP8_E4M3). */
+ * (BF16, BF16, BF16), (BF16, BF16, FP8_E4M3), (BF16, FP8_E4M3, FP8_E4M3), and
+ * with 8-bit queries ("w8a8", tpu-inference layers/vllm/attention.py,
+ * quantisation block; the q_scale argument of the ejkernel interface):
+ * (FP8_E4M3, BF16, FP8_E4M3), (FP8_E4M3, FP8_E4M3, FP8_E4M3).  E4M3 queries
+ * are codes whose values are code * q_scale; their output is BF16. */
 
 /* Scalar options of rpa_forward (the v3 keyword arguments). */
 typedef struct rpa_options {
@@ -104,7 +110,8 @@ typedef struct rpa_options {
                                negative scale favours the least similar keys */
   int32_t sliding_window;   /* 0 = off; W > 0: key j visible iff pos - j < W */
   float logits_soft_cap;    /* 0 = off; c > 0: s -> c * tanh(s / c), after all scales */
-  float q_scale;            /* 0 = none (1.0); multiplies the logits */
+  float q_scale;            /* 0 = none (1.0); multiplies the logits (for e4m3 queries:
+                               Q as read = stored code * q_scale) */
   float k_scale;            /* 0 = none (1.0); K as read = stored element * k_scale */
   float v_scale;            /* 0 = none (1.0); V as read = stored element * v_scale */
   int32_t chunk_prefill_size;      /* tuning hints; 0 = automatic; results do */
@@ -220,7 +227,8 @@ int rpa_workspace_bytes(const rpa_desc* desc, const rpa_options* opts, size_t* b
  *   out[r][h] = sum_{j visible} e^{s_j} v_scale*Vstored[s][j][g]
  *               / (sum_{j visible} e^{s_j} + e^{sink[h]} if a sink is given)
  * computed with an online softmax in float32 and rounded (nearest even) to
- * q_dtype.  Rows >= qsl[num_seqs] of `out` are not written.  The result does
+ * q_dtype (BF16 for e4m3 queries).  Rows >= qsl[num_seqs] of `out` are not
+ * written.  The result does
  * not depend on `distribution` beyond num_seqs, nor on the tuning hints.
  * `workspace` must hold rpa_workspace_bytes() bytes (device memory, caller
  * owned, contents need not be initialised; it is overwritten).
