@@ -28,6 +28,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <climits>
 #include <cstdio>
 
 #include <type_traits>
@@ -243,6 +244,21 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
     const int r = RPIK * j + lane / CPRK;
     dma_off_k[j] = r * row_bytes + (kchunk(r, lane % CPRK) << 4);
   }
+  // Fused update: the same rows read from the new keys / values, whose token
+  // rows are in_row_bytes apart.
+  const bool fused = p.fuse_update != 0;
+  const uint32_t in_row = p.in_row_bytes;
+  uint32_t dma_in[VDIRECT ? IPW : 1], dma_in_k[KDIRECT ? IPWK : 1];
+#pragma unroll
+  for (int j = 0; j < (VDIRECT ? IPW : 1); ++j) {
+    const int r = RPI * j + lane / CPR;
+    dma_in[j] = r * in_row + (swz_chunk<D>(r, lane % CPR) << 4);
+  }
+#pragma unroll
+  for (int j = 0; j < (KDIRECT ? IPWK : 1); ++j) {
+    const int r = RPIK * j + lane / CPRK;
+    dma_in_k[j] = r * in_row + (kchunk(r, lane % CPRK) << 4);
+  }
 
   // LDS byte offsets inside a K / V buffer (fixed per lane):
   //  K read (half hf, k-step ks): row hf*32 + col, logical chunk 2ks + kg,
@@ -329,6 +345,16 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
     const int kv_hi = ctx + it.q_end;               // exclusive
     const int* bt = p.block_tables + (long long)seq * p.pps;
     const char* kv_head = static_cast<const char*>(p.cache) + 2LL * g * p.Dpad * ESZ;
+    // Fused update: new tokens (positions >= ctx) come from the call's new K
+    // / V rows (row q0 + pos - ctx), and the unit of the first q head of kv
+    // head g writes its own tile's new tokens (positions ctx + q_begin ..
+    // ctx + q_end - 1) into their cache slots.
+    const char* in_k = fused ? static_cast<const char*>(p.new_k) + (long long)g * D * ESZ : nullptr;
+    const char* in_v = fused ? static_cast<const char*>(p.new_v) + (long long)g * D * ESZ : nullptr;
+    const int new_lo = fused ? ctx : INT_MAX;       // first key read from the new rows
+    const bool writer = fused && hh < Hkv;
+    const int own_lo = ctx + it.q_begin, own_hi = ctx + it.q_end;
+    char* cache_w = const_cast<char*>(kv_head);
 
     const int row_q = it.q_begin + wave * 32 + col;  // this lane's query row (within the seq)
     const bool row_ok = row_q < it.q_end;
@@ -374,13 +400,19 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
       constexpr int IPW_ = K_ ? IPWK : IPW, RPI_ = K_ ? RPIK : RPI, CPR_ = K_ ? CPRK : CPR;
       const int t0 = blk * BK + 16 * wave;           // the wave's first token
       const uint32_t lds0 = lds_addr(buf + wave * IPW_ * 1024);
-      if (t0 >= kv_lo && t0 + 16 <= kv_hi) {
-        // 16 tokens of one page (page_size >= 16): uniform base + lane offsets
+      const char* in_base = K_ ? in_k : in_v;
+      if (t0 >= kv_lo && t0 + 16 <= min(kv_hi, new_lo)) {
+        // 16 cached tokens of one page (page_size >= 16): uniform base + lane offsets
         const int page = __builtin_amdgcn_readfirstlane(s_pt[(t0 >> sh) - pt_base]);
         const uint32_t crow = ((uint32_t)page << sh) | (uint32_t)(t0 & pmask);
         const char* base = uniform_ptr(kv_head + vofs + (uint64_t)crow * row_bytes);
 #pragma unroll
         for (int j = 0; j < IPW_; ++j) dma16_s(base, K_ ? dma_off_k[j] : dma_off[j], lds0 + j * 1024);
+      } else if (t0 >= max(kv_lo, new_lo) && t0 + 16 <= kv_hi) {
+        // 16 new tokens: consecutive rows of the call's new K / V
+        const char* base = uniform_ptr(in_base + (uint64_t)(q0 + t0 - ctx) * in_row);
+#pragma unroll
+        for (int j = 0; j < IPW_; ++j) dma16_s(base, K_ ? dma_in_k[j] : dma_in[j], lds0 + j * 1024);
       } else {
         // range edge: rows outside [kv_lo, kv_hi) come from the zero row
 #pragma unroll
@@ -390,9 +422,13 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
           const int lc = K_ ? kchunk(r, lane % CPR_) : swz_chunk<D>(r, lane % CPR_);
           const char* src = zero_row + (lc << 4);
           if (tok >= kv_lo && tok < kv_hi) {
-            const int page = s_pt[(tok >> sh) - pt_base];
-            const uint32_t crow = ((uint32_t)page << sh) | (uint32_t)(tok & pmask);
-            src = kv_head + vofs + (uint64_t)crow * row_bytes + (lc << 4);
+            if (tok >= new_lo) {
+              src = in_base + (uint64_t)(q0 + tok - ctx) * in_row + (lc << 4);
+            } else {
+              const int page = s_pt[(tok >> sh) - pt_base];
+              const uint32_t crow = ((uint32_t)page << sh) | (uint32_t)(tok & pmask);
+              src = kv_head + vofs + (uint64_t)crow * row_bytes + (lc << 4);
+            }
           }
           dma16(src, lds0 + j * 1024);
         }
@@ -406,11 +442,63 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
         const int tok = blk * BK + cidx / GCPR, cc = cidx % GCPR;
         uint4 a = make_uint4(0, 0, 0, 0);
         if (tok >= kv_lo && tok < kv_hi) {
-          const int page = s_pt[(tok >> sh) - pt_base];
-          const uint32_t crow = ((uint32_t)page << sh) | (uint32_t)(tok & pmask);
-          a = *reinterpret_cast<const uint4*>(kv_head + vofs + (uint64_t)crow * row_bytes + cc * 16);
+          if (tok >= new_lo) {
+            const char* in_base = vofs ? in_v : in_k;
+            a = *reinterpret_cast<const uint4*>(in_base + (uint64_t)(q0 + tok - ctx) * in_row + cc * 16);
+          } else {
+            const int page = s_pt[(tok >> sh) - pt_base];
+            const uint32_t crow = ((uint32_t)page << sh) | (uint32_t)(tok & pmask);
+            a = *reinterpret_cast<const uint4*>(kv_head + vofs + (uint64_t)crow * row_bytes + cc * 16);
+          }
         }
         regs[i] = a;
+      }
+    };
+    // The cache slot of key position tok (its K row; + v_bytes for V).
+    auto slot_row = [&](int tok) -> char* {
+      const int page = bt[tok >> sh];
+      return cache_w + (uint64_t)(((uint32_t)page << sh) | (uint32_t)(tok & pmask)) * row_bytes;
+    };
+    // Fused update, staged rows: the writer stores the codes of its own new
+    // tokens (rows of block blk) as they were fetched, and zeroes pad lanes.
+    auto write_staged = [&](const uint4* regs, int blk, uint32_t vofs) {
+      if (!writer) return;
+      const int lo = max(blk * BK, own_lo), hi = min(blk * BK + BK, own_hi);
+      if (lo >= hi) return;
+#pragma unroll
+      for (int i = 0; i < (VDIRECT ? 0 : PER); ++i) {
+        const int cidx = tid + NT * i;
+        const int tok = blk * BK + cidx / GCPR, cc = cidx % GCPR;
+        if (tok >= lo && tok < hi) {
+          char* dst = slot_row(tok) + vofs;
+          *reinterpret_cast<uint4*>(dst + cc * 16) = regs[i];
+          if (cc == 0)
+            for (int pc = GCPR; pc < (int)(p.Dpad * ESZ / 16); ++pc)
+              *reinterpret_cast<uint4*>(dst + pc * 16) = make_uint4(0, 0, 0, 0);
+        }
+      }
+    };
+    // Fused update, rows copied into LDS as stored (bf16 K and V, e4m3 K of
+    // the fp8-query kernel): the writer stores its own new tokens of block
+    // blk from the LDS buffer, pad lanes zeroed.
+    auto write_lds = [&](auto isk, int blk, const char* buf) __attribute__((always_inline)) {
+      constexpr bool K_ = decltype(isk)::value;
+      constexpr int RB_ = K_ ? RBK : RB;
+      constexpr int DCH = (K_ ? RBK : RB) / 16;        // chunks holding data
+      if (!writer) return;
+      const int lo = max(blk * BK, own_lo), hi = min(blk * BK + BK, own_hi);
+      if (lo >= hi) return;
+      const int wch = p.Dpad * ESZ / 16;               // chunks of a cache head row
+      const int n = (hi - lo) * wch;
+      for (int i = tid; i < n; i += NT) {
+        const int rr = i / wch, c = i - rr * wch;
+        const int tok = lo + rr, r = tok - blk * BK;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (c < DCH) {
+          const int pc = K_ ? kchunk(r, c) : swz_chunk<D>(r, c);
+          v = *reinterpret_cast<const uint4*>(buf + r * RB_ + (pc << 4));
+        }
+        *reinterpret_cast<uint4*>(slot_row(tok) + (K_ ? 0u : v_bytes) + c * 16) = v;
       }
     };
     auto stage_staged = [&](const uint4* regs, char* buf) {  // e4m3 -> bf16 into swizzled rows
@@ -451,14 +539,25 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
         ensure_pages(blk + 2);
         load_k(blk + 2);
       }
+      // fused update: K(blk + 1) and V(blk) stay in LDS through this step
+      if constexpr (KDIRECT) {
+        if (blk + 1 < blk_end) write_lds(std::true_type{}, blk + 1, kbuf(blk + 1));
+      }
+      if constexpr (VDIRECT) write_lds(std::false_type{}, blk, vbuf(blk));
     };
     // step b, last part (e4m3): widen the fetched rows into their buffers
     auto end_step = [&](int blk) __attribute__((always_inline)) {
       if constexpr (!VDIRECT) {
-        if (blk + 1 < blk_end) stage_staged(vr, vbuf(blk + 1));
+        if (blk + 1 < blk_end) {
+          stage_staged(vr, vbuf(blk + 1));
+          write_staged(vr, blk + 1, v_bytes);
+        }
       }
       if constexpr (!KDIRECT) {
-        if (blk + 2 < blk_end) stage_staged(kr, kbuf(blk + 2));
+        if (blk + 2 < blk_end) {
+          stage_staged(kr, kbuf(blk + 2));
+          write_staged(kr, blk + 2, 0);
+        }
       }
     };
 
@@ -678,9 +777,13 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
     const int b0 = blk_first;
     ensure_pages(b0);
     load_k(b0);
-    if constexpr (!KDIRECT) stage_staged(kr, kbuf(b0));
+    if constexpr (!KDIRECT) {
+      stage_staged(kr, kbuf(b0));
+      write_staged(kr, b0, 0);
+    }
     if constexpr (KDIRECT) wait_vmem_all();
     __syncthreads();
+    if constexpr (KDIRECT) write_lds(std::true_type{}, b0, kbuf(b0));
     load_v(b0);
     if (b0 + 1 < blk_end) {
       ensure_pages(b0 + 1);
@@ -714,9 +817,15 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
       }
       mx = to_mx(red(t, __shfl_xor(t, 32)));
     }
-    if constexpr (!VDIRECT) stage_staged(vr, vbuf(b0));
+    if constexpr (!VDIRECT) {
+      stage_staged(vr, vbuf(b0));
+      write_staged(vr, b0, v_bytes);
+    }
     if constexpr (!KDIRECT) {
-      if (b0 + 1 < blk_end) stage_staged(kr, kbuf(b0 + 1));
+      if (b0 + 1 < blk_end) {
+        stage_staged(kr, kbuf(b0 + 1));
+        write_staged(kr, b0 + 1, 0);
+      }
     }
 
     // ---- the steps: masked [b0, A), unmasked [A, B), masked [B, end) ----
@@ -782,9 +891,9 @@ hipError_t launch_d(const AttnParams& p, long long blocks, hipStream_t s) {
   if (blocks > resident) blocks = resident;
   if (trace_active()) {
     char nm[80];
-    std::snprintf(nm, sizeof nm, "prefill_kernel<%s%s,D%d%s>(%s)", elem_name<CT>(),
+    std::snprintf(nm, sizeof nm, "prefill_kernel<%s%s,D%d%s>(%s%s)", elem_name<CT>(),
                   QF8 ? ",q_fp8" : "", D, CAP ? ",cap" : "",
-                  p.fuse_merge ? "merge+tiles" : "tiles");
+                  p.fuse_merge ? "merge+tiles" : "tiles", p.fuse_update ? "+update" : "");
     if (trace_launch(nm, (unsigned)blocks, NT, 0, s)) return hipSuccess;
   }
   prefill_kernel<CT, D, CAP, QF8><<<dim3((unsigned)blocks), NT, 0, s>>>(p);

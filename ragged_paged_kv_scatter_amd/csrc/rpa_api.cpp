@@ -334,6 +334,7 @@ ScatterParams scatter_params(const rpa_desc& d, const void* keys, const void* va
   p.Dpad = d.head_dim_padded;
   p.inv_k_scale_src = k_scale > 0.f ? k_scale : 1.f;
   p.inv_v_scale_src = v_scale > 0.f ? v_scale : 1.f;
+  p.skip_min_q = INT_MAX;
   return p;
 }
 }  // namespace
@@ -565,11 +566,20 @@ int forward_impl(const rpa_desc* desc, const rpa_options* opts, const void* quer
       !one_stream && prefill_supported(*desc) && desc->total_tokens > desc->max_num_seqs;
   pp.co_allowed = side ? 1 : 0;
   trace_printf("[rpa] streams %s row_waves=%d\n", side ? "caller+side" : "caller", pp.row_waves);
+  // The update fused into the prefill kernel: when the new tokens are a bit
+  // copy (no quantisation), the prefill kernel reads its sequences' new
+  // tokens from keys / values and writes them into their pages itself; the
+  // planner's launch then writes only the other sequences' tokens.
+  const bool fuse = keys && prefill_supported(*desc) && desc->kv_in_dtype == desc->cache_dtype;
   // one launch: the planner, and the cache update when new tokens come along
   ScatterParams sp = {};
-  if (keys)
+  if (keys) {
     sp = scatter_params(*desc, keys, values, kv_cache, kv_lens, block_tables, query_start_loc,
                         distribution, opts->k_scale, opts->v_scale);
+    if (fuse) sp.skip_min_q = prefill_min_q(*desc);
+  }
+  trace_printf("[rpa] update %s\n", !keys ? "none" : fuse ? "fused (prefill sequences in the "
+               "prefill kernel, the rest in prep_kernel)" : "prep_kernel");
   prof_begin(keys ? "plan+scatter" : "plan", s);
   hipError_t e = launch_prep(pp, keys ? &sp : nullptr, (rpa_dtype)desc->kv_in_dtype,
                              (rpa_dtype)desc->cache_dtype, s);
@@ -599,6 +609,10 @@ int forward_impl(const rpa_desc* desc, const rpa_options* opts, const void* quer
   ap.qk_scale = opts->softmax_scale * qs * ks;
   ap.v_scale = opts->v_scale > 0.f ? opts->v_scale : 1.f;
   ap.cap = opts->logits_soft_cap;
+  ap.fuse_update = fuse ? 1 : 0;
+  ap.new_k = fuse ? keys : nullptr;
+  ap.new_v = fuse ? values : nullptr;
+  ap.in_row_bytes = (uint32_t)desc->num_kv_heads * desc->head_dim * elem_size(desc->kv_in_dtype);
   const rpa_dtype qd = (rpa_dtype)desc->q_dtype, cd = (rpa_dtype)desc->cache_dtype;
 
   if (!side) {

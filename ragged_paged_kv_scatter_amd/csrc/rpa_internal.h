@@ -120,6 +120,8 @@ struct ScatterParams {
   const int32_t* dist;
   int32_t T, max_num_seqs, pps, page_size, Hkv, D, Dpad;
   float inv_k_scale_src, inv_v_scale_src;  // the scales themselves (division done in-kernel)
+  int32_t skip_min_q;    // tokens of sequences with q_len >= this are left to the prefill
+                         // kernel (the fused update); INT_MAX: write every token
 };
 
 struct SlotMapParams {    // flat slot of each new token row
@@ -180,6 +182,14 @@ struct AttnParams {
   float v_scale;       // 1 when none
   float cap;           // 0 when none
   int32_t fuse_merge;  // prefill kernel: first merge the row kernel's split partials
+  // Fused update (the prefill kernel's sequences): new tokens (positions
+  // >= kv_len - q_len) are read from new_k / new_v, [T, Hkv, D] rows of
+  // in_row_bytes, in the cache's own element type, and written into the
+  // cache by the unit of the first q head of each kv head's group.
+  int32_t fuse_update;
+  uint32_t in_row_bytes;
+  const void* new_k;
+  const void* new_v;
 };
 
 // Launchers (return hipSuccess or the launch error).

@@ -79,9 +79,11 @@ __device__ __forceinline__ void scatter_body(const ScatterParams& p, int tpw, in
       const int s = qsl_in_lds ? find_seq(s_qsl, num_seqs, tok) : find_seq(p.qsl, num_seqs, tok);
       const int q0 = p.qsl[s];
       const int q_len = p.qsl[s + 1] - q0;
-      const int pos = p.kv_lens[s] - q_len + (tok - q0);
-      const int page = p.block_tables[(long long)s * p.pps + pos / p.page_size];
-      row = (long long)page * p.page_size + pos % p.page_size;
+      if (q_len < p.skip_min_q) {      // else the prefill kernel writes this token
+        const int pos = p.kv_lens[s] - q_len + (tok - q0);
+        const int page = p.block_tables[(long long)s * p.pps + pos / p.page_size];
+        row = (long long)page * p.page_size + pos % p.page_size;
+      }
     }
     s_row[threadIdx.x] = row;
   }

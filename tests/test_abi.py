@@ -308,15 +308,21 @@ def test_trace_format_lines(lib, kind):
     assert offs == sorted(offs) and all(x % 256 == 0 for x in offs)
     assert int(ws["max_parts"]) <= 2 * int(ws["max_chunks"])
     assert lines[2].split()[2] == ("caller+side" if kind == "mixed" else "caller")
-    launches = [l for l in lines[3:] if l.split()[1] == "launch"]
-    assert len(launches) == len(lines) - 3
+    # the update: fused into the prefill kernel for bit-copy updates of batches
+    # with a prefill kernel, else in the planner's launch
+    assert lines[3].split()[1] == "update"
+    assert lines[3].split()[2] == ("prep_kernel" if kind == "f32" else "fused")
+    launches = [l for l in lines[4:] if l.split()[1] == "launch"]
+    assert len(launches) == len(lines) - 4
     assert [l.split()[2].split("<")[0] for l in launches] == order
     for l in launches:
         f = _kv(l)
         assert int(f["grid"]) >= 1 and int(f["block"]) in (256, 1024)
     # without the update the planner's launch carries no scatter
     text2 = rpa.rpa_trace_format(d, o, with_update=False)
-    assert "plan+scatter" not in text2 and "update=0" in text2
+    assert "plan+scatter" not in text2 and "update=0" in text2 and "[rpa] update none" in text2
+    if kind != "f32":
+        assert "+update)" in text and "+update)" not in text2   # the prefill kernel's share
 
 
 def test_trace_format_reports_host_errors(lib):
