@@ -49,7 +49,10 @@
  *   0 <= q_len <= kv_len <= pages_per_seq*page_size; qsl non-decreasing from
  *   0 with qsl[num_seqs] <= total_tokens; block-table entries that cover
  *   [0, kv_len) are < num_pages; the slots written by one update are
- *   distinct.  Block-table entries past ceil(kv_len/page_size) are not read.
+ *   distinct, and none of them holds a context key (a position below
+ *   kv_len - q_len) of any sequence of the call: rpa_forward writes the new
+ *   tokens of prefill sequences while it attends.  Block-table entries past
+ *   ceil(kv_len/page_size) are not read.
  */
 #ifndef RPA_H_
 #define RPA_H_
@@ -299,7 +302,8 @@ enum {
   RPA_META_LENS = 2,          /* kv_len < 0, q_len > kv_len, or kv_len > pages_per_seq*page_size */
   RPA_META_BLOCK_TABLE = 4,   /* an entry covering [0, kv_len) outside [0, num_pages) */
   RPA_META_SLOTS = 8,         /* two new tokens of the update map to one cache slot */
-  RPA_META_DISTRIBUTION = 16  /* a negative count, or counts summing past max_num_seqs */
+  RPA_META_DISTRIBUTION = 16, /* a negative count, or counts summing past max_num_seqs */
+  RPA_META_WRITE_IN_CONTEXT = 32 /* a slot the update writes holds a context key of a sequence */
 };
 
 /* Device-side check of the metadata preconditions listed at the top of this
@@ -308,7 +312,7 @@ enum {
  * kv_len - q_len + t of a sequence goes to slot (block_tables page, offset))
  * but not what an inconsistent table does; the update and attention calls do
  * not check it on the device, so a caller can run this first.
- * Enqueues three small kernels on `stream` and returns without a host sync;
+ * Enqueues four small kernels on `stream` and returns without a host sync;
  * when they have run, *status (device int32) holds the OR of the RPA_META_*
  * bits of every violated precondition, 0 when all hold.  slot_bits is device
  * scratch of (num_pages * page_size + 31) / 32 uint32 words, caller owned,

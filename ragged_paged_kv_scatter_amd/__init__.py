@@ -23,10 +23,12 @@ __all__ = ["rpa_update_kv_cache", "rpa_forward", "rpa_forward_noalloc", "rpa_wor
            "rpa_reshape_and_cache", "rpa_copy_blocks", "rpa_swap_blocks",
            "rpa_validate_metadata", "rpa_trace_format", "profile_enable", "profile_read",
            "RpaError",
-           "META_QSL", "META_LENS", "META_BLOCK_TABLE", "META_SLOTS", "META_DISTRIBUTION"]
+           "META_QSL", "META_LENS", "META_BLOCK_TABLE", "META_SLOTS", "META_DISTRIBUTION",
+           "META_WRITE_IN_CONTEXT"]
 
 # bits of rpa_validate_metadata's status word (include/rpa.h RPA_META_*)
 META_QSL, META_LENS, META_BLOCK_TABLE, META_SLOTS, META_DISTRIBUTION = 1, 2, 4, 8, 16
+META_WRITE_IN_CONTEXT = 32
 
 _DT = {torch.float32: _lib.RPA_F32, torch.bfloat16: _lib.RPA_BF16, torch.uint8: _lib.RPA_FP8_E4M3,
        torch.float8_e4m3fn: _lib.RPA_FP8_E4M3}

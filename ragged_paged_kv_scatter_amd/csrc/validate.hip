@@ -7,7 +7,11 @@
 //      block-table entries that cover [0, kv_len);
 //   3. one thread per new token: its slot (page * page_size + offset) is
 //      marked in the bitmap; a bit already set means two writes of one
-//      update land on the same slot.
+//      update land on the same slot;
+//   4. one workgroup per sequence: every context position [0, kv_len - q_len)
+//      whose slot is marked means the update overwrites a key that a
+//      sequence reads as context (the prefill kernel's fused update writes
+//      new tokens while other units read context, so the two must not meet).
 // Every read stays inside the documented array sizes whatever the values, so
 // the check itself is safe on bad metadata.
 #include "rpa.h"
@@ -95,6 +99,26 @@ __global__ __launch_bounds__(kVThreads) void validate_slots(ValidateParams p) {
   }
 }
 
+__global__ __launch_bounds__(kVThreads) void validate_reads(ValidateParams p) {
+  const int num_seqs = num_seqs_of(p);
+  for (int s = blockIdx.x; s < num_seqs; s += gridDim.x) {
+    const int q0 = p.qsl[s], q1 = p.qsl[s + 1];
+    const int kv = p.kv_lens[s];
+    const int q_len = q1 - q0;
+    if (q1 < q0 || q_len > kv || kv < 0 || kv > p.pps * p.page_size) continue;
+    const int ctx = kv - q_len;
+    const int32_t* bt = p.block_tables + (long long)s * p.pps;
+    bool hit = false;
+    for (int pos = threadIdx.x; pos < ctx; pos += kVThreads) {
+      const int pg = bt[pos / p.page_size];
+      if (pg < 0 || pg >= p.num_pages) continue;
+      const long long slot = (long long)pg * p.page_size + pos % p.page_size;
+      if (p.slot_bits[slot >> 5] & (1u << (slot & 31))) hit = true;
+    }
+    if (hit) atomicOr(p.status, (int)RPA_META_WRITE_IN_CONTEXT);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_validate(const ValidateParams& p, hipStream_t s) {
@@ -106,6 +130,8 @@ hipError_t launch_validate(const ValidateParams& p, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long long tok_wgs = std::min<long long>((p.T + kVThreads - 1) / kVThreads, 4096);
   validate_slots<<<dim3((unsigned)std::max<long long>(tok_wgs, 1)), kVThreads, 0, s>>>(p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  validate_reads<<<dim3((unsigned)std::max(std::min(p.max_num_seqs, 4096), 1)), kVThreads, 0, s>>>(p);
   return hipGetLastError();
 }
 

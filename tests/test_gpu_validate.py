@@ -52,6 +52,16 @@ def expected_bits(kv_lens, bt, qsl, dist, T, pps, ps, num_pages):
         if slot in slots:
             bits |= rpa.META_SLOTS
         slots.add(slot)
+    # no written slot may hold a context key (positions below kv_len - q_len)
+    for s in range(n):
+        q0, q1, kv = int(qsl[s]), int(qsl[s + 1]), int(kv_lens[s])
+        if q1 < q0 or (q1 - q0) > kv or kv < 0 or kv > pps * ps:
+            continue
+        for pos in range(kv - (q1 - q0)):
+            pg = int(bt[s * pps + pos // ps])
+            if 0 <= pg < num_pages and pg * ps + pos % ps in slots:
+                bits |= rpa.META_WRITE_IN_CONTEXT
+                break
     return bits
 
 
@@ -119,6 +129,13 @@ def _plant(w, kind):
         s, ps = pre, w.page_size
         last = (int(kv[s]) - 1) // ps
         bt[s * w.pages_per_seq + last] = bt[s * w.pages_per_seq + last - 1]
+    elif kind == "written_slot_in_context":
+        # the longest query's first new-token page becomes the first context
+        # page of another sequence that has context
+        s, ps = pre, w.page_size
+        ctx = int(kv[s]) - int(qlen[s])
+        other = next(o for o in range(n) if o != s and int(kv[o]) - int(qlen[o]) > 0)
+        bt[other * w.pages_per_seq] = bt[s * w.pages_per_seq + ctx // ps]
     elif kind == "distribution_negative":
         dist[1] = -1
         dist[2] += 1
@@ -134,7 +151,8 @@ KINDS = {"qsl_start": rpa.META_QSL, "qsl_order": rpa.META_QSL,
          "kv_past_table": rpa.META_LENS, "block_entry_out_of_pool": rpa.META_BLOCK_TABLE,
          "block_entry_negative": rpa.META_BLOCK_TABLE, "shared_slot": rpa.META_SLOTS,
          "distribution_negative": rpa.META_DISTRIBUTION,
-         "distribution_past_max": rpa.META_DISTRIBUTION}
+         "distribution_past_max": rpa.META_DISTRIBUTION,
+         "written_slot_in_context": rpa.META_WRITE_IN_CONTEXT}
 
 
 @pytest.mark.parametrize("kind", list(KINDS))
