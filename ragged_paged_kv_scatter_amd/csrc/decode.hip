@@ -670,8 +670,19 @@ __device__ __forceinline__ u32x4 nt_load16(const char* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-template <typename CT, int D, int G, bool CAP, bool QF8>
-__global__ __launch_bounds__(64 * kWavesPerWG) void mfma_row_kernel(AttnParams p) {
+// SH (kv heads a multiple of 4, no lane padding): the 4 waves of a workgroup
+// hold 4 consecutive kv heads of one chunk (wave w = head 4j + w), so they
+// walk the same items in step.  Their K and V rows are contiguous 4-head runs
+// of 8 D element-bytes per token (512 bytes for e4m3 at D = 64): each wave
+// loads whole runs of 8 of the step's 32 tokens and stages every 16-byte
+// piece into the LDS rows of the wave whose head it holds, between two
+// workgroup barriers.  Reading runs instead of each head's own 2 D bytes
+// per token is what keeps the HBM reads long.
+// At D = 64 the LDS of 4 workgroups fits a CU, so registers are held to four
+// waves per SIMD (the planner sizes its chunks by the resident waves).
+template <typename CT, int D, int G, bool CAP, bool QF8, bool SH>
+__global__ __launch_bounds__(64 * kWavesPerWG)
+__attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1))) void mfma_row_kernel(AttnParams p) {
   using Cfg = MfCfg<CT, D>;
   constexpr int ESZ = Cfg::ESZ, E = Cfg::E, LPTK = Cfg::LPTK, TPI = Cfg::TPI, NLI = Cfg::NLI,
                 NMQ = Cfg::NMQ, NMP = Cfg::NMP, LRK = Cfg::LRK, LRV = Cfg::LRV;
@@ -710,6 +721,12 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void mfma_row_kernel(AttnParams p
   const int i_first = min(max(__builtin_amdgcn_readfirstlane(chunk_first[c]), 0), n_items);
   const int i_last = min(max(__builtin_amdgcn_readfirstlane(chunk_first[c + 1]), i_first), n_items);
   const char* kv_head = reinterpret_cast<const char*>(p.cache) + 2LL * g * p.Dpad * ESZ;
+  // SH: this workgroup's run of 4 heads, and the loads that cover it
+  constexpr int RUN = 8 * D * ESZ;               // bytes of 4 heads' K and V of a token
+  constexpr int NLS = RUN / 128;                 // 16-byte loads per lane per step (8 runs a wave)
+  static_assert(!SH || (RUN % 1024 == 0 || 1024 % RUN == 0), "runs tile 1 KiB loads");
+  const char* kv_run = reinterpret_cast<const char*>(p.cache) + 2LL * (g & ~3) * D * ESZ;
+  static_assert(kWavesPerWG == 4, "SH: one wave per head of a group of 4");
 
 
   for (int ii = i_first; ii < i_last; ++ii) {
@@ -800,6 +817,35 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void mfma_row_kernel(AttnParams p
         stage(vw[i], vt + r * LRV + cb);
       }
     };
+    // SH: the runs of tokens k0 + 8 wave .. + 7 (from lim on, lim - 1 again):
+    // load i, lane l holds bytes 1024 i + 16 l of the wave's 8 runs
+    auto load_runs = [&](int lim, int k0, u32x4* rw) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < (SH ? NLS : 0); ++i) {
+        const int b = 1024 * i + 16 * lane;
+        const int tok = min(k0 + 8 * wave + b / RUN, lim - 1);
+        const int page = __builtin_amdgcn_ds_bpermute(((tok >> sh) - pw0) << 2, page_reg);
+        const uint32_t row = ((uint32_t)page << sh) | (uint32_t)(tok & pmask);
+        rw[i] = nt_load16(kv_run + (uint64_t)row * row_bytes + (b % RUN));
+      }
+    };
+    // SH: each loaded piece -> the K or V row (token - k0) of the wave that
+    // owns its head, widened to bf16 as stage() does
+    auto stage_runs = [&](const u32x4* rw) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < (SH ? NLS : 0); ++i) {
+        const int b = 1024 * i + 16 * lane;
+        const int r = 8 * wave + b / RUN;
+        const int in_run = b % RUN;
+        const int hl = in_run / (2 * D * ESZ);                 // head of the group
+        const bool isv = (in_run % (2 * D * ESZ)) >= D * ESZ;
+        const int chunk = (in_run % (D * ESZ)) / 16;
+        char* base = s_v + hl * Cfg::LWAVE;
+        char* dst = isv ? base + 32 * LRK + r * LRV : base + r * LRK;
+        stage(rw[i], dst + 2 * E * chunk);
+      }
+    };
+
     auto compute_step = [&](int k0, int lim) __attribute__((always_inline)) {
       // ---- S = K Q^T for the two groups ----
       f32x4 sg[2];
@@ -871,20 +917,43 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void mfma_row_kernel(AttnParams p
     // step's loads are issued into the same registers and stay in flight while
     // the step is computed from LDS.  The loads are unconditional (past the
     // chunk they re-read its last token), so no wait drains them early.
-    u32x4 kb[NLI], vb[NLI];
-    load_window(lo);
-    load_step(chunk_end(lo), lo, kb, vb);
-    for (int c_lo = lo;;) {
-      const int c_hi = chunk_end(c_lo);
-      for (int k0 = c_lo; k0 < c_hi; k0 += 32) {
-        stage_step(kb, vb);
-        load_step(c_hi, k0 + 32, kb, vb);
-        compute_step(k0, c_hi);
+    if constexpr (SH) {
+      // All 4 waves take the same items, windows and steps: the barriers
+      // match.  (A) nobody still reads the LDS rows of the previous step;
+      // (B) every wave's pieces of this step are staged.
+      u32x4 rb[NLS];
+      load_window(lo);
+      load_runs(chunk_end(lo), lo, rb);
+      for (int c_lo = lo;;) {
+        const int c_hi = chunk_end(c_lo);
+        for (int k0 = c_lo; k0 < c_hi; k0 += 32) {
+          __syncthreads();                                   // (A)
+          stage_runs(rb);
+          load_runs(c_hi, k0 + 32, rb);
+          __syncthreads();                                   // (B)
+          compute_step(k0, c_hi);
+        }
+        if (c_hi >= hi) break;
+        c_lo = c_hi;
+        load_window(c_lo);
+        load_runs(chunk_end(c_lo), c_lo, rb);
       }
-      if (c_hi >= hi) break;
-      c_lo = c_hi;
-      load_window(c_lo);
-      load_step(chunk_end(c_lo), c_lo, kb, vb);
+    } else {
+      u32x4 kb[NLI], vb[NLI];
+      load_window(lo);
+      load_step(chunk_end(lo), lo, kb, vb);
+      for (int c_lo = lo;;) {
+        const int c_hi = chunk_end(c_lo);
+        for (int k0 = c_lo; k0 < c_hi; k0 += 32) {
+          stage_step(kb, vb);
+          load_step(c_hi, k0 + 32, kb, vb);
+          compute_step(k0, c_hi);
+        }
+        if (c_hi >= hi) break;
+        c_lo = c_hi;
+        load_window(c_lo);
+        load_step(chunk_end(c_lo), c_lo, kb, vb);
+      }
     }
 
     // ---- epilogue: l of head c16 over its lane groups; O rows are heads 4 g4 + e ----
@@ -956,7 +1025,7 @@ struct RowCfg {
   static constexpr bool MF = sizeof(QT) <= 2 && G >= 8;
   static constexpr bool QF8 = sizeof(QT) == 1;
   static const void* kernel() {
-    if constexpr (MF) return reinterpret_cast<const void*>(&mfma_row_kernel<CT, D, (MF ? G : 8), CAP, QF8>);
+    if constexpr (MF) return reinterpret_cast<const void*>(&mfma_row_kernel<CT, D, (MF ? G : 8), CAP, QF8, false>);
     else return reinterpret_cast<const void*>(&row_kernel<QT, CT, D, G, EPL, NR, CAP>);
   }
   static int resident() {
@@ -975,14 +1044,21 @@ hipError_t launch_rows_t(const AttnParams& p, hipStream_t s) {
   if (trace_active()) {
     char nm[96];
     if constexpr (Cfg::MF)
-      std::snprintf(nm, sizeof nm, "mfma_row_kernel<%s%s,D%d,G%d%s>", elem_name<CT>(),
-                    Cfg::QF8 ? ",q_fp8" : "", D, G, CAP ? ",cap" : "");
+      std::snprintf(nm, sizeof nm, "mfma_row_kernel<%s%s,D%d,G%d%s%s>", elem_name<CT>(),
+                    Cfg::QF8 ? ",q_fp8" : "", D, G, CAP ? ",cap" : "",
+                    (p.Hkv % 4 == 0 && p.Dpad == D) ? ",shared_loads" : "");
     else
       std::snprintf(nm, sizeof nm, "row_kernel<%s,%s,D%d,G%d,EPL%d,NR%d%s>", elem_name<QT>(),
                     elem_name<CT>(), D, G, Cfg::EPL, Cfg::NR, CAP ? ",cap" : "");
     if (trace_launch(nm, grid.x, 64 * kWavesPerWG, 0, s)) return hipSuccess;
   }
-  if constexpr (Cfg::MF) mfma_row_kernel<CT, D, (Cfg::MF ? G : 8), CAP, Cfg::QF8><<<grid, 64 * kWavesPerWG, 0, s>>>(p);
+  // the 4 waves of a workgroup share their K / V loads when they hold 4 heads
+  // of one chunk and rows carry no lane padding
+  const bool sh = p.Hkv % 4 == 0 && p.Dpad == D;
+  if constexpr (Cfg::MF) {
+    if (sh) mfma_row_kernel<CT, D, (Cfg::MF ? G : 8), CAP, Cfg::QF8, true><<<grid, 64 * kWavesPerWG, 0, s>>>(p);
+    else mfma_row_kernel<CT, D, (Cfg::MF ? G : 8), CAP, Cfg::QF8, false><<<grid, 64 * kWavesPerWG, 0, s>>>(p);
+  }
   else row_kernel<QT, CT, D, G, Cfg::EPL, Cfg::NR, CAP><<<grid, 64 * kWavesPerWG, 0, s>>>(p);
   return hipGetLastError();
 }

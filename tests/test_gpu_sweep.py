@@ -47,6 +47,18 @@ CASES = {
                                        (0.02, 0.04, 0.06)),
     "fp8q_g1_d128_ps16": ("fp8", "fp8", "fp8", 128, 128, 2, 2, 16, 0, 0.0, False,
                           (0.05, 0.05, 0.05)),
+    # kv heads a multiple of 4 with G >= 8: the MFMA row kernel's shared
+    # 4-head loads (the long row crosses 64-page windows at page_size 16)
+    "bf16_g8_d128_hkv4_ps16_sh": ("bf16", "bf16", "bf16", 128, 128, 32, 4, 16, 0, 0.0, False,
+                                  (0, 0, 0)),
+    "bf16_g16_d64_hkv4_ps128_sh": ("bf16", "bf16", "bf16", 64, 64, 64, 4, 128, 0, 0.0, True,
+                                   (0, 0, 0)),
+    "fp8_g16_d64_hkv4_window_sink_sh": ("bf16", "bf16", "fp8", 64, 64, 64, 4, 16, 200, 0.0, True,
+                                        (0, 0.05, 0.05)),
+    "fp8q_g8_d64_hkv8_cap_sh": ("fp8", "bf16", "fp8", 64, 64, 64, 8, 64, 0, 10.0, False,
+                                (0.05, 0.05, 0.05)),
+    "fp8_g8_d128_hkv8_sh": ("bf16", "fp8", "fp8", 128, 128, 64, 8, 32, 0, 0.0, False,
+                            (0, 0.1, 0.1)),
 }
 
 
