@@ -666,6 +666,19 @@ struct MfCfg {
   static constexpr int LWAVE = 32 * (LRK + LRV);  // LDS bytes per wave
 };
 
+// Issue priority of the wave (0 lowest .. 3).  The CU's arbiter prefers the
+// highest priority, then the oldest wave; a wave lowers its priority as it
+// gets through its chunk, so the waves that started later are not starved
+// of loads by the older ones and all finish together.
+__device__ __forceinline__ void wave_priority(int pr) {
+  switch (pr) {
+    case 0: __builtin_amdgcn_s_setprio(0); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    default: __builtin_amdgcn_s_setprio(3); break;
+  }
+}
+
 __device__ __forceinline__ u32x4 nt_load16(const char* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
@@ -678,11 +691,25 @@ __device__ __forceinline__ u32x4 nt_load16(const char* p) {
 // piece into the LDS rows of the wave whose head it holds, between two
 // workgroup barriers.  Reading runs instead of each head's own 2 D bytes
 // per token is what keeps the HBM reads long.
-// At D = 64 the LDS of 4 workgroups fits a CU, so registers are held to four
-// waves per SIMD (the planner sizes its chunks by the resident waves).
+// The planner sizes its chunks by the resident waves of the form launched.
+//
+// Register buffers of the step stream: two (a step in LDS, two in flight)
+// where they fit, one for bf16 rows at D = 128 (64 registers a step) and for
+// bf16 rows at D = 64 without shared loads (K and V loaded per head).  The
+// minimum of waves per SIMD keeps the count the buffers were sized for.
+template <typename CT, int D, bool SH>
+constexpr int mfma_row_nbuf() {
+  return (sizeof(CT) == 2 && (D == 128 || !SH)) ? 1 : 2;
+}
+template <typename CT, int D, bool SH>
+constexpr int mfma_row_min_waves() {
+  return D == 64 ? (mfma_row_nbuf<CT, D, SH>() == 2 ? 3 : 4) : (mfma_row_nbuf<CT, D, SH>() == 2 ? 2 : 1);
+}
+
 template <typename CT, int D, int G, bool CAP, bool QF8, bool SH>
 __global__ __launch_bounds__(64 * kWavesPerWG)
-__attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1))) void mfma_row_kernel(AttnParams p) {
+__attribute__((amdgpu_waves_per_eu(mfma_row_min_waves<CT, D, SH>()))) void mfma_row_kernel(AttnParams p) {
+  constexpr int NBUF = mfma_row_nbuf<CT, D, SH>();
   using Cfg = MfCfg<CT, D>;
   constexpr int ESZ = Cfg::ESZ, E = Cfg::E, LPTK = Cfg::LPTK, TPI = Cfg::TPI, NLI = Cfg::NLI,
                 NMQ = Cfg::NMQ, NMP = Cfg::NMP, LRK = Cfg::LRK, LRV = Cfg::LRV;
@@ -715,11 +742,17 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1))) void mfma_row_kernel(AttnP
   const float cap_l2 = p.cap * kLog2e;
 
   const long long ch = (long long)blockIdx.x * kWavesPerWG + wave;
-  if (ch >= total) return;
   const int c = (int)(ch / Hkv);
   const int g = (int)(ch - (long long)c * Hkv);
-  const int i_first = min(max(__builtin_amdgcn_readfirstlane(chunk_first[c]), 0), n_items);
-  const int i_last = min(max(__builtin_amdgcn_readfirstlane(chunk_first[c + 1]), i_first), n_items);
+  // the chunk's item range is read beside the header (c clamped into the
+  // table; waves past the plan's chunks leave below)
+  const int cc = min(c, p.lay.max_chunks - 1);
+  const int cf0 = __builtin_amdgcn_readfirstlane(chunk_first[cc]);
+  const int cf1 = __builtin_amdgcn_readfirstlane(chunk_first[cc + 1]);
+  if (ch >= total) return;
+  const int i_first = min(max(cf0, 0), n_items);
+  const int i_last = min(max(cf1, i_first), n_items);
+  if (i_first >= i_last) return;
   const char* kv_head = reinterpret_cast<const char*>(p.cache) + 2LL * g * p.Dpad * ESZ;
   // SH: this workgroup's run of 4 heads, and the loads that cover it
   constexpr int RUN = 8 * D * ESZ;               // bytes of 4 heads' K and V of a token
@@ -728,235 +761,252 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1))) void mfma_row_kernel(AttnP
   const char* kv_run = reinterpret_cast<const char*>(p.cache) + 2LL * (g & ~3) * D * ESZ;
   static_assert(kWavesPerWG == 4, "SH: one wave per head of a group of 4");
 
-
-  for (int ii = i_first; ii < i_last; ++ii) {
-    const ItemDesc dsc = items[ii];
-    const int token = __builtin_amdgcn_readfirstlane(dsc.token);
-    const int seq = __builtin_amdgcn_readfirstlane(dsc.seq);
-    const int lo = __builtin_amdgcn_readfirstlane(dsc.lo);
-    const int hi = __builtin_amdgcn_readfirstlane(dsc.hi);
-    const int part = __builtin_amdgcn_readfirstlane(dsc.part);
-    const int* bt = p.block_tables + (long long)seq * p.pps;
-
-    // q^T operands: lane (head c16, d slots of g4) per MFMA (e4m3 queries
-    // widened exactly to bf16)
-    bf16x8 qb[NMQ];
-    {
-      const long long qrow = (long long)token * p.Hq + g * G + (c16 < G ? c16 : 0);
+  struct Desc {
+    int token, seq, lo, hi, part;
+  };
+  auto read_desc = [&](int i) __attribute__((always_inline)) {
+    const ItemDesc dsc = items[i];
+    Desc r;
+    r.token = __builtin_amdgcn_readfirstlane(dsc.token);
+    r.seq = __builtin_amdgcn_readfirstlane(dsc.seq);
+    r.lo = __builtin_amdgcn_readfirstlane(dsc.lo);
+    r.hi = __builtin_amdgcn_readfirstlane(dsc.hi);
+    r.part = __builtin_amdgcn_readfirstlane(dsc.part);
+    return r;
+  };
+  // lane i: the page of the 64-page window from page pw of item d's sequence
+  // (0 past the item's last page)
+  auto window_pages = [&](const Desc& d, int pw) __attribute__((always_inline)) {
+    const int pi = pw + lane;
+    return (pi <= ((d.hi - 1) >> sh)) ? p.block_tables[(long long)d.seq * p.pps + pi] : 0;
+  };
+  // end of the window that holds key k of item d
+  auto chunk_end = [&](const Desc& d, int k) __attribute__((always_inline)) {
+    const long long e = ((long long)(k >> sh) + 64) << sh;
+    return e < d.hi ? (int)e : d.hi;
+  };
+  // K and V rows of the 32 tokens from k0: instruction i, lane l loads 16
+  // bytes of token k0 + TPI i + l / LPTK (tokens from lim on re-read lim - 1),
+  // pages from the window (pw, pg)
+  auto load_step = [&](int pw, int pg, int lim, int k0, u32x4* kw, u32x4* vw) __attribute__((always_inline)) {
+    const uint32_t off = 16u * (uint32_t)(lane % LPTK);
 #pragma unroll
-      for (int m = 0; m < NMQ; ++m) {
-        const int d0 = 32 * m + 8 * g4;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if constexpr (QF8) {
-          if (c16 < G) {
-            const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(p.q) + qrow * D + d0);
-            v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, 1.f, false));
-            v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, 1.f, true));
-            v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, 1.f, false));
-            v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, 1.f, true));
-          }
-        } else {
-          if (c16 < G) v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + qrow * D + d0);
-        }
-        qb[m] = __builtin_bit_cast(bf16x8, v);
-      }
+    for (int i = 0; i < NLI; ++i) {
+      const int tok = min(k0 + TPI * i + lane / LPTK, lim - 1);
+      const int page = __builtin_amdgcn_ds_bpermute(((tok >> sh) - pw) << 2, pg);
+      const uint32_t row = ((uint32_t)page << sh) | (uint32_t)(tok & pmask);
+      const char* kp = kv_head + (uint64_t)row * row_bytes + off;
+      kw[i] = nt_load16(kp);
+      vw[i] = nt_load16(kp + head_bytes);
     }
-
-    int pw0 = 0, page_reg = 0;
-    auto load_window = [&](int k0) __attribute__((always_inline)) {
-      pw0 = k0 >> sh;
-      const int pi = pw0 + lane;
-      page_reg = (pi <= ((hi - 1) >> sh)) ? bt[pi] : 0;
-    };
-    auto chunk_end = [&](int k) __attribute__((always_inline)) {
-      const long long e = ((long long)(k >> sh) + 64) << sh;
-      return e < hi ? (int)e : hi;
-    };
-    // K and V rows of the 32 tokens from k0: instruction i, lane l loads 16
-    // bytes of token k0 + TPI i + l / LPTK (tokens from lim on re-read lim - 1)
-    auto load_step = [&](int lim, int k0, u32x4* kw, u32x4* vw) __attribute__((always_inline)) {
-      const uint32_t off = 16u * (uint32_t)(lane % LPTK);
+  };
+  // one loaded 16-byte piece -> bf16 in LDS at dst (16 or 32 bytes)
+  auto stage = [&](const u32x4& w, char* dst) __attribute__((always_inline)) {
+    if constexpr (FP8) {
+      uint32_t x[8];
 #pragma unroll
-      for (int i = 0; i < NLI; ++i) {
-        const int tok = min(k0 + TPI * i + lane / LPTK, lim - 1);
-        const int page = __builtin_amdgcn_ds_bpermute(((tok >> sh) - pw0) << 2, page_reg);
-        const uint32_t row = ((uint32_t)page << sh) | (uint32_t)(tok & pmask);
-        const char* kp = kv_head + (uint64_t)row * row_bytes + off;
-        kw[i] = nt_load16(kp);
-        vw[i] = nt_load16(kp + head_bytes);
+      for (int k = 0; k < 4; ++k) {
+        x[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[k], 1.f, false));
+        x[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[k], 1.f, true));
       }
-    };
-    // one loaded 16-byte piece -> bf16 in LDS at dst (16 or 32 bytes)
-    auto stage = [&](const u32x4& w, char* dst) __attribute__((always_inline)) {
-      if constexpr (FP8) {
-        uint32_t x[8];
+      *reinterpret_cast<uint4*>(dst) = make_uint4(x[0], x[1], x[2], x[3]);
+      *reinterpret_cast<uint4*>(dst + 16) = make_uint4(x[4], x[5], x[6], x[7]);
+    } else {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  };
+  // the step's K and V rows -> LDS as bf16 (row = token - k0)
+  auto stage_step = [&](const u32x4* kw, const u32x4* vw) __attribute__((always_inline)) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          x[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[k], 1.f, false));
-          x[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[k], 1.f, true));
+    for (int i = 0; i < NLI; ++i) {
+      const int r = TPI * i + lane / LPTK;
+      const int cb = 2 * E * (lane % LPTK);
+      stage(kw[i], kt + r * LRK + cb);
+      stage(vw[i], vt + r * LRV + cb);
+    }
+  };
+  // SH: the runs of tokens k0 + 8 wave .. + 7 (from lim on, lim - 1 again):
+  // load i, lane l holds bytes 1024 i + 16 l of the wave's 8 runs
+  auto load_runs = [&](int pw, int pg, int lim, int k0, u32x4* rw) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < (SH ? NLS : 0); ++i) {
+      const int b = 1024 * i + 16 * lane;
+      const int tok = min(k0 + 8 * wave + b / RUN, lim - 1);
+      const int page = __builtin_amdgcn_ds_bpermute(((tok >> sh) - pw) << 2, pg);
+      const uint32_t row = ((uint32_t)page << sh) | (uint32_t)(tok & pmask);
+      rw[i] = nt_load16(kv_run + (uint64_t)row * row_bytes + (b % RUN));
+    }
+  };
+  // SH: each loaded piece -> the K or V row (token - k0) of the wave that
+  // owns its head, widened to bf16 as stage() does
+  auto stage_runs = [&](const u32x4* rw) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < (SH ? NLS : 0); ++i) {
+      const int b = 1024 * i + 16 * lane;
+      const int r = 8 * wave + b / RUN;
+      const int in_run = b % RUN;
+      const int hl = in_run / (2 * D * ESZ);                 // head of the group
+      const bool isv = (in_run % (2 * D * ESZ)) >= D * ESZ;
+      const int chunk = (in_run % (D * ESZ)) / 16;
+      char* base = s_v + hl * Cfg::LWAVE;
+      char* dst = isv ? base + 32 * LRK + r * LRV : base + r * LRK;
+      stage(rw[i], dst + 2 * E * chunk);
+    }
+  };
+
+  // The wave's steps form one stream over its items and their page windows.
+  // A load cursor runs NBUF steps ahead of the step being computed: each
+  // step's rows go from their register buffer to LDS, the buffer is refilled
+  // with the step NBUF ahead, and those loads stay in flight while this and
+  // the next NBUF - 1 steps are computed.  Past the wave's last key the
+  // cursor re-reads that key, so every step issues the same loads and no
+  // wait drains them early.
+  constexpr int NB = SH ? NLS : 2 * NLI;         // 16-byte loads per lane per step
+  struct LoadCursor {
+    Desc d;
+    int ii, pw, pg, k0, lim;   // item, page window (first page, lane's page), step, window end
+    bool done;
+  };
+  LoadCursor L;
+  L.ii = i_first;
+  L.d = read_desc(i_first);
+  L.pw = L.d.lo >> sh;
+  L.pg = window_pages(L.d, L.pw);
+  L.k0 = L.d.lo;
+  L.lim = chunk_end(L.d, L.d.lo);
+  L.done = false;
+  auto advance = [&]() __attribute__((always_inline)) {
+    if (L.done) return;
+    L.k0 += 32;
+    if (L.k0 < L.lim) return;
+    if (L.lim < L.d.hi) {                        // the item's next page window
+      L.pw = L.lim >> sh;
+      L.pg = window_pages(L.d, L.pw);
+      L.k0 = L.lim;
+      L.lim = chunk_end(L.d, L.k0);
+    } else if (L.ii + 1 < i_last) {              // the next item
+      ++L.ii;
+      L.d = read_desc(L.ii);
+      L.pw = L.d.lo >> sh;
+      L.pg = window_pages(L.d, L.pw);
+      L.k0 = L.d.lo;
+      L.lim = chunk_end(L.d, L.k0);
+    } else {                                     // past the end: the last key again
+      L.done = true;
+      L.k0 = L.lim - 1;
+    }
+  };
+  auto issue = [&](u32x4* buf) __attribute__((always_inline)) {
+    if constexpr (SH) load_runs(L.pw, L.pg, L.lim, L.k0, buf);
+    else load_step(L.pw, L.pg, L.lim, L.k0, buf, buf + NLI);
+  };
+  auto stage_buf = [&](const u32x4* buf) __attribute__((always_inline)) {
+    if constexpr (SH) stage_runs(buf);
+    else stage_step(buf, buf + NLI);
+  };
+
+  // q^T operands of item d: lane (head c16, d slots of g4) per MFMA (e4m3
+  // queries widened exactly to bf16)
+  bf16x8 qb[NMQ];
+  auto load_q = [&](const Desc& d) __attribute__((always_inline)) {
+    const long long qrow = (long long)d.token * p.Hq + g * G + (c16 < G ? c16 : 0);
+#pragma unroll
+    for (int m = 0; m < NMQ; ++m) {
+      const int d0 = 32 * m + 8 * g4;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if constexpr (QF8) {
+        if (c16 < G) {
+          const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(p.q) + qrow * D + d0);
+          v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, 1.f, false));
+          v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, 1.f, true));
+          v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, 1.f, false));
+          v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, 1.f, true));
         }
-        *reinterpret_cast<uint4*>(dst) = make_uint4(x[0], x[1], x[2], x[3]);
-        *reinterpret_cast<uint4*>(dst + 16) = make_uint4(x[4], x[5], x[6], x[7]);
       } else {
-        *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+        if (c16 < G) v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + qrow * D + d0);
       }
-    };
+      qb[m] = __builtin_bit_cast(bf16x8, v);
+    }
+  };
 
-    f32x4 o[NMP];
+  f32x4 o[NMP];
+  float m_run, l_run;   // head c16
+  auto reset = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int b = 0; b < NMP; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;   // head c16
+    m_run = -INFINITY;
+    l_run = 0.f;
+  };
 
-    // the step's K and V rows -> LDS as bf16 (row = token - k0)
-    auto stage_step = [&](const u32x4* kw, const u32x4* vw) __attribute__((always_inline)) {
+  auto compute_step = [&](int k0, int lim) __attribute__((always_inline)) {
+    // ---- S = K Q^T for the two groups ----
+    f32x4 sg[2];
 #pragma unroll
-      for (int i = 0; i < NLI; ++i) {
-        const int r = TPI * i + lane / LPTK;
-        const int cb = 2 * E * (lane % LPTK);
-        stage(kw[i], kt + r * LRK + cb);
-        stage(vw[i], vt + r * LRV + cb);
-      }
-    };
-    // SH: the runs of tokens k0 + 8 wave .. + 7 (from lim on, lim - 1 again):
-    // load i, lane l holds bytes 1024 i + 16 l of the wave's 8 runs
-    auto load_runs = [&](int lim, int k0, u32x4* rw) __attribute__((always_inline)) {
+    for (int t = 0; t < 2; ++t) {
+      sg[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const char* kr = kt + (16 * t + c16) * LRK + 16 * g4;
 #pragma unroll
-      for (int i = 0; i < (SH ? NLS : 0); ++i) {
-        const int b = 1024 * i + 16 * lane;
-        const int tok = min(k0 + 8 * wave + b / RUN, lim - 1);
-        const int page = __builtin_amdgcn_ds_bpermute(((tok >> sh) - pw0) << 2, page_reg);
-        const uint32_t row = ((uint32_t)page << sh) | (uint32_t)(tok & pmask);
-        rw[i] = nt_load16(kv_run + (uint64_t)row * row_bytes + (b % RUN));
-      }
-    };
-    // SH: each loaded piece -> the K or V row (token - k0) of the wave that
-    // owns its head, widened to bf16 as stage() does
-    auto stage_runs = [&](const u32x4* rw) __attribute__((always_inline)) {
-#pragma unroll
-      for (int i = 0; i < (SH ? NLS : 0); ++i) {
-        const int b = 1024 * i + 16 * lane;
-        const int r = 8 * wave + b / RUN;
-        const int in_run = b % RUN;
-        const int hl = in_run / (2 * D * ESZ);                 // head of the group
-        const bool isv = (in_run % (2 * D * ESZ)) >= D * ESZ;
-        const int chunk = (in_run % (D * ESZ)) / 16;
-        char* base = s_v + hl * Cfg::LWAVE;
-        char* dst = isv ? base + 32 * LRK + r * LRV : base + r * LRK;
-        stage(rw[i], dst + 2 * E * chunk);
-      }
-    };
-
-    auto compute_step = [&](int k0, int lim) __attribute__((always_inline)) {
-      // ---- S = K Q^T for the two groups ----
-      f32x4 sg[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        sg[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const char* kr = kt + (16 * t + c16) * LRK + 16 * g4;
-#pragma unroll
-        for (int m = 0; m < NMQ; ++m) {
-          const uint4 a = *reinterpret_cast<const uint4*>(kr + 64 * m);
-          sg[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qb[m], sg[t], 0, 0, 0);
-        }
-      }
-      // ---- logits of head c16 for tokens k0 + 16 t + 4 g4 + e, online softmax ----
-      float x[8];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float s = sg[t][e];
-          if (use_cap) {
-            const float e2 = __builtin_amdgcn_exp2f(s * cap_k);
-            s = cap_l2 * (1.f - 2.f * __builtin_amdgcn_rcpf(e2 + 1.f));
-          } else {
-            s *= c_log2;
-          }
-          x[4 * t + e] = (k0 + 16 * t + 4 * g4 + e < lim) ? s : -INFINITY;
-        }
-      float bm = x[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) bm = fmaxf(bm, x[i]);
-      bm = slots_max<4>(bm);                    // over the head's four lane groups
-      if (__any(bm > m_run + 8.f)) {
-        const float m_new = fmaxf(m_run, bm);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first step
-        m_run = m_new;
-        l_run *= alpha;
-        // O rows are heads 4 g4 + e: their alpha sits in lane 4 g4 + e
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float a_e = __shfl(alpha, 4 * g4 + e);
-#pragma unroll
-          for (int b = 0; b < NMP; ++b) o[b][e] *= a_e;
-        }
-      }
-      float pr[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pr[i] = __builtin_amdgcn_exp2f(x[i] - m_run);
-        l_run += pr[i];
-      }
-      const uint4 pw = make_uint4(pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3]),
-                                  pack_bf16(pr[4], pr[5]), pack_bf16(pr[6], pr[7]));
-      const bf16x8 pa = __builtin_bit_cast(bf16x8, pw);
-      // ---- O += P V: B from the transposed V rows (tokens 4 g4 + j and 16 + 4 g4 + j) ----
-      const char* r1 = vt + (4 * g4 + (c16 >> 2)) * LRV + 8 * (c16 & 3);
-      const char* r2 = r1 + 16 * LRV;
-#pragma unroll
-      for (int b = 0; b < NMP; ++b) {
-        const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(r1 + 32 * b));
-        const i16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(r2 + 32 * b));
-        typedef short i16x8 __attribute__((ext_vector_type(8)));
-        const i16x8 vb = {x1[0], x1[1], x1[2], x1[3], x2[0], x2[1], x2[2], x2[3]};
-        o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, vb), o[b], 0, 0, 0);
-      }
-    };
-
-    // One register buffer: a step's rows go to LDS first, then the next
-    // step's loads are issued into the same registers and stay in flight while
-    // the step is computed from LDS.  The loads are unconditional (past the
-    // chunk they re-read its last token), so no wait drains them early.
-    if constexpr (SH) {
-      // All 4 waves take the same items, windows and steps: the barriers
-      // match.  (A) nobody still reads the LDS rows of the previous step;
-      // (B) every wave's pieces of this step are staged.
-      u32x4 rb[NLS];
-      load_window(lo);
-      load_runs(chunk_end(lo), lo, rb);
-      for (int c_lo = lo;;) {
-        const int c_hi = chunk_end(c_lo);
-        for (int k0 = c_lo; k0 < c_hi; k0 += 32) {
-          __syncthreads();                                   // (A)
-          stage_runs(rb);
-          load_runs(c_hi, k0 + 32, rb);
-          __syncthreads();                                   // (B)
-          compute_step(k0, c_hi);
-        }
-        if (c_hi >= hi) break;
-        c_lo = c_hi;
-        load_window(c_lo);
-        load_runs(chunk_end(c_lo), c_lo, rb);
-      }
-    } else {
-      u32x4 kb[NLI], vb[NLI];
-      load_window(lo);
-      load_step(chunk_end(lo), lo, kb, vb);
-      for (int c_lo = lo;;) {
-        const int c_hi = chunk_end(c_lo);
-        for (int k0 = c_lo; k0 < c_hi; k0 += 32) {
-          stage_step(kb, vb);
-          load_step(c_hi, k0 + 32, kb, vb);
-          compute_step(k0, c_hi);
-        }
-        if (c_hi >= hi) break;
-        c_lo = c_hi;
-        load_window(c_lo);
-        load_step(chunk_end(c_lo), c_lo, kb, vb);
+      for (int m = 0; m < NMQ; ++m) {
+        const uint4 a = *reinterpret_cast<const uint4*>(kr + 64 * m);
+        sg[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qb[m], sg[t], 0, 0, 0);
       }
     }
+    // ---- logits of head c16 for tokens k0 + 16 t + 4 g4 + e, online softmax ----
+    float x[8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float s = sg[t][e];
+        if (use_cap) {
+          const float e2 = __builtin_amdgcn_exp2f(s * cap_k);
+          s = cap_l2 * (1.f - 2.f * __builtin_amdgcn_rcpf(e2 + 1.f));
+        } else {
+          s *= c_log2;
+        }
+        x[4 * t + e] = (k0 + 16 * t + 4 * g4 + e < lim) ? s : -INFINITY;
+      }
+    float bm = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) bm = fmaxf(bm, x[i]);
+    bm = slots_max<4>(bm);                    // over the head's four lane groups
+    if (__any(bm > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, bm);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first step
+      m_run = m_new;
+      l_run *= alpha;
+      // O rows are heads 4 g4 + e: their alpha sits in lane 4 g4 + e
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a_e = __shfl(alpha, 4 * g4 + e);
+#pragma unroll
+        for (int b = 0; b < NMP; ++b) o[b][e] *= a_e;
+      }
+    }
+    float pr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pr[i] = __builtin_amdgcn_exp2f(x[i] - m_run);
+      l_run += pr[i];
+    }
+    const uint4 pw = make_uint4(pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3]),
+                                pack_bf16(pr[4], pr[5]), pack_bf16(pr[6], pr[7]));
+    const bf16x8 pa = __builtin_bit_cast(bf16x8, pw);
+    // ---- O += P V: B from the transposed V rows (tokens 4 g4 + j and 16 + 4 g4 + j) ----
+    const char* r1 = vt + (4 * g4 + (c16 >> 2)) * LRV + 8 * (c16 & 3);
+    const char* r2 = r1 + 16 * LRV;
+#pragma unroll
+    for (int b = 0; b < NMP; ++b) {
+      const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(r1 + 32 * b));
+      const i16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(r2 + 32 * b));
+      typedef short i16x8 __attribute__((ext_vector_type(8)));
+      const i16x8 vb = {x1[0], x1[1], x1[2], x1[3], x2[0], x2[1], x2[2], x2[3]};
+      o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, vb), o[b], 0, 0, 0);
+    }
+  };
 
-    // ---- epilogue: l of head c16 over its lane groups; O rows are heads 4 g4 + e ----
+  // ---- epilogue of item d: l of head c16 over its lane groups; O rows are heads 4 g4 + e ----
+  auto finish = [&](const Desc& d) __attribute__((always_inline)) {
     const float l_tot = slots_sum<4>(l_run);
     const float vs = p.v_scale;
 #pragma unroll
@@ -966,7 +1016,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1))) void mfma_row_kernel(AttnP
       const float m_h = __shfl(m_run, hl);
       if (hl >= G) continue;
       const int h = g * G + hl;
-      if (part < 0) {
+      if (d.part < 0) {
         float ll = l_h, f = 1.f;
         if (p.sink) {
           const float sgk = p.sink[h] * kLog2e;
@@ -975,11 +1025,11 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1))) void mfma_row_kernel(AttnP
           ll = ll * f + __builtin_amdgcn_exp2f(sgk - mx);
         }
         const float scale = f * vs / ll;
-        uint16_t* op = static_cast<uint16_t*>(p.out) + ((long long)token * p.Hq + h) * D;
+        uint16_t* op = static_cast<uint16_t*>(p.out) + ((long long)d.token * p.Hq + h) * D;
 #pragma unroll
         for (int b = 0; b < NMP; ++b) op[16 * b + c16] = (uint16_t)f32_to_bf16(o[b][e] * scale);
-      } else if (part < p.lay.max_parts) {
-        const long long pb = (long long)part * p.Hq + h;
+      } else if (d.part < p.lay.max_parts) {
+        const long long pb = (long long)d.part * p.Hq + h;
         if (c16 == 0) {
           part_ml[2 * pb] = m_h;
           part_ml[2 * pb + 1] = l_h;
@@ -987,6 +1037,66 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1))) void mfma_row_kernel(AttnP
 #pragma unroll
         for (int b = 0; b < NMP; ++b) part_acc[pb * D + 16 * b + c16] = o[b][e];
       }
+    }
+  };
+
+  // the step being computed: item ci (d, the next one dn), keys [k0, k0 + 32) of the window ending at lim
+  int ci = i_first;
+  Desc d = L.d;
+  Desc dn = read_desc(min(ci + 1, i_last - 1));
+  int k0 = d.lo, lim = L.lim;
+  const int chunk_keys = max(hdr->split, 32);
+  int keys_done = 0;
+  wave_priority(3);
+  u32x4 b0[NB], b1[NBUF == 2 ? NB : 1];
+  issue(b0);
+  advance();
+  if constexpr (NBUF == 2) {
+    issue(b1);
+    advance();
+  }
+  load_q(d);
+  reset();
+  // one step from buffer buf; false once the wave's last item is finished
+  auto step = [&](u32x4* buf) __attribute__((always_inline)) {
+    if constexpr (SH) {
+      // All 4 waves take the same items, windows and steps: the barriers
+      // match.  (A) nobody still reads the LDS rows of the previous step;
+      // (B) every wave's pieces of this step are staged.
+      __syncthreads();                                   // (A)
+      stage_buf(buf);
+      issue(buf);
+      __syncthreads();                                   // (B)
+    } else {
+      stage_buf(buf);
+      issue(buf);
+    }
+    advance();
+    keys_done += 32;
+    wave_priority(3 - min(3, (4 * keys_done) / chunk_keys));
+    compute_step(k0, lim);
+    k0 += 32;
+    if (k0 < lim) return true;
+    if (lim < d.hi) {                                    // the item's next page window
+      k0 = lim;
+      lim = chunk_end(d, k0);
+      return true;
+    }
+    finish(d);
+    if (ci + 1 >= i_last) return false;
+    ++ci;
+    d = dn;
+    dn = read_desc(min(ci + 1, i_last - 1));
+    load_q(d);
+    reset();
+    k0 = d.lo;
+    lim = chunk_end(d, k0);
+    return true;
+  };
+  for (;;) {
+    if (!step(b0)) break;
+    if constexpr (NBUF == 2) {
+      if (!step(b1)) break;
     }
   }
 }
@@ -1024,37 +1134,43 @@ struct RowCfg {
   // bf16 or e4m3 queries with G >= 8 q heads per kv head: the MFMA kernel
   static constexpr bool MF = sizeof(QT) <= 2 && G >= 8;
   static constexpr bool QF8 = sizeof(QT) == 1;
-  static const void* kernel() {
-    if constexpr (MF) return reinterpret_cast<const void*>(&mfma_row_kernel<CT, D, (MF ? G : 8), CAP, QF8, false>);
-    else return reinterpret_cast<const void*>(&row_kernel<QT, CT, D, G, EPL, NR, CAP>);
+  // sh: the MFMA kernel's shared-load form (its own register budget)
+  static const void* kernel(bool sh) {
+    if constexpr (MF) {
+      if (sh) return reinterpret_cast<const void*>(&mfma_row_kernel<CT, D, (MF ? G : 8), CAP, QF8, true>);
+      return reinterpret_cast<const void*>(&mfma_row_kernel<CT, D, (MF ? G : 8), CAP, QF8, false>);
+    } else {
+      return reinterpret_cast<const void*>(&row_kernel<QT, CT, D, G, EPL, NR, CAP>);
+    }
   }
-  static int resident() {
-    static const int cap = resident_blocks(kernel(), 64 * kWavesPerWG, 0);
-    return cap;
+  static int resident(bool sh) {
+    static const int cap[2] = {resident_blocks(kernel(false), 64 * kWavesPerWG, 0),
+                               resident_blocks(kernel(true), 64 * kWavesPerWG, 0)};
+    return cap[MF && sh ? 1 : 0];
   }
 };
 
 template <typename QT, typename CT, int D, int G, bool CAP>
 hipError_t launch_rows_t(const AttnParams& p, hipStream_t s) {
   using Cfg = RowCfg<QT, CT, D, G, CAP>;
+  // the 4 waves of a workgroup share their K / V loads when they hold 4 heads
+  // of one chunk and rows carry no lane padding
+  const bool sh = row_shared_loads(p.Hkv, p.Dpad, D);
   // one wave per (chunk, kv head) for as many chunks as the planner may make
   const long long waves =
-      (long long)row_chunks_max(Cfg::resident() * kWavesPerWG, p.Hkv) * p.Hkv;
+      (long long)row_chunks_max(Cfg::resident(sh) * kWavesPerWG, p.Hkv) * p.Hkv;
   dim3 grid((unsigned)((waves + kWavesPerWG - 1) / kWavesPerWG));
   if (trace_active()) {
     char nm[96];
     if constexpr (Cfg::MF)
       std::snprintf(nm, sizeof nm, "mfma_row_kernel<%s%s,D%d,G%d%s%s>", elem_name<CT>(),
                     Cfg::QF8 ? ",q_fp8" : "", D, G, CAP ? ",cap" : "",
-                    (p.Hkv % 4 == 0 && p.Dpad == D) ? ",shared_loads" : "");
+                    sh ? ",shared_loads" : "");
     else
       std::snprintf(nm, sizeof nm, "row_kernel<%s,%s,D%d,G%d,EPL%d,NR%d%s>", elem_name<QT>(),
                     elem_name<CT>(), D, G, Cfg::EPL, Cfg::NR, CAP ? ",cap" : "");
     if (trace_launch(nm, grid.x, 64 * kWavesPerWG, 0, s)) return hipSuccess;
   }
-  // the 4 waves of a workgroup share their K / V loads when they hold 4 heads
-  // of one chunk and rows carry no lane padding
-  const bool sh = p.Hkv % 4 == 0 && p.Dpad == D;
   if constexpr (Cfg::MF) {
     if (sh) mfma_row_kernel<CT, D, (Cfg::MF ? G : 8), CAP, Cfg::QF8, true><<<grid, 64 * kWavesPerWG, 0, s>>>(p);
     else mfma_row_kernel<CT, D, (Cfg::MF ? G : 8), CAP, Cfg::QF8, false><<<grid, 64 * kWavesPerWG, 0, s>>>(p);
@@ -1064,21 +1180,21 @@ hipError_t launch_rows_t(const AttnParams& p, hipStream_t s) {
 }
 
 template <typename QT, typename CT, int D, bool CAP>
-int row_waves_g(int G) {
+int row_waves_g(int G, bool sh) {
   switch (G) {
-    case 1: return RowCfg<QT, CT, D, 1, CAP>::resident() * kWavesPerWG;
-    case 2: return RowCfg<QT, CT, D, 2, CAP>::resident() * kWavesPerWG;
-    case 4: return RowCfg<QT, CT, D, 4, CAP>::resident() * kWavesPerWG;
-    case 8: return RowCfg<QT, CT, D, 8, CAP>::resident() * kWavesPerWG;
-    case 16: return RowCfg<QT, CT, D, 16, CAP>::resident() * kWavesPerWG;
+    case 1: return RowCfg<QT, CT, D, 1, CAP>::resident(sh) * kWavesPerWG;
+    case 2: return RowCfg<QT, CT, D, 2, CAP>::resident(sh) * kWavesPerWG;
+    case 4: return RowCfg<QT, CT, D, 4, CAP>::resident(sh) * kWavesPerWG;
+    case 8: return RowCfg<QT, CT, D, 8, CAP>::resident(sh) * kWavesPerWG;
+    case 16: return RowCfg<QT, CT, D, 16, CAP>::resident(sh) * kWavesPerWG;
     default: return 0;
   }
 }
 
 template <typename QT, typename CT, bool CAP>
-int row_waves_d(int D, int G) {
-  if (D == 64) return row_waves_g<QT, CT, 64, CAP>(G);
-  if (D == 128) return row_waves_g<QT, CT, 128, CAP>(G);
+int row_waves_d(int D, int G, bool sh) {
+  if (D == 64) return row_waves_g<QT, CT, 64, CAP>(G, sh);
+  if (D == 128) return row_waves_g<QT, CT, 128, CAP>(G, sh);
   return 0;
 }
 
@@ -1102,11 +1218,11 @@ hipError_t launch_rows_d(const AttnParams& p, hipStream_t s) {
 }
 
 template <bool CAP>
-int row_waves_c(rpa_dtype q_dt, rpa_dtype cache_dt, int D, int G) {
-  if (q_dt == RPA_F32 && cache_dt == RPA_F32) return row_waves_d<float, float, CAP>(D, G);
-  if (q_dt == RPA_BF16 && cache_dt == RPA_BF16) return row_waves_d<uint16_t, uint16_t, CAP>(D, G);
-  if (q_dt == RPA_BF16 && cache_dt == RPA_FP8_E4M3) return row_waves_d<uint16_t, uint8_t, CAP>(D, G);
-  if (q_dt == RPA_FP8_E4M3 && cache_dt == RPA_FP8_E4M3) return row_waves_d<uint8_t, uint8_t, CAP>(D, G);
+int row_waves_c(rpa_dtype q_dt, rpa_dtype cache_dt, int D, int G, bool sh) {
+  if (q_dt == RPA_F32 && cache_dt == RPA_F32) return row_waves_d<float, float, CAP>(D, G, sh);
+  if (q_dt == RPA_BF16 && cache_dt == RPA_BF16) return row_waves_d<uint16_t, uint16_t, CAP>(D, G, sh);
+  if (q_dt == RPA_BF16 && cache_dt == RPA_FP8_E4M3) return row_waves_d<uint16_t, uint8_t, CAP>(D, G, sh);
+  if (q_dt == RPA_FP8_E4M3 && cache_dt == RPA_FP8_E4M3) return row_waves_d<uint8_t, uint8_t, CAP>(D, G, sh);
   return 0;
 }
 
@@ -1123,8 +1239,9 @@ hipError_t launch_rows_c(const AttnParams& p, rpa_dtype q_dt, rpa_dtype cache_dt
 
 // The soft cap is a template choice of the row kernels, so that the per-logit
 // code of the uncapped kernels carries no test of it.
-int row_waves(rpa_dtype q_dt, rpa_dtype cache_dt, int D, int G, bool cap) {
-  return cap ? row_waves_c<true>(q_dt, cache_dt, D, G) : row_waves_c<false>(q_dt, cache_dt, D, G);
+int row_waves(rpa_dtype q_dt, rpa_dtype cache_dt, int D, int Dpad, int Hkv, int G, bool cap) {
+  const bool sh = row_shared_loads(Hkv, Dpad, D);
+  return cap ? row_waves_c<true>(q_dt, cache_dt, D, G, sh) : row_waves_c<false>(q_dt, cache_dt, D, G, sh);
 }
 
 hipError_t launch_rows(const AttnParams& p, rpa_dtype q_dt, rpa_dtype cache_dt, hipStream_t s) {

@@ -260,7 +260,8 @@ int prefill_min_q(const rpa_desc& d) {
 // row_chunks_max(waves, Hkv) chunks, which bounds the work lists.
 int row_waves_of(const rpa_desc& d, const rpa_options& o) {
   return row_waves((rpa_dtype)d.q_dtype, (rpa_dtype)d.cache_dtype, d.head_dim,
-                   d.num_q_heads / d.num_kv_heads, o.logits_soft_cap > 0.f);
+                   d.head_dim_padded, d.num_kv_heads, d.num_q_heads / d.num_kv_heads,
+                   o.logits_soft_cap > 0.f);
 }
 
 Workspace workspace_layout(const rpa_desc& d, const rpa_options& o) {

@@ -200,7 +200,11 @@ hipError_t launch_prep(const PlanParams& pp, const ScatterParams* sp, rpa_dtype 
                        rpa_dtype cache_dt, hipStream_t s);
 hipError_t launch_rows(const AttnParams& p, rpa_dtype q_dt, rpa_dtype cache_dt, hipStream_t s);
 // waves of the row kernel for these types and sizes that fit on the device at once
-int row_waves(rpa_dtype q_dt, rpa_dtype cache_dt, int D, int G, bool cap);
+int row_waves(rpa_dtype q_dt, rpa_dtype cache_dt, int D, int Dpad, int Hkv, int G, bool cap);
+// The MFMA row kernel's shared-load form: kv heads in groups of 4 whose rows
+// carry no lane padding (a workgroup's 4 waves then read 4 heads' K and V as
+// one contiguous run per token).
+inline bool row_shared_loads(int Hkv, int Dpad, int D) { return Hkv % 4 == 0 && Dpad == D; }
 hipError_t launch_merge(const AttnParams& p, rpa_dtype q_dt, hipStream_t s);
 hipError_t launch_prefill(const AttnParams& p, rpa_dtype q_dt, rpa_dtype cache_dt,
                           hipStream_t s);

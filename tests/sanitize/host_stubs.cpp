@@ -19,7 +19,7 @@ bool prefill_supported(const rpa_desc& d) {
   return d.q_dtype == RPA_BF16 && (d.cache_dtype == RPA_BF16 || d.cache_dtype == RPA_FP8_E4M3) &&
          (d.head_dim == 64 || d.head_dim == 128);
 }
-int row_waves(rpa_dtype, rpa_dtype, int, int, bool) { return 2048; }
+int row_waves(rpa_dtype, rpa_dtype, int, int, int, int, bool) { return 2048; }
 hipError_t launch_scatter(const ScatterParams& p, rpa_dtype, rpa_dtype, hipStream_t s) {
   return stub("scatter_kernel", (unsigned)p.T, 256, s);
 }
