@@ -641,6 +641,10 @@ def measure_forward(args, w, dev, flush, ceilings, with_graph=True):
                    "parallelism": "single GPU"},
         "roofline": roof,
         "kernels_ms": {k: v[1] / max(v[0], 1) for k, v in kstats.items()},
+        # batches with prefill tiles run the two attention kernels on two
+        # streams: a kernel's event span then also covers its wait for CUs
+        # that the other stream's kernel holds
+        "kernels_on_two_streams": bool(w.total_tokens > w.max_num_seqs),
     }
     if ceilings and pf_flops > 0 and "prefill" in kstats:
         # VALU roof of the prefill kernel: its transcendental count at the
