@@ -80,6 +80,15 @@ def work_counts(w, split=False):
     return kvb, flops
 
 
+def update_bytes(w):
+    """HBM bytes of the cache update: the valid new rows' K and V read in the
+    input dtype and written as whole cache rows (D elements, pad lanes zeroed
+    up to Dpad) in the cache dtype."""
+    n_tok = int(np.asarray(w.query_start_loc)[w.num_seqs])
+    in_sz, c_sz = ELEM[w.kv_in_dtype], ELEM[w.cache_dtype]
+    return n_tok * 2 * w.num_kv_heads * (w.head_dim * in_sz + w.head_dim_padded * c_sz)
+
+
 def cpu_info():
     """Host CPU model and logical CPU count (where the oracle baseline runs)."""
     model = ""
@@ -576,6 +585,25 @@ def measure_forward(args, w, dev, flush, ceilings, with_graph=True):
     step_ms, wall_ms = timed_steps(step, args.steps, flush)
     ms = float(np.mean(step_ms))
     nf_ms = back_to_back(step, args.steps)
+    # the two halves on their own: attention over the updated cache (no new
+    # keys / values), and the update by itself
+    def attn_step():
+        rpa.rpa_forward(w.queries, None, None, w.kv_cache, meta["kv_lens"],
+                        meta["block_tables"], meta["query_start_loc"], meta["distribution"],
+                        w.attention_sink, out=out, workspace=workspace, **opts)
+
+    def update_step():
+        rpa.rpa_update_kv_cache(w.keys, w.values, w.kv_cache, meta["kv_lens"],
+                                meta["block_tables"], meta["query_start_loc"],
+                                meta["distribution"], k_scale=w.k_scale, v_scale=w.v_scale,
+                                queries_dtype=w.queries.dtype)
+
+    progress(f"{w.name}: attention-only and update-only steps")
+    for _ in range(max(args.warmup, 1)):
+        attn_step()
+        update_step()
+    ao_ms = float(np.mean(timed_steps(attn_step, args.steps, flush)[0]))
+    up_ms = float(np.mean(timed_steps(update_step, args.steps, flush)[0]))
     # per-kernel times: a second pass with the library's launch events
     rpa.profile_enable(True)
     rpa.profile_read()
@@ -645,6 +673,10 @@ def measure_forward(args, w, dev, flush, ceilings, with_graph=True):
         # streams: a kernel's event span then also covers its wait for CUs
         # that the other stream's kernel holds
         "kernels_on_two_streams": bool(w.total_tokens > w.max_num_seqs),
+        "attention_only": {"ms_per_step": ao_ms, "value": work / (ao_ms * 1e-3) / scale,
+                           "unit": unit},
+        "update_only": {"ms_per_step": up_ms, "bytes": update_bytes(w),
+                        "GB/s": update_bytes(w) / (up_ms * 1e-3) / 1e9},
     }
     if ceilings and pf_flops > 0 and "prefill" in kstats:
         # VALU roof of the prefill kernel: its transcendental count at the

@@ -82,3 +82,14 @@ def test_cpu_baseline_fields():
     assert f["value"] > 0 and f["rows"] >= 1
     info = bench.cpu_info()
     assert info["cpu_count"] >= 1
+
+
+def test_update_bytes_closed_form():
+    # tiny batch: 7 new tokens, 2 kv heads, D = Dpad = 64, f32 in and out:
+    # K and V read (64 x 4 bytes each) and written (64 x 4 bytes each)
+    w = W.make("tiny_fp32")
+    assert bench.update_bytes(w) == 7 * 2 * 2 * (64 * 4 + 64 * 4)
+    # fp8 batch: bf16 keys / values in, e4m3 rows out
+    f = W.make("fp8_full", small=True)
+    n = int(np.asarray(f.query_start_loc)[f.num_seqs])
+    assert bench.update_bytes(f) == n * 2 * 8 * (64 * 2 + 64 * 1)
