@@ -624,7 +624,8 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
 
 // ---------------------------------------------------------------------------
 // Row kernel for large GQA groups (G = 8 or 16 q heads per kv head, bf16
-// queries, bf16 or e4m3 cache) on v_mfma_f32_16x16x32_bf16.  With G >= 8 the
+// queries or e4m3 ones widened exactly to bf16, bf16 or e4m3 cache) on
+// v_mfma_f32_16x16x32_bf16.  With G >= 8 the
 // dot products of the VALU kernel above outweigh the HBM time; here they run
 // on the matrix cores and the wave keeps up with its loads.  Same plan, work
 // items, split partials and output as the VALU kernel.
