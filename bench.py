@@ -210,11 +210,17 @@ KERNEL_SYMBOL = {"decode": "row_kernel", "prefill": "prefill_kernel"}
 
 
 def source_hash(kernel):
+    """Hash of the kernel's sources with comments and blank space removed, so
+    that a counter summary stays valid across comment-only edits."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "ragged_paged_kv_scatter_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "ragged_paged_kv_scatter_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
