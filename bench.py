@@ -604,12 +604,14 @@ def measure_forward(args, w, dev, flush, ceilings, with_graph=True):
                                 meta["distribution"], k_scale=w.k_scale, v_scale=w.v_scale,
                                 queries_dtype=w.queries.dtype)
 
-    progress(f"{w.name}: attention-only and update-only steps")
-    for _ in range(max(args.warmup, 1)):
-        attn_step()
-        update_step()
-    ao_ms = float(np.mean(timed_steps(attn_step, args.steps, flush)[0]))
-    up_ms = float(np.mean(timed_steps(update_step, args.steps, flush)[0]))
+    ao_ms = up_ms = None
+    if not getattr(args, "no_halves", False):
+        progress(f"{w.name}: attention-only and update-only steps")
+        for _ in range(max(args.warmup, 1)):
+            attn_step()
+            update_step()
+        ao_ms = float(np.mean(timed_steps(attn_step, args.steps, flush)[0]))
+        up_ms = float(np.mean(timed_steps(update_step, args.steps, flush)[0]))
     # per-kernel times: a second pass with the library's launch events
     rpa.profile_enable(True)
     rpa.profile_read()
@@ -679,11 +681,12 @@ def measure_forward(args, w, dev, flush, ceilings, with_graph=True):
         # streams: a kernel's event span then also covers its wait for CUs
         # that the other stream's kernel holds
         "kernels_on_two_streams": bool(w.total_tokens > w.max_num_seqs),
-        "attention_only": {"ms_per_step": ao_ms, "value": work / (ao_ms * 1e-3) / scale,
-                           "unit": unit},
-        "update_only": {"ms_per_step": up_ms, "bytes": update_bytes(w),
-                        "GB/s": update_bytes(w) / (up_ms * 1e-3) / 1e9},
     }
+    if ao_ms is not None:
+        res["attention_only"] = {"ms_per_step": ao_ms, "value": work / (ao_ms * 1e-3) / scale,
+                                 "unit": unit}
+        res["update_only"] = {"ms_per_step": up_ms, "bytes": update_bytes(w),
+                              "GB/s": update_bytes(w) / (up_ms * 1e-3) / 1e9}
     if ceilings and pf_flops > 0 and "prefill" in kstats:
         # VALU roof of the prefill kernel: its transcendental count at the
         # measured issue rates (one exp2 per visible logit; with a soft cap
@@ -730,6 +733,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true",
                     help="default workload only: skip the nested long-prefill measurement")
     ap.add_argument("--no-probes", action="store_true", help="skip the probe ceilings")
+    ap.add_argument("--no-halves", action="store_true",
+                    help="skip the attention-only and update-only timings (counter runs: "
+                         "every dispatch of a kernel is then one of the whole step)")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle time per CPU-baseline run (two runs per workload)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
