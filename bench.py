@@ -209,9 +209,31 @@ KERNEL_SOURCES = {  # kernel -> sources whose hash identifies a counter summary
 KERNEL_SYMBOL = {"decode": "row_kernel", "prefill": "prefill_kernel"}
 
 
+def strip_timeline(text):
+    """The source without the wave-timeline instrumentation: the blocks under
+    `#ifdef RPA_WAVE_TIMELINE` (to their matching #endif) and the RPA_TL_*
+    statements, which expand to nothing unless that macro is defined."""
+    import re
+    out, depth = [], 0
+    for line in text.split("\n"):
+        d = line.strip()
+        if depth:
+            if d.startswith("#if"):
+                depth += 1
+            elif d.startswith("#endif"):
+                depth -= 1
+            continue
+        if d == "#ifdef RPA_WAVE_TIMELINE":
+            depth = 1
+            continue
+        out.append(line)
+    return re.sub(r"RPA_TL_(BEGIN|STEP|END)\([^()]*\);", " ", "\n".join(out))
+
+
 def source_hash(kernel):
-    """Hash of the kernel's sources with comments and blank space removed, so
-    that a counter summary stays valid across comment-only edits."""
+    """Hash of the kernel's sources with comments, blank space and the
+    wave-timeline instrumentation removed, so that a counter summary stays
+    valid across edits that leave the product build's code unchanged."""
     import hashlib
     import re
     h = hashlib.sha256()
@@ -220,6 +242,7 @@ def source_hash(kernel):
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
+        text = strip_timeline(text)
         h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
@@ -486,6 +509,81 @@ def back_to_back(step, steps):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
+def timeline_summary(a):
+    """Per-wave stamps (rows of start, first step, end, steps << 32 | XCC_ID
+    << 16 | HW_ID; 100 MHz ticks) -> where the waves of one launch start and
+    end, how each CU's workgroups end, and the mean end per XCD (us)."""
+    a = a[a[:, 0] > 0]
+    if len(a) == 0:
+        return {"waves": 0}
+    t0, t1, t2 = (a[:, i].astype(np.int64) for i in range(3))
+    base = int(t0.min())
+    steps = (a[:, 3] >> 32).astype(np.int64)
+    hw = (a[:, 3] & 0xFFFF).astype(np.int64)
+    xcc = ((a[:, 3] >> 16) & 0xF).astype(np.int64)
+    # HW_ID: wave slot 3:0, SIMD 5:4, CU 11:8, shader array 12, shader engine 15:13
+    cu = xcc * 1000 + ((hw >> 13) & 7) * 100 + ((hw >> 12) & 1) * 16 + ((hw >> 8) & 0xF)
+    slot = hw & 0xF
+    us = lambda v: float(v) / 100.0
+    q = lambda v: [round(us(np.percentile(v, x)), 2) for x in (0, 10, 50, 90, 100)]
+    end = t2 - base
+    cu_last, cu_spread = [], []
+    for c in np.unique(cu):
+        m = cu == c
+        cu_last.append(end[m].max())
+        by_slot = [end[m & (slot == s)].mean() for s in np.unique(slot[m])]
+        cu_spread.append(max(by_slot) - min(by_slot))
+    return {
+        "waves": int(len(a)), "cus": int(len(cu_last)),
+        "start_us": q(t0 - base), "first_step_end_us": q(t1 - base), "end_us": q(end),
+        "steps": [int(steps.min()), int(np.median(steps)), int(steps.max())],
+        "cu_last_end_us": q(np.array(cu_last)), "cu_mean_last_end_us": round(us(np.mean(cu_last)), 2),
+        "cu_slot_spread_us": q(np.array(cu_spread)),
+        "xcd_mean_end_us": [round(us(end[xcc == x].mean()), 1) for x in range(8) if (xcc == x).any()],
+    }
+
+
+def bench_timeline(args, w, dev):
+    """The row kernels' per-wave clock stamps (librpa_timeline.so) over a few
+    flushed steps of the workload: one JSON line per launch."""
+    import ctypes
+
+    import torch
+
+    import ragged_paged_kv_scatter_amd as rpa
+    from ragged_paged_kv_scatter_amd import _lib
+
+    lib = _lib.load()
+    words = 8192 * 4
+    buf = (ctypes.c_ulonglong * words)()
+    meta = {k: torch.from_numpy(np.ascontiguousarray(getattr(w, k))).to(dev)
+            for k in ("kv_lens", "block_tables", "query_start_loc", "distribution")}
+    out = torch.empty(w.queries.shape, dtype=rpa.out_dtype_for(w.queries.dtype), device=dev)
+    opts = w.options()
+    flush = Flusher(dev)
+
+    def step():
+        rpa.rpa_forward(w.queries, w.keys, w.values, w.kv_cache, meta["kv_lens"],
+                        meta["block_tables"], meta["query_start_loc"], meta["distribution"],
+                        w.attention_sink, out=out, **opts)
+
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(min(args.steps, 5)):
+        if lib.rpa_timeline_clear() != 0:
+            raise SystemExit("rpa_timeline_clear failed")
+        flush()
+        torch.cuda.synchronize()
+        step()
+        torch.cuda.synchronize()
+        if lib.rpa_timeline_read(buf, words) != 0:
+            raise SystemExit("rpa_timeline_read failed")
+        a = np.frombuffer(buf, dtype=np.uint64).reshape(-1, 4).copy()
+        print(json.dumps({"metric": "row kernel wave timeline", "workload": w.name, "launch": rep,
+                          **timeline_summary(a)}), flush=True)
+
+
 def probe_ceilings(dev):
     """Measured ceilings of this GPU from librpa_probes.so: HBM streaming read
     and copy (GB/s), dense bf16 MFMA (TFLOP/s) with the shader clock it runs
@@ -720,13 +818,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_bf16")
     ap.add_argument("--op", default="forward",
-                    choices=["forward", "reshape_and_cache", "copy_blocks", "probes"],
+                    choices=["forward", "reshape_and_cache", "copy_blocks", "probes", "timeline"],
                     help="forward: the whole step (default; with the default workload the line "
                          "also carries the long-prefill measurement); reshape_and_cache: the "
                          "update's slot-mapping form into split K/V caches, at the workload's "
                          "token count; copy_blocks: 2048 block copies in 8192-block split "
                          "caches of the workload's block shape; probes: the measured ceilings "
-                         "(HBM read / copy, bf16 MFMA and shader clock, VALU issue rates)")
+                         "(HBM read / copy, bf16 MFMA and shader clock, VALU issue rates); "
+                         "timeline: the row kernels' per-wave clock stamps over a few steps "
+                         "(needs librpa_timeline.so)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip timing the step replayed from a captured HIP graph")
@@ -753,6 +853,12 @@ def main():
               "collective and shards by kv head or by sequence with no exchange.", file=sys.stderr)
         sys.exit(2)
 
+    if args.op == "timeline":
+        # the measurement build, loaded in place of librpa.so
+        from ragged_paged_kv_scatter_amd import _lib
+        from ragged_paged_kv_scatter_amd.build import TIMELINE_LIB
+        _lib.LIB_PATH = TIMELINE_LIB
+
     import torch
 
     from ragged_paged_kv_scatter_amd import workloads as W
@@ -771,6 +877,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.op == "timeline":
+        bench_timeline(args, W.make(args.workload, device=dev), dev)
+        return
     if args.op in ("reshape_and_cache", "copy_blocks"):
         w = W.make(args.workload, device=dev)
         if args.op == "reshape_and_cache":

@@ -1,5 +1,6 @@
 """Builds librpa.so (the HIP kernels and the C ABI) and librpa_probes.so (the
-measurement probes) in-tree with hipcc for gfx950.
+measurement probes) in-tree with hipcc for gfx950; on request (--timeline)
+also the measurement build librpa_timeline.so.
 
 Run as ``python -m ragged_paged_kv_scatter_amd.build``, or call :func:`build`.
 Every call recompiles."""
@@ -18,6 +19,9 @@ SOURCES = ["rpa_api.cpp", "scatter.hip", "plan.hip", "decode.hip", "prefill.hip"
 # measurement probes (include/rpa_probes.h), a library of their own
 PROBES_LIB = os.path.join(HERE, "librpa_probes.so")
 PROBES_SOURCES = ["probes.hip"]
+# measurement build of librpa.so with the row kernels' per-wave clock stamps
+# (RPA_WAVE_TIMELINE; read by bench.py --op timeline), built on request only
+TIMELINE_LIB = os.path.join(HERE, "librpa_timeline.so")
 ARCH = os.environ.get("RPA_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
@@ -36,12 +40,13 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def _compile(sources, obj_dir, jobs, verbose):
+def _compile(sources, obj_dir, jobs, verbose, defines=()):
     procs, objs = [], []
     for src in sources:
         obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc(), *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src),
+               "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
         procs.append((src, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE,
@@ -83,6 +88,21 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     return LIB
 
 
+def build_timeline(verbose: bool = False, jobs: int = 8) -> str:
+    """Compile and link librpa_timeline.so: librpa.so with the row kernels'
+    per-wave clock stamps (a measurement build; the product is librpa.so)."""
+    obj_dir = os.path.join(HERE, "_build", "timeline")
+    os.makedirs(obj_dir, exist_ok=True)
+    t0 = time.time()
+    _link(_compile(SOURCES, obj_dir, jobs, verbose, defines=("RPA_WAVE_TIMELINE",)), TIMELINE_LIB)
+    if verbose:
+        print(f"built {TIMELINE_LIB} in {time.time() - t0:.1f}s")
+    return TIMELINE_LIB
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--timeline" in sys.argv[1:]:
+        build_timeline(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)

@@ -34,6 +34,42 @@
 namespace rpa {
 namespace {
 
+// Per-wave clock stamps of the row kernels, compiled only into the
+// measurement build (RPA_WAVE_TIMELINE, librpa_timeline.so): for wave w of
+// a launch, its start, the end of its first step and its end on the 100 MHz
+// constant clock, its step count and its CU (HW_ID) and XCD (XCC_ID).  They
+// show how the waves of a launch share the chip; the library never reads
+// them.
+#ifdef RPA_WAVE_TIMELINE
+constexpr int kTimelineWaves = 8192;
+__device__ unsigned long long g_timeline[kTimelineWaves * 4];
+__device__ __forceinline__ void timeline_put(long long w, unsigned long long t0,
+                                             unsigned long long t1, int steps) {
+  const unsigned long long t2 = __builtin_amdgcn_s_memrealtime();
+  const unsigned hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);    // HW_ID, 32 bits
+  const unsigned xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20);  // XCC_ID, 32 bits
+  if ((threadIdx.x & 63) == 0 && w >= 0 && w < kTimelineWaves) {
+    g_timeline[w * 4 + 0] = t0;
+    g_timeline[w * 4 + 1] = t1;
+    g_timeline[w * 4 + 2] = t2;
+    g_timeline[w * 4 + 3] = ((unsigned long long)steps << 32) | ((xcc & 0xFu) << 16) | (hw & 0xFFFFu);
+  }
+}
+#define RPA_TL_BEGIN()                                                      \
+  const unsigned long long tl_t0 = __builtin_amdgcn_s_memrealtime();        \
+  unsigned long long tl_t1 = 0;                                             \
+  int tl_steps = 0
+#define RPA_TL_STEP()                                                       \
+  do {                                                                      \
+    if (tl_steps++ == 0) tl_t1 = __builtin_amdgcn_s_memrealtime();         \
+  } while (0)
+#define RPA_TL_END(w) timeline_put((w), tl_t0, tl_t1, tl_steps)
+#else
+#define RPA_TL_BEGIN() static_assert(true, "")
+#define RPA_TL_STEP() static_assert(true, "")
+#define RPA_TL_END(w) static_assert(true, "")
+#endif
+
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -265,6 +301,7 @@ __device__ __forceinline__ void store_slice(QT* o, long long base, const float* 
 // exactly to bf16 on load); the output is QT, or bf16 for e4m3 queries.
 template <typename QT, typename CT, int D, int G, int EPL, int NR, bool CAP>
 __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
+  RPA_TL_BEGIN();
   using OT = std::conditional_t<sizeof(QT) == 1, uint16_t, QT>;
   constexpr bool F32 = sizeof(CT) == 4;
   constexpr int LPT = D / EPL;          // lanes per token
@@ -551,8 +588,10 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
       for (int k0 = c_lo; k0 < c_hi; k0 += 2 * STEP) {
         load_step(cur, c_hi, pw0, page_reg, k0 + STEP, kB, vB);
         compute_step(k0, c_hi, kA, vA);
+        RPA_TL_STEP();
         load_step(cur, c_hi, pw0, page_reg, k0 + 2 * STEP, kA, vA);
         compute_step(k0 + STEP, c_hi, kB, vB);
+        RPA_TL_STEP();
       }
       if (c_hi >= cur.hi) break;
       c_lo = c_hi;
@@ -620,6 +659,7 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void row_kernel(AttnParams p) {
     idx_n = idx_nn;
     if constexpr (!kLean) load_step(cur, chunk_end(cur, cur.lo), pw0, page_reg, cur.lo, kA, vA);
   }
+  RPA_TL_END(ch);
 }
 
 // ---------------------------------------------------------------------------
@@ -711,6 +751,7 @@ template <typename CT, int D, int G, bool CAP, bool QF8, bool SH>
 __global__ __launch_bounds__(64 * kWavesPerWG)
 __attribute__((amdgpu_waves_per_eu(mfma_row_min_waves<CT, D, SH>()))) void mfma_row_kernel(AttnParams p) {
   constexpr int NBUF = mfma_row_nbuf<CT, D, SH>();
+  RPA_TL_BEGIN();
   using Cfg = MfCfg<CT, D>;
   constexpr int ESZ = Cfg::ESZ, E = Cfg::E, LPTK = Cfg::LPTK, TPI = Cfg::TPI, NLI = Cfg::NLI,
                 NMQ = Cfg::NMQ, NMP = Cfg::NMP, LRK = Cfg::LRK, LRV = Cfg::LRV;
@@ -1072,6 +1113,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_row_min_waves<CT, D, SH>()))) void mfma_
       stage_buf(buf);
       issue(buf);
     }
+    RPA_TL_STEP();
     advance();
     keys_done += 32;
     wave_priority(3 - min(3, (4 * keys_done) / chunk_keys));
@@ -1100,6 +1142,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_row_min_waves<CT, D, SH>()))) void mfma_
       if (!step(b1)) break;
     }
   }
+  RPA_TL_END(ch);
 }
 
 // Stand-alone merge of the split partials (when no prefill kernel runs after
@@ -1283,3 +1326,18 @@ hipError_t launch_merge(const AttnParams& p, rpa_dtype q_dt, hipStream_t s) {
 }
 
 }  // namespace rpa
+
+#ifdef RPA_WAVE_TIMELINE
+// The row kernels' per-wave stamps of the measurement build: n words of
+// (start, first step, end, steps << 32 | XCC_ID << 16 | HW_ID) per wave.
+extern "C" int rpa_timeline_read(unsigned long long* host, int n) {
+  if (n > rpa::kTimelineWaves * 4) n = rpa::kTimelineWaves * 4;
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(rpa::g_timeline),
+                                  (size_t)n * sizeof(unsigned long long), 0, hipMemcpyDeviceToHost);
+}
+extern "C" int rpa_timeline_clear(void) {
+  static unsigned long long zero[rpa::kTimelineWaves * 4];
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(rpa::g_timeline), zero, sizeof(zero), 0,
+                                hipMemcpyHostToDevice);
+}
+#endif

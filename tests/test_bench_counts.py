@@ -93,3 +93,34 @@ def test_update_bytes_closed_form():
     f = W.make("fp8_full", small=True)
     n = int(np.asarray(f.query_start_loc)[f.num_seqs])
     assert bench.update_bytes(f) == n * 2 * 8 * (64 * 2 + 64 * 1)
+
+
+def test_timeline_summary_by_hand():
+    # two CUs (CU ids 0 and 1 of XCD 0), two workgroup slots each; stamps in
+    # 100 MHz ticks: every wave starts at 1000, ends 100 us (10000 ticks) or
+    # 200 us later depending on its slot
+    rows = []
+    for cu in (0, 1):
+        for slot in (0, 1):
+            for _ in range(4):
+                hw = (cu << 8) | slot
+                end = 1000 + (10000 if slot == 0 else 20000) + cu * 100
+                rows.append([1000, 1500, end, (5 << 32) | (0 << 16) | hw])
+    rows.append([0, 0, 0, 0])                      # an empty record is skipped
+    s = bench.timeline_summary(np.array(rows, dtype=np.uint64))
+    assert s["waves"] == 16 and s["cus"] == 2
+    assert s["start_us"] == [0.0] * 5
+    assert s["end_us"][0] == 100.0 and s["end_us"][-1] == 201.0
+    assert s["cu_last_end_us"][0] == 200.0 and s["cu_last_end_us"][-1] == 201.0
+    assert s["cu_slot_spread_us"] == [100.0] * 5
+    assert s["steps"] == [5, 5, 5]
+    assert s["xcd_mean_end_us"] == [150.5]
+
+
+def test_strip_timeline_removes_only_the_instrumentation():
+    src = ("int a;\n#ifdef RPA_WAVE_TIMELINE\n#if X\nint b;\n#endif\nint c;\n#else\n"
+           "#define RPA_TL_STEP()\n#endif\nvoid f() {\n  RPA_TL_BEGIN();\n  g();\n"
+           "  RPA_TL_END(ch);\n}\n#ifdef OTHER\nint d;\n#endif\n")
+    out = " ".join(bench.strip_timeline(src).split())
+    assert out == "int a; void f() { g(); } #ifdef OTHER int d; #endif"
+
