@@ -635,10 +635,12 @@ int forward_impl(const rpa_desc* desc, const rpa_options* opts, const void* quer
     prof_end(s);
     if (e != hipSuccess) return hip_fail(e);
   } else {
-    // The prefill tiles on the side stream, the rows and then the merge of
-    // their splits on the caller's stream; the caller's stream waits for
+    // The rows and then the merge of their splits on the caller's stream,
+    // the prefill tiles on the side stream; the caller's stream waits for
     // both.  The planner's co_run flag sizes both kernels to share the CUs
-    // when the batch has enough of each kind of work.
+    // when the batch has enough of each kind of work.  The rows go first so
+    // that their workgroups take CU slots before the persistent prefill grid
+    // does: a row kernel that queues behind it starts late.
     std::unique_lock<std::mutex> lk(g_side_mu, std::defer_lock);
     SideStream dry_side;
     SideStream* ss = &dry_side;
@@ -650,15 +652,15 @@ int forward_impl(const rpa_desc* desc, const rpa_options* opts, const void* quer
         return hip_fail(e);
     }
     ap.fuse_merge = 0;
+    prof_begin("decode", s);
+    e = launch_rows(ap, qd, cd, s);
+    prof_end(s);
+    if (e != hipSuccess) return hip_fail(e);
     prof_begin("prefill", ss->s);
     e = launch_prefill(ap, qd, cd, ss->s);
     prof_end(ss->s);
     if (e != hipSuccess) return hip_fail(e);
     if (!dry && (e = hipEventRecord(ss->join, ss->s)) != hipSuccess) return hip_fail(e);
-    prof_begin("decode", s);
-    e = launch_rows(ap, qd, cd, s);
-    prof_end(s);
-    if (e != hipSuccess) return hip_fail(e);
     prof_begin("merge", s);
     e = launch_merge(ap, qd, s);
     prof_end(s);

@@ -277,7 +277,7 @@ def test_trace_format_lines(lib, kind):
     """rpa_trace_format runs rpa_forward's host path dry: the forward,
     workspace and stream lines, then one launch line per kernel in launch
     order (decode-only: plan, rows, prefill kernel merging the splits; with
-    prefill tiles: plan, prefill on the side stream, rows, merge; f32: plan,
+    prefill tiles: plan, rows, prefill on the side stream, merge; f32: plan,
     rows, merge), and the workspace size rpa_workspace_bytes reports."""
     import ragged_paged_kv_scatter_amd as rpa
     if kind == "f32":
@@ -292,7 +292,7 @@ def test_trace_format_lines(lib, kind):
             order = ["prep_kernel", "row_kernel", "prefill_kernel"]
         else:
             d.total_tokens, d.max_num_seqs = 2176, 132
-            order = ["prep_kernel", "prefill_kernel", "row_kernel", "merge_kernel"]
+            order = ["prep_kernel", "row_kernel", "prefill_kernel", "merge_kernel"]
     o = good_opts()
     text = rpa.rpa_trace_format(d, o, with_update=True)
     lines = text.strip().split("\n")
