@@ -227,7 +227,7 @@ def strip_timeline(text):
             depth = 1
             continue
         out.append(line)
-    return re.sub(r"RPA_TL_(BEGIN|STEP|END)\([^()]*\);", " ", "\n".join(out))
+    return re.sub(r"RPA_TL_\w+\([^()]*\);", " ", "\n".join(out))
 
 
 def source_hash(kernel):
@@ -543,9 +543,36 @@ def timeline_summary(a):
     }
 
 
+PF_PHASES = ("issue", "qk", "pv", "tail")
+
+
+def pf_timeline_summary(a):
+    """Per-wave prefill kernel counts (rows of total, copy-wait and
+    barrier-wait shader clocks, steps, then the issue / q.k / p.v / tail
+    parts of the steps) -> how the waves' time splits: the means over waves
+    of each share of the wave's time and of the clocks per pipeline step."""
+    a = a[a[:, 3] > 0].astype(np.float64)
+    if len(a) == 0:
+        return {"waves": 0}
+    tot, vm, bar, steps = a[:, 0], a[:, 1], a[:, 2], a[:, 3]
+    out = {
+        "waves": int(len(a)), "steps": [int(steps.min()), int(np.median(steps)), int(steps.max())],
+        "total_clk": [round(float(np.percentile(tot, x))) for x in (0, 50, 100)],
+        "copy_wait_share": round(float((vm / tot).mean()), 4),
+        "barrier_wait_share": round(float((bar / tot).mean()), 4),
+        "clk_per_step": round(float((tot / steps).mean()), 1),
+        "copy_wait_clk_per_step": round(float((vm / steps).mean()), 1),
+        "barrier_wait_clk_per_step": round(float((bar / steps).mean()), 1),
+    }
+    for i, name in enumerate(PF_PHASES):
+        out[f"{name}_clk_per_step"] = round(float((a[:, 4 + i] / steps).mean()), 1)
+    return out
+
+
 def bench_timeline(args, w, dev):
-    """The row kernels' per-wave clock stamps (librpa_timeline.so) over a few
-    flushed steps of the workload: one JSON line per launch."""
+    """The row kernels' per-wave clock stamps and the prefill kernel's per-wave
+    wait counts (librpa_timeline.so) over a few flushed steps of the workload:
+    one JSON line per launch."""
     import ctypes
 
     import torch
@@ -554,8 +581,9 @@ def bench_timeline(args, w, dev):
     from ragged_paged_kv_scatter_amd import _lib
 
     lib = _lib.load()
-    words = 8192 * 4
+    words, pwords = 8192 * 4, 8192 * 8
     buf = (ctypes.c_ulonglong * words)()
+    pbuf = (ctypes.c_ulonglong * pwords)()
     meta = {k: torch.from_numpy(np.ascontiguousarray(getattr(w, k))).to(dev)
             for k in ("kv_lens", "block_tables", "query_start_loc", "distribution")}
     out = torch.empty(w.queries.shape, dtype=rpa.out_dtype_for(w.queries.dtype), device=dev)
@@ -571,8 +599,8 @@ def bench_timeline(args, w, dev):
         step()
     torch.cuda.synchronize()
     for rep in range(min(args.steps, 5)):
-        if lib.rpa_timeline_clear() != 0:
-            raise SystemExit("rpa_timeline_clear failed")
+        if lib.rpa_timeline_clear() != 0 or lib.rpa_pf_timeline_clear() != 0:
+            raise SystemExit("timeline clear failed")
         flush()
         torch.cuda.synchronize()
         step()
@@ -580,14 +608,21 @@ def bench_timeline(args, w, dev):
         if lib.rpa_timeline_read(buf, words) != 0:
             raise SystemExit("rpa_timeline_read failed")
         a = np.frombuffer(buf, dtype=np.uint64).reshape(-1, 4).copy()
+        if lib.rpa_pf_timeline_read(pbuf, pwords) != 0:
+            raise SystemExit("rpa_pf_timeline_read failed")
+        b = np.frombuffer(pbuf, dtype=np.uint64).reshape(-1, 8).copy()
         print(json.dumps({"metric": "row kernel wave timeline", "workload": w.name, "launch": rep,
-                          **timeline_summary(a)}), flush=True)
+                          **timeline_summary(a), "prefill": pf_timeline_summary(b)}), flush=True)
 
 
-def probe_ceilings(dev):
+def probe_ceilings(dev, full=False):
     """Measured ceilings of this GPU from librpa_probes.so: HBM streaming read
     and copy (GB/s), dense bf16 MFMA (TFLOP/s) with the shader clock it runs
-    at, and v_exp_f32 / v_rcp_f32 / v_fma_f32 issue rates (lane-ops/s)."""
+    at, v_exp_f32 / v_rcp_f32 / v_fma_f32 issue rates (lane-ops/s), LDS read,
+    transposed read and write rates and the L2 -> LDS copy rate (bytes per CU
+    and clock, and TB/s over the chip).  full (bench.py --op probes) adds the
+    MFMA rates beside VALU work and fed from LDS, and LDS reads beside
+    copies."""
     import ctypes
 
     import torch
@@ -644,6 +679,35 @@ def probe_ceilings(dev):
     c = clocks.view(-1, 2).double()
     ok = c[:, 1] > 0
     out["shader_clock_ghz_mfma"] = float((c[ok, 0] / c[ok, 1]).mean() * 0.1)
+    # MFMA beside 0..4 VALU pairs per MFMA (fma + exp, or two fma), at 2
+    # waves per SIMD (the prefill kernel's residency) and at 1, where a wave's
+    # VALU work can only run under its own MFMAs
+    for per_cu in ((2, 1) if full else ()):
+        xb = cus * per_cu
+        xflops = xb * 4 * 4 * iters * 32 * 32 * 16 * 2
+        for exp_ in (1, 0):
+            for nv in (0, 1, 2, 4):
+                if nv == 0 and exp_ == 0:
+                    continue
+                ms = time_it(lambda: _probes.check(lib.rpa_probe_mix(
+                    ctypes.c_void_p(msink.data_ptr()), ctypes.c_void_p(clocks.data_ptr()), nv,
+                    exp_, iters, xb, stream), "mix probe"))
+                tag = f"mfma_w{4 * per_cu}_with_{nv}_{'fma_exp' if exp_ else 'fma_fma'}"
+                out[f"{tag}_tflops"] = xflops / (ms * 1e-3) / 1e12
+                c = clocks.view(-1, 2)[: xb * 4].double()
+                ok = c[:, 1] > 0
+                out[f"{tag}_clock_ghz"] = float((c[ok, 0] / c[ok, 1]).mean() * 0.1)
+    # MFMA fed from LDS in the prefill kernel's patterns, 2 workgroups per CU
+    for name, mode in (_probes.LDS_MFMA_MODES.items() if full else ()):
+        liters = iters // 4
+        ms = time_it(lambda: _probes.check(lib.rpa_probe_lds_mfma(
+            ctypes.c_void_p(msink.data_ptr()), ctypes.c_void_p(clocks.data_ptr()), mode, liters,
+            mblocks, stream), "lds mfma probe"))
+        lflops = mblocks * 4 * 16 * liters * 32 * 32 * 16 * 2
+        out[f"mfma_{name}_tflops"] = lflops / (ms * 1e-3) / 1e12
+        c = clocks.view(-1, 2)[: mblocks * 4].double()
+        ok = c[:, 1] > 0
+        out[f"mfma_{name}_clock_ghz"] = float((c[ok, 0] / c[ok, 1]).mean() * 0.1)
     # VALU: 8 workgroups (32 waves) per CU, 8 chains per lane
     vblocks, viters = cus * 8, 4096
     vsink = torch.empty(vblocks * 256 * 8, dtype=torch.float32, device=dev)
@@ -651,6 +715,60 @@ def probe_ceilings(dev):
         ms = time_it(lambda: _probes.check(lib.rpa_probe_valu(
             ctypes.c_void_p(vsink.data_ptr()), op, viters, vblocks, stream), "valu probe"))
         out[f"{name}_per_s"] = vblocks * 256 * 8 * viters / (ms * 1e-3)
+
+    def clock_hz(clk):
+        c = clk.view(-1, 2).double()
+        ok = c[:, 1] > 0
+        return float((c[ok, 0] / c[ok, 1]).mean()) * 1e8
+
+    # LDS: 2 workgroups (8 waves, the prefill kernel's residency) and 4 per CU;
+    # bytes per CU and shader clock, and the chip's total rate
+    for per_cu in (2, 4):
+        lblocks, liters = cus * per_cu, 4000
+        lsink = torch.empty(lblocks * 256, dtype=torch.int32, device=dev)
+        lclk = torch.zeros(lblocks * 4 * 2, dtype=torch.int64, device=dev)
+        for name, (op, nb) in _probes.LDS_OPS.items():
+            ms = time_it(lambda: _probes.check(lib.rpa_probe_lds(
+                ctypes.c_void_p(lsink.data_ptr()), ctypes.c_void_p(lclk.data_ptr()), op, liters,
+                lblocks, stream), "lds probe"))
+            nbytes_l = lblocks * 4 * liters * 8 * nb
+            out[f"lds_{name}_w{4 * per_cu}_bytes_per_cu_clk"] = (
+                nbytes_l / (ms * 1e-3) / (clock_hz(lclk) * cus))
+            out[f"lds_{name}_w{4 * per_cu}_tbs"] = nbytes_l / (ms * 1e-3) / 1e12
+    # global -> LDS copies from a 2 MiB window (L2-resident on every XCD), at
+    # the prefill kernel's 8 waves per CU and at 16
+    window = 2 << 20
+    dsrc = torch.ones(window // 4, dtype=torch.int32, device=dev)
+    for per_cu in (2, 4):
+        dblocks, diters = cus * per_cu, 2000
+        dsink = torch.empty(dblocks * 256, dtype=torch.int32, device=dev)
+        dclk = torch.zeros(dblocks * 4 * 2, dtype=torch.int64, device=dev)
+        ms = time_it(lambda: _probes.check(lib.rpa_probe_dma(
+            ctypes.c_void_p(dsrc.data_ptr()), window, ctypes.c_void_p(dsink.data_ptr()),
+            ctypes.c_void_p(dclk.data_ptr()), diters, dblocks, stream), "dma probe"))
+        nbytes_d = dblocks * 4 * diters * 8192
+        out[f"l2_to_lds_w{4 * per_cu}_bytes_per_cu_clk"] = (
+            nbytes_d / (ms * 1e-3) / (clock_hz(dclk) * cus))
+        out[f"l2_to_lds_w{4 * per_cu}_tbs"] = nbytes_d / (ms * 1e-3) / 1e12
+    # LDS reads (2 waves per workgroup) beside copies (the other 2), 2
+    # workgroups per CU, 2 ms per run: rates of each alone and side by side,
+    # bytes per CU and shader clock
+    xblocks, ticks = cus * 2, 200000
+    xsink = torch.empty(xblocks * 256, dtype=torch.int32, device=dev)
+    xcnt = torch.zeros(xblocks * 4 * 2, dtype=torch.int64, device=dev)
+    modes = ((1, "reads_alone"), (2, "copies_alone"), (3, "side_by_side")) if full else ()
+    for mode, tag in modes:
+        _probes.check(lib.rpa_probe_lds_dma(
+            ctypes.c_void_p(dsrc.data_ptr()), window, ctypes.c_void_p(xsink.data_ptr()),
+            ctypes.c_void_p(xcnt.data_ptr()), mode, ticks, xblocks, stream), "lds+dma probe")
+        torch.cuda.synchronize()
+        c = xcnt.view(xblocks, 4, 2).double()
+        for kind, waves in (("read", slice(0, 2)), ("copy", slice(2, 4))):
+            r = c[:, waves, 0]
+            if float(r.sum()) == 0:
+                continue
+            cyc = float(c[:, waves, 1].mean())
+            out[f"lds_{kind}_{tag}_bytes_per_cu_clk"] = float(r.sum()) * 8192 / cyc / cus
     torch.cuda.synchronize()
     return out
 
@@ -867,7 +985,7 @@ def main():
     torch.cuda.set_device(dev)
     if args.op == "probes":
         line = {"metric": "GPU ceilings (probes)", "n_gpus": 1, "data": "synthetic",
-                "ceilings": probe_ceilings(dev)}
+                "ceilings": probe_ceilings(dev, full=True)}
         print(json.dumps(line), flush=True)
         return
     if args.calib_copy_mib:

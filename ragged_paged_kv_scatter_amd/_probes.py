@@ -1,15 +1,21 @@
 """ctypes view of librpa_probes.so (include/rpa_probes.h): measurement probes
 of the GPU (HBM streaming, dense bf16 MFMA with its shader clock, VALU issue
-rates) that the benchmark reports as measured ceilings beside the published
-peaks.  Only argument marshalling lives here; the attention path never uses
+rates, LDS and global -> LDS rates) that the benchmark reports as measured
+ceilings beside the published peaks.  Only argument marshalling lives here; the attention path never uses
 this library."""
 import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "librpa_probes.so")
-EXPORTS = ("rpa_probe_read", "rpa_probe_copy", "rpa_probe_mfma", "rpa_probe_valu")
+EXPORTS = ("rpa_probe_read", "rpa_probe_copy", "rpa_probe_mfma", "rpa_probe_valu",
+           "rpa_probe_lds", "rpa_probe_dma", "rpa_probe_lds_dma", "rpa_probe_mix",
+           "rpa_probe_lds_mfma")
 VALU_OPS = {"exp": 0, "rcp": 1, "fma": 2}
+# LDS op -> bytes per instruction and wave
+LDS_OPS = {"ds_read_b128": (0, 1024), "ds_read_b64_tr_b16": (1, 512), "ds_write_b128": (2, 1024)}
+# LDS-fed MFMA patterns
+LDS_MFMA_MODES = {"qk_lds_2acc": 0, "pv_lds_4acc": 1, "qk_regs_2acc": 2, "qk_lds_4acc": 3}
 
 _lib = None
 
@@ -26,6 +32,11 @@ def load():
     lib.rpa_probe_copy.argtypes = [P, P, SZ, I, P]
     lib.rpa_probe_mfma.argtypes = [P, P, I, I, P]
     lib.rpa_probe_valu.argtypes = [P, I, I, I, P]
+    lib.rpa_probe_lds.argtypes = [P, P, I, I, I, P]
+    lib.rpa_probe_dma.argtypes = [P, SZ, P, P, I, I, P]
+    lib.rpa_probe_lds_dma.argtypes = [P, SZ, P, P, I, ctypes.c_int64, I, P]
+    lib.rpa_probe_mix.argtypes = [P, P, I, I, I, I, P]
+    lib.rpa_probe_lds_mfma.argtypes = [P, P, I, I, I, P]
     for n in EXPORTS:
         getattr(lib, n).restype = ctypes.c_int
     _lib = lib

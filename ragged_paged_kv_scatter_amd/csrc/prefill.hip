@@ -40,6 +40,66 @@
 namespace rpa {
 namespace {
 
+// Per-wave shader-clock counts of the prefill kernel, compiled only into the
+// measurement build (RPA_WAVE_TIMELINE, librpa_timeline.so).  For wave w,
+// kPfWords words: its clocks from start to end; clocks spent waiting for its
+// own block copies at the top of each pipeline step, and at the step's
+// barrier after that; its step count; then, summed over the steps that do
+// math, the clocks from the barrier to the first q.k MFMA (copy issue and
+// rescale), of the q.k part, of the p.v part, and of the row max / sum tail.
+// Stamps are read back only after the next step's barrier, where the wave
+// waits for its outstanding LDS and scalar loads anyway.  The library never
+// reads them.
+#ifdef RPA_WAVE_TIMELINE
+constexpr int kPfTimelineWaves = 8192;
+constexpr int kPfWords = 8;
+__device__ unsigned long long g_pf_timeline[kPfTimelineWaves * kPfWords];
+#define RPA_TL_PF_BEGIN()                                                   \
+  const unsigned long long tlp_t0 = __builtin_amdgcn_s_memtime();           \
+  unsigned long long tlp_vm = 0, tlp_bar = 0;                               \
+  unsigned long long tlp_ph[4] = {0, 0, 0, 0};                              \
+  unsigned long long tlp_s[5] = {0, 0, 0, 0, 0};                            \
+  int tlp_steps = 0
+#define RPA_TL_PF_MARK(v) const unsigned long long v = __builtin_amdgcn_s_memtime()
+#define RPA_TL_PF_FOLD()                                                    \
+  do {                                                                      \
+    if (tlp_s[4] != 0) {                                                    \
+      for (int i_ = 0; i_ < 4; ++i_) tlp_ph[i_] += tlp_s[i_ + 1] - tlp_s[i_]; \
+      tlp_s[4] = 0;                                                         \
+    }                                                                       \
+  } while (0)
+#define RPA_TL_PF_WAITS(a, b)                                               \
+  do {                                                                      \
+    const unsigned long long c_ = __builtin_amdgcn_s_memtime();             \
+    RPA_TL_PF_FOLD();                                                       \
+    tlp_vm += (b) - (a);                                                    \
+    tlp_bar += c_ - (b);                                                    \
+    ++tlp_steps;                                                            \
+    tlp_s[0] = c_;                                                          \
+  } while (0)
+#define RPA_TL_PF_AT(i) tlp_s[i] = __builtin_amdgcn_s_memtime()
+#define RPA_TL_PF_END()                                                     \
+  do {                                                                      \
+    const unsigned long long t_ = __builtin_amdgcn_s_memtime();             \
+    RPA_TL_PF_FOLD();                                                       \
+    const long long w_ = (long long)blockIdx.x * (NT / 64) + (threadIdx.x >> 6); \
+    if ((threadIdx.x & 63) == 0 && w_ < kPfTimelineWaves) {                 \
+      unsigned long long* r_ = g_pf_timeline + w_ * kPfWords;               \
+      r_[0] = t_ - tlp_t0;                                                  \
+      r_[1] = tlp_vm;                                                       \
+      r_[2] = tlp_bar;                                                      \
+      r_[3] = (unsigned long long)tlp_steps;                                \
+      for (int i_ = 0; i_ < 4; ++i_) r_[4 + i_] = tlp_ph[i_];               \
+    }                                                                       \
+  } while (0)
+#else
+#define RPA_TL_PF_BEGIN() static_assert(true, "")
+#define RPA_TL_PF_MARK(v) static_assert(true, "")
+#define RPA_TL_PF_WAITS(a, b) static_assert(true, "")
+#define RPA_TL_PF_AT(i) static_assert(true, "")
+#define RPA_TL_PF_END() static_assert(true, "")
+#endif
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -165,6 +225,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 template <typename CT, int D, bool CAP, bool QF8>
 __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
   static_assert(!QF8 || sizeof(CT) == 1, "e4m3 queries go with an e4m3 cache");
+  RPA_TL_PF_BEGIN();
   constexpr bool VDIRECT = sizeof(CT) == 2;        // bf16 cache: V global -> LDS directly
   constexpr bool KDIRECT = VDIRECT || QF8;         // K rows copied as stored
   constexpr int RB = D * 2;                        // LDS row bytes of V (and of bf16 K)
@@ -532,8 +593,11 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
     };
     // step b, first part: K(b+1), V(b) are in LDS; start K(b+2), V(b+1)
     auto begin_step = [&](int blk) __attribute__((always_inline)) {
+      RPA_TL_PF_MARK(tlp_a);
       if constexpr (KDIRECT) wait_vmem_all();     // this wave's loads have landed
+      RPA_TL_PF_MARK(tlp_b);
       __syncthreads();                            // everyone's; last readers are done
+      RPA_TL_PF_WAITS(tlp_a, tlp_b);
       if (blk + 1 < blk_end) load_v(blk + 1);     // its pages are in the table already
       if (blk + 2 < blk_end) {
         ensure_pages(blk + 2);
@@ -642,6 +706,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
       const float c_bias = cap_l2 - m_use;                 // cap path: p = 2^(c_bias - 2 cap_l2 r)
       const char* kn = kbuf(blk + 1);
       const char* vb = vbuf(blk);
+      RPA_TL_PF_AT(1);
       __builtin_amdgcn_sched_barrier(0);
 
       // (1) P(b) = 2^(S(b) - m) packed to bf16, under the MFMAs of S(b+1)
@@ -720,6 +785,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
         }
       }
 
+      RPA_TL_PF_AT(2);
       // (2) O^T += V^T(b) P^T(b)
       const int k0n = (blk + 1) * BK;
       float m0 = kRedInit, m1 = kRedInit;
@@ -753,11 +819,13 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
           va = vn;
         }
       }
+      RPA_TL_PF_AT(3);
       __builtin_amdgcn_s_setprio(0);
       l_run += ls0 + ls1;
       const float mr = red(m0, m1);
       mx = to_mx(red(mr, __shfl_xor(mr, 32)));
       end_step(blk);
+      RPA_TL_PF_AT(4);
     };
     // steps [blk, end) in pairs; on return S(blk) is in sa again
     auto run = [&](auto mask_next, int& blk, int end) __attribute__((always_inline)) {
@@ -870,6 +938,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
     }
     __syncthreads();  // LDS is reused by the next unit
   }
+  RPA_TL_PF_END();
 }
 
 long long resident_grid(const void* kernel) {
@@ -930,3 +999,19 @@ hipError_t launch_prefill(const AttnParams& p, rpa_dtype q_dt, rpa_dtype cache_d
 }
 
 }  // namespace rpa
+
+#ifdef RPA_WAVE_TIMELINE
+// The prefill kernel's per-wave clock counts of the measurement build: n
+// words, 8 per wave (total, copy wait, barrier wait, steps, then the issue,
+// q.k, p.v and tail parts of the steps).
+extern "C" int rpa_pf_timeline_read(unsigned long long* host, int n) {
+  if (n > rpa::kPfTimelineWaves * rpa::kPfWords) n = rpa::kPfTimelineWaves * rpa::kPfWords;
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(rpa::g_pf_timeline),
+                                  (size_t)n * sizeof(unsigned long long), 0, hipMemcpyDeviceToHost);
+}
+extern "C" int rpa_pf_timeline_clear(void) {
+  static unsigned long long zero[rpa::kPfTimelineWaves * rpa::kPfWords];
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(rpa::g_pf_timeline), zero, sizeof(zero), 0,
+                                hipMemcpyHostToDevice);
+}
+#endif

@@ -124,3 +124,21 @@ def test_strip_timeline_removes_only_the_instrumentation():
     out = " ".join(bench.strip_timeline(src).split())
     assert out == "int a; void f() { g(); } #ifdef OTHER int d; #endif"
 
+
+
+def test_pf_timeline_summary_by_hand():
+    # two waves: 1000 clocks over 10 steps with 100 waiting on copies and 200
+    # at barriers; 3000 clocks over 20 steps with 300 and 900; one empty record
+    # (the step parts: issue 50 / q.k 400 / p.v 300 / tail 100 clocks per step
+    # on the first wave, twice that on the second)
+    a = np.array([[1000, 100, 200, 10, 500, 4000, 3000, 1000],
+                  [3000, 300, 900, 20, 2000, 16000, 12000, 4000],
+                  [0, 0, 0, 0, 0, 0, 0, 0]], dtype=np.uint64)
+    s = bench.pf_timeline_summary(a)
+    assert s["issue_clk_per_step"] == 75.0 and s["qk_clk_per_step"] == 600.0
+    assert s["pv_clk_per_step"] == 450.0 and s["tail_clk_per_step"] == 150.0
+    assert s["waves"] == 2 and s["steps"] == [10, 15, 20]
+    assert s["total_clk"] == [1000, 2000, 3000]
+    assert s["copy_wait_share"] == 0.1 and s["barrier_wait_share"] == 0.25
+    assert s["clk_per_step"] == 125.0
+    assert s["copy_wait_clk_per_step"] == 12.5 and s["barrier_wait_clk_per_step"] == 32.5
