@@ -206,7 +206,10 @@ KERNEL_SOURCES = {  # kernel -> sources whose hash identifies a counter summary
     "decode": ["decode.hip", "merge.h", "device_common.h", "rpa_internal.h"],
     "prefill": ["prefill.hip", "merge.h", "device_common.h", "rpa_internal.h"],
 }
-KERNEL_SYMBOL = {"decode": "row_kernel", "prefill": "prefill_kernel"}
+# kernel -> the symbols whose dispatches make up one launch of it; the first
+# is dispatched once per step (prefill_kernel is, and the two-group kernel
+# runs after it on bf16 batches, one of the two taking the tiles)
+KERNEL_SYMBOL = {"decode": ("row_kernel",), "prefill": ("prefill_kernel", "prefill_pair_kernel")}
 
 
 def strip_timeline(text):
@@ -269,20 +272,21 @@ def summarize_counters(workload, kernel, fetch_csv, write_csv, copy_bytes):
     reads for the calibration copy of `copy_bytes` (read once, written once).
     The flush writes between timed steps are dispatches of their own and are
     not counted."""
-    sym = KERNEL_SYMBOL[kernel]
+    syms = KERNEL_SYMBOL[kernel]
     res = {}
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         disp = read_counter_csv(path)
         copies = [c[name] for k, c in disp.values()
                   if "copy" in k.lower() and "probe" not in k.lower() and name in c]
-        ours = [c[name] for k, c in disp.values() if sym in k and name in c]
-        if not copies or not ours:
-            raise SystemExit(f"no copy or {sym} dispatch with {name} in {path}")
+        ours = [c[name] for k, c in disp.values() if any(s in k for s in syms) and name in c]
+        launches = sum(1 for k, c in disp.values() if syms[0] in k and name in c)
+        if not copies or not ours or not launches:
+            raise SystemExit(f"no copy or {syms[0]} dispatch with {name} in {path}")
         copy_kib = max(copies)
         factor = copy_bytes / (copy_kib * 1024.0)
-        res[name] = dict(kernel_kib=sum(ours) / len(ours), dispatches=len(ours),
-                         copy_kib=copy_kib, factor=factor,
-                         bytes=sum(ours) / len(ours) * 1024.0 * factor)
+        res[name] = dict(kernel_kib=sum(ours) / launches, dispatches=len(ours),
+                         launches=launches, copy_kib=copy_kib, factor=factor,
+                         bytes=sum(ours) / launches * 1024.0 * factor)
     out = dict(workload=workload, kernel=kernel, source_hash=source_hash(kernel),
                copy_bytes=copy_bytes, fetch=res["FETCH_SIZE"], write=res["WRITE_SIZE"],
                traffic_bytes=res["FETCH_SIZE"]["bytes"] + res["WRITE_SIZE"]["bytes"])
@@ -569,6 +573,31 @@ def pf_timeline_summary(a):
     return out
 
 
+PP_PARTS = ("pre_qk", "qk", "group_b_barrier", "pv", "tail", "unit_end")
+
+
+def pp_timeline_summary(a):
+    """Per-wave counts of the two-group prefill kernel (rows of total clocks,
+    steps, then clocks in: step start -> q.k (group A's barrier and copies,
+    the rescale), q.k, group B's mid-step barrier, p.v, the row max / sum
+    tail, and unit set-up / end) -> means per step over the waves of each
+    group (waves 0-3 and 4-7 of each workgroup)."""
+    out = {}
+    for gname, sel in (("group_a", lambda w: (w % 8) < 4), ("group_b", lambda w: (w % 8) >= 4)):
+        idx = np.array([i for i in range(len(a)) if sel(i)], dtype=np.int64)
+        r = a[idx]
+        r = r[r[:, 1] > 0].astype(np.float64)
+        if len(r) == 0:
+            out[gname] = {"waves": 0}
+            continue
+        steps = r[:, 1]
+        d = {"waves": int(len(r)), "clk_per_step": round(float((r[:, 0] / steps).mean()), 1)}
+        for i, name in enumerate(PP_PARTS):
+            d[f"{name}_clk_per_step"] = round(float((r[:, 2 + i] / steps).mean()), 1)
+        out[gname] = d
+    return out
+
+
 def bench_timeline(args, w, dev):
     """The row kernels' per-wave clock stamps and the prefill kernel's per-wave
     wait counts (librpa_timeline.so) over a few flushed steps of the workload:
@@ -611,8 +640,12 @@ def bench_timeline(args, w, dev):
         if lib.rpa_pf_timeline_read(pbuf, pwords) != 0:
             raise SystemExit("rpa_pf_timeline_read failed")
         b = np.frombuffer(pbuf, dtype=np.uint64).reshape(-1, 8).copy()
+        if lib.rpa_pp_timeline_read(pbuf, pwords) != 0:
+            raise SystemExit("rpa_pp_timeline_read failed")
+        c = np.frombuffer(pbuf, dtype=np.uint64).reshape(-1, 8).copy()
         print(json.dumps({"metric": "row kernel wave timeline", "workload": w.name, "launch": rep,
-                          **timeline_summary(a), "prefill": pf_timeline_summary(b)}), flush=True)
+                          **timeline_summary(a), "prefill": pf_timeline_summary(b),
+                          "prefill_pair": pp_timeline_summary(c)}), flush=True)
 
 
 def probe_ceilings(dev, full=False):

@@ -92,7 +92,37 @@ __device__ unsigned long long g_pf_timeline[kPfTimelineWaves * kPfWords];
       for (int i_ = 0; i_ < 4; ++i_) r_[4 + i_] = tlp_ph[i_];               \
     }                                                                       \
   } while (0)
+// The two-group kernel's laps: per wave, clocks in each part of its steps,
+// read at once (each lap waits for its own stamp).
+__device__ unsigned long long g_pp_timeline[kPfTimelineWaves * kPfWords];
+#define RPA_TL_PP_BEGIN()                                                   \
+  unsigned long long tlq_last = __builtin_amdgcn_s_memtime();               \
+  const unsigned long long tlq_t0 = tlq_last;                               \
+  unsigned long long tlq_acc[6] = {0, 0, 0, 0, 0, 0};                       \
+  int tlq_steps = 0
+#define RPA_TL_PP_LAP(i)                                                    \
+  do {                                                                      \
+    const unsigned long long t_ = __builtin_amdgcn_s_memtime();             \
+    tlq_acc[i] += t_ - tlq_last;                                            \
+    tlq_last = t_;                                                          \
+  } while (0)
+#define RPA_TL_PP_STEP() ++tlq_steps
+#define RPA_TL_PP_END()                                                     \
+  do {                                                                      \
+    const unsigned long long t_ = __builtin_amdgcn_s_memtime();             \
+    const long long w_ = (long long)blockIdx.x * (2 * NT / 64) + (threadIdx.x >> 6); \
+    if ((threadIdx.x & 63) == 0 && w_ < kPfTimelineWaves) {                 \
+      unsigned long long* r_ = g_pp_timeline + w_ * kPfWords;               \
+      r_[0] = t_ - tlq_t0;                                                  \
+      r_[1] = (unsigned long long)tlq_steps;                                \
+      for (int i_ = 0; i_ < 6; ++i_) r_[2 + i_] = tlq_acc[i_];              \
+    }                                                                       \
+  } while (0)
 #else
+#define RPA_TL_PP_BEGIN() static_assert(true, "")
+#define RPA_TL_PP_LAP(i) static_assert(true, "")
+#define RPA_TL_PP_STEP() static_assert(true, "")
+#define RPA_TL_PP_END() static_assert(true, "")
 #define RPA_TL_PF_BEGIN() static_assert(true, "")
 #define RPA_TL_PF_MARK(v) static_assert(true, "")
 #define RPA_TL_PF_WAITS(a, b) static_assert(true, "")
@@ -112,6 +142,7 @@ constexpr int NT = 256;         // threads per workgroup
 constexpr int kPT = 512;        // page ids cached in LDS per refill
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr long long kPrefillGrid = 1024;  // fallback persistent grid (multiple of 8)
+constexpr int kPairPages = 8192;           // page ids the two-group kernel holds in LDS
 
 template <typename CT> struct CacheElem;
 template <> struct CacheElem<uint16_t> { static constexpr int size = 2; };
@@ -382,6 +413,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
   // When the planner runs this kernel beside the row kernel (co_run), only
   // the first (8 - kCoRowEighths) / 8 of the grid (a multiple of 8) takes
   // units, leaving the other slots of the CUs to the row kernel's waves.
+  if (p.pf_pair && !hdr->co_run) return;           // the two-group kernel has the batch
   unsigned grid = gridDim.x;
   if (hdr->co_run && grid >= 64) grid = grid / 64 * (8 - kCoRowEighths) * 8;
   if (blockIdx.x >= grid) return;
@@ -941,6 +973,456 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
   RPA_TL_PF_END();
 }
 
+// ---------------------------------------------------------------------------
+// Two-group prefill kernel: bf16 queries over a bf16 cache, an even GQA group.
+//
+// One workgroup of 8 waves per CU, and waves w and w + 4 share a SIMD.  A
+// unit is (sequence, tile of up to 128 query tokens, pair of q heads of one
+// kv head): group A (waves 0-3) takes the pair's first head, group B (waves
+// 4-7) the second, each wave 32 query rows as in prefill_kernel.  Both heads
+// see the same keys, so one LDS copy of each K / V block serves both groups,
+// half the global -> LDS copies per FLOP of prefill_kernel, and group A's
+// waves issue all of them.  Each group runs prefill_kernel's step (rescale;
+// q.k of S(b+1) under the exps of S(b); p.v of block b under the max of
+// S(b+1); row max and sum), but the step's workgroup barrier falls at a
+// different point of it: for A before the q.k part (A then issues the
+// copies), for B between the q.k and p.v parts.  The two waves of a SIMD
+// therefore run half a step apart, and each one's copies, barrier and tail
+// run while the other's MFMAs keep the matrix core busy.
+//
+// Blocks: A's step b copies V(b+1) and K(b+3).  Barrier b thus finds K(b+1),
+// K(b+2) and V(b) in LDS; B computes S(b+1) before barrier b, so K(b+1) must
+// have landed by barrier b - 1: three K buffers (block mod 3) and two V
+// buffers (block mod 2).  The unit's page ids sit in LDS whole.
+template <int D, bool CAP>
+__global__ __launch_bounds__(2 * NT, 1) void prefill_pair_kernel(AttnParams p) {
+  constexpr int RB = D * 2;                        // LDS row bytes (bf16 K and V)
+  constexpr int CPR = RB / 16;                     // 16-byte chunks per row
+  constexpr int BLKB = BK * RB;                    // bytes of one K or V block
+  constexpr int KS = D / 16;                       // MFMA k-steps of q.k
+  constexpr int DT = D / 32;                       // 32-row d tiles of O^T
+  constexpr int IPW = BLKB / 1024 / 4;             // direct loads per A wave per block
+  constexpr int RPI = 1024 / RB;                   // rows per direct load instruction
+  constexpr int PDK = 2;                           // q.k MFMAs a K fragment read runs ahead
+  constexpr int PDV = 1;                           // p.v MFMAs a V^T fragment read runs ahead
+  static_assert(IPW * RPI == 16, "a wave loads 16 consecutive rows");
+  __shared__ __attribute__((aligned(1024))) char s_k[3 * BLKB];
+  __shared__ __attribute__((aligned(1024))) char s_v[2 * BLKB];
+  __shared__ int s_pt[kPairPages];
+  RPA_TL_PP_BEGIN();
+
+  const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(p.ws + p.lay.header);
+  // beside the row kernel (co_run) prefill_kernel takes the batch instead
+  if (hdr->co_run) return;
+  const PrefillItem* items = reinterpret_cast<const PrefillItem*>(p.ws + p.lay.pf_items);
+  const char* zero_row = reinterpret_cast<const char*>(p.ws + p.lay.zeros);
+  const int Hq = p.Hq, Hkv = p.Hkv, G = Hq / Hkv, NPAIR = Hq / 2;
+  const long long n_units = (long long)hdr->n_pf_items * NPAIR;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, gw = wave & 3, gtid = tid & (NT - 1);
+  const int kg = lane >> 5, col = lane & 31;
+  const int sh = p.ps_shift;
+  const int pmask = (1 << sh) - 1;
+  const uint32_t row_bytes = 2u * Hkv * p.Dpad * 2u;
+  const uint32_t v_bytes = (uint32_t)p.Dpad * 2u;
+  // non-positive scales: as in prefill_kernel
+  const bool q_zero = p.qk_scale == 0.f;
+  const uint32_t q_and = q_zero ? 0u : 0xFFFFFFFFu;
+  const uint32_t q_xor = p.qk_scale < 0.f ? 0x80008000u : 0u;
+  const float scale_pos = q_zero ? 1.f : fabsf(p.qk_scale);
+  const float c_scale = CAP ? scale_pos : scale_pos * kLog2e;
+  const float c_eff = CAP ? 1.f : c_scale;
+  const float cap_k = CAP ? c_scale * 2.f * kLog2e / p.cap : 0.f;
+  const float cap_l2 = CAP ? p.cap * kLog2e : 0.f;
+  constexpr float kRedInit = CAP ? INFINITY : -INFINITY;
+  auto red = [](float a, float b) { return CAP ? fminf(a, b) : fmaxf(a, b); };
+  auto to_mx = [&](float v) { return CAP ? fmaf(v, -2.f * cap_l2, cap_l2) : v * c_eff; };
+
+  uint32_t dma_off[IPW], dma_in[IPW];
+  const uint32_t in_row = p.in_row_bytes;
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int r = RPI * j + lane / CPR;
+    dma_off[j] = r * row_bytes + (swz_chunk<D>(r, lane % CPR) << 4);
+    dma_in[j] = r * in_row + (swz_chunk<D>(r, lane % CPR) << 4);
+  }
+  const bool fused = p.fuse_update != 0;
+  const int fk = swz_f<D>(col);
+  const uint32_t k_off = col * RB + ((((fk >> 1) << 1) | (kg ^ (fk & 1))) << 4);
+  const int grp16 = lane >> 4, r16 = lane & 15;
+  const int rr = (grp16 >> 1) * 4 + (r16 >> 2);
+  const int g1 = (2 * (grp16 & 1) + ((r16 & 3) >> 1)) ^ swz_f<D>(rr);
+  const uint32_t v_off1 = rr * RB + (g1 << 4) + (r16 & 1) * 8;
+  const uint32_t v_off2 = v_off1 ^ 32u;
+  auto ld_k = [&](const char* kb, int ks, int hf) -> bf16x8 {
+    const char* a = kb + ((k_off ^ (uint32_t)(ks << 5)) + hf * 32 * RB);
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(a));
+  };
+  auto ld_vt = [&](const char* vb, int ks, int dt) -> bf16x8 {
+    const char* a1 = vb + ((v_off1 ^ (uint32_t)(dt << 6)) + ks * 16 * RB);
+    const char* a2 = vb + ((v_off2 ^ (uint32_t)(dt << 6)) + (ks * 16 + 8) * RB);
+    const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(a1));
+    const i16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(a2));
+    const i16x8 av = {x1[0], x1[1], x1[2], x1[3], x2[0], x2[1], x2[2], x2[3]};
+    return __builtin_bit_cast(bf16x8, av);
+  };
+
+  // persistent grid over units, as in prefill_kernel (snake order by rounds)
+  const unsigned grid = gridDim.x;
+  const bool snake = (grid & 7) == 0;
+  for (long long k = 0;; ++k) {
+    const long long b = (snake && (k & 1)) ? (long long)(grid / 8 - 1 - blockIdx.x / 8) * 8 +
+                                                 (blockIdx.x & 7)
+                                           : (long long)blockIdx.x;
+    const long long u = k * grid + b;
+    if (u >= n_units) break;
+    const int item_i = (int)(u / NPAIR);
+    const int pp = (int)(u - (long long)item_i * NPAIR);
+    const int g = pp % Hkv;
+    const int h = g * G + 2 * (pp / Hkv) + grp;
+    const PrefillItem it = items[item_i];
+    const int seq = it.seq;
+    const int q0 = p.qsl[seq];
+    const int q_len = p.qsl[seq + 1] - q0;
+    const int ctx = p.kv_lens[seq] - q_len;
+    const int W = p.window;
+    const int kv_lo = W > 0 ? max(0, ctx + it.q_begin - W + 1) : 0;
+    const int kv_hi = ctx + it.q_end;
+    const int* bt = p.block_tables + (long long)seq * p.pps;
+    const char* kv_head = static_cast<const char*>(p.cache) + 2LL * g * p.Dpad * 2;
+    const char* in_k = fused ? static_cast<const char*>(p.new_k) + (long long)g * D * 2 : nullptr;
+    const char* in_v = fused ? static_cast<const char*>(p.new_v) + (long long)g * D * 2 : nullptr;
+    const int new_lo = fused ? ctx : INT_MAX;
+    // the pair's first q head is kv head g's first: its group writes the new rows
+    const bool writer = fused && pp < Hkv && grp == 0;
+    const int own_lo = ctx + it.q_begin, own_hi = ctx + it.q_end;
+    char* cache_w = const_cast<char*>(kv_head);
+
+    const int row_q = it.q_begin + gw * 32 + col;
+    const bool row_ok = row_q < it.q_end;
+    const int pos = ctx + row_q;
+    const bool wave_live = it.q_begin + gw * 32 < it.q_end;
+
+    const int blk_first = kv_lo / BK;
+    const int blk_end = (kv_hi + BK - 1) / BK;
+    const int tpos_lo = ctx + it.q_begin, tpos_hi = kv_hi - 1;
+    int f_lo = blk_first;
+    if (W > 0 && tpos_hi - W >= 0) f_lo = max(f_lo, (tpos_hi - W) / BK + 1);
+    f_lo = min(f_lo, blk_end);
+    const int f_hi = min(max((tpos_lo + 1) / BK, f_lo), blk_end);
+    const int UA = min(max(blk_first, f_lo - 1), blk_end);
+    const int UB = max(UA, f_hi - 1);
+
+    // page ids of the unit's whole key range in LDS (the host launches this
+    // kernel only when a sequence's block table fits)
+    const int pt_base = kv_lo >> sh;
+    for (int i = tid, n = ((kv_hi - 1) >> sh) - pt_base + 1; i < n; i += 2 * NT)
+      s_pt[i] = bt[pt_base + i];
+    auto kbuf = [&](int blk) -> char* { return s_k + (blk % 3) * BLKB; };
+    auto vbuf = [&](int blk) -> char* { return s_v + (blk & 1) * BLKB; };
+    // group A's copy of a block's 16 rows per wave (vofs: 0 K rows, v_bytes V rows)
+    auto copy_block = [&](int blk, char* buf, uint32_t vofs, const char* in_base)
+                          __attribute__((always_inline)) {
+      const int t0 = blk * BK + 16 * gw;
+      const uint32_t lds0 = lds_addr(buf + gw * IPW * 1024);
+      if (t0 >= kv_lo && t0 + 16 <= min(kv_hi, new_lo)) {
+        const int page = __builtin_amdgcn_readfirstlane(s_pt[(t0 >> sh) - pt_base]);
+        const uint32_t crow = ((uint32_t)page << sh) | (uint32_t)(t0 & pmask);
+        const char* base = uniform_ptr(kv_head + vofs + (uint64_t)crow * row_bytes);
+#pragma unroll
+        for (int j = 0; j < IPW; ++j) dma16_s(base, dma_off[j], lds0 + j * 1024);
+      } else if (t0 >= max(kv_lo, new_lo) && t0 + 16 <= kv_hi) {
+        const char* base = uniform_ptr(in_base + (uint64_t)(q0 + t0 - ctx) * in_row);
+#pragma unroll
+        for (int j = 0; j < IPW; ++j) dma16_s(base, dma_in[j], lds0 + j * 1024);
+      } else {
+#pragma unroll
+        for (int j = 0; j < IPW; ++j) {
+          const int r = RPI * j + lane / CPR;
+          const int tok = t0 + r;
+          const int lc = swz_chunk<D>(r, lane % CPR);
+          const char* src = zero_row + (lc << 4);
+          if (tok >= kv_lo && tok < kv_hi) {
+            if (tok >= new_lo) {
+              src = in_base + (uint64_t)(q0 + tok - ctx) * in_row + (lc << 4);
+            } else {
+              const int page = s_pt[(tok >> sh) - pt_base];
+              const uint32_t crow = ((uint32_t)page << sh) | (uint32_t)(tok & pmask);
+              src = kv_head + vofs + (uint64_t)crow * row_bytes + (lc << 4);
+            }
+          }
+          dma16(src, lds0 + j * 1024);
+        }
+      }
+    };
+    auto load_k = [&](int blk) { copy_block(blk, kbuf(blk), 0, in_k); };
+    auto load_v = [&](int blk) { copy_block(blk, vbuf(blk), v_bytes, in_v); };
+    // fused update: group A of the writer pair stores its tile's new rows of
+    // block blk from the LDS buffer (pad lanes zeroed)
+    auto write_lds = [&](int blk, const char* buf, uint32_t vofs) {
+      if (!writer) return;
+      const int lo = max(blk * BK, own_lo), hi = min(blk * BK + BK, own_hi);
+      if (lo >= hi) return;
+      const int wch = p.Dpad * 2 / 16;
+      const int n = (hi - lo) * wch;
+      for (int i = gtid; i < n; i += NT) {
+        const int r2 = i / wch, c = i - r2 * wch;
+        const int tok = lo + r2, r = tok - blk * BK;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (c < CPR) v = *reinterpret_cast<const uint4*>(buf + r * RB + (swz_chunk<D>(r, c) << 4));
+        const int page = bt[tok >> sh];
+        char* row = cache_w + (uint64_t)(((uint32_t)page << sh) | (uint32_t)(tok & pmask)) * row_bytes;
+        *reinterpret_cast<uint4*>(row + vofs + c * 16) = v;
+      }
+    };
+
+    bf16x8 qreg[KS];
+    {
+      const long long qrow = (long long)(q0 + (row_ok ? row_q : it.q_begin)) * Hq + h;
+      const uint16_t* qp = static_cast<const uint16_t*>(p.q) + qrow * D + 8 * kg;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qp + 16 * ks) : make_uint4(0, 0, 0, 0);
+        v = make_uint4((v.x & q_and) ^ q_xor, (v.y & q_and) ^ q_xor, (v.z & q_and) ^ q_xor,
+                       (v.w & q_and) ^ q_xor);
+        qreg[ks] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+    f32x16 oacc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x16 sa[2], sb[2];
+    float mx = -INFINITY;
+    auto logit = [&](auto masked, int k0, float sv, int e) __attribute__((always_inline)) -> float {
+      if constexpr (CAP) sv = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(sv * cap_k) + 1.f);
+      if constexpr (decltype(masked)::value) {
+        const int ko = (e >> 4) * 32 + ((e & 15) >> 2) * 8 + (e & 3);
+        const int lim = pos - k0 - 4 * kg;
+        const bool vis = ko <= lim && (W <= 0 || ko > lim - W);
+        sv = vis ? sv : kRedInit;
+      }
+      return sv;
+    };
+
+    // One step on block blk: sacc holds S(blk), s2 receives S(blk + 1).  The
+    // barrier (and for group A the copies) sits where the wave's group takes
+    // it (see above).
+    auto step = [&](auto mask_next, int blk, f32x16(&sacc)[2], f32x16(&s2)[2])
+                    __attribute__((always_inline)) {
+      constexpr bool MASK_NEXT = decltype(mask_next)::value;
+      if (grp == 0) {
+        wait_vmem_all();
+        __syncthreads();
+        if (blk + 1 < blk_end) load_v(blk + 1);
+        if (blk + 3 < blk_end) load_k(blk + 3);
+        if (blk + 1 < blk_end) write_lds(blk + 1, kbuf(blk + 1), 0);
+        write_lds(blk, vbuf(blk), v_bytes);
+      }
+      if (__any(mx > m_run + 8.f)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      const float c_bias = cap_l2 - m_use;
+      const char* kn = kbuf(blk + 1);
+      const char* vb = vbuf(blk);
+      RPA_TL_PP_LAP(0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s2[hf][i] = 0.f;
+      float pf[32];
+      uint32_t pk[16];
+      float ls0 = 0.f, ls1 = 0.f;
+      auto expo = [&](int e) __attribute__((always_inline)) {
+        pf[e] = CAP ? __builtin_amdgcn_exp2f(fmaf(sacc[e >> 4][e & 15], -2.f * cap_l2, c_bias))
+                    : __builtin_amdgcn_exp2f(fmaf(sacc[e >> 4][e & 15], c_eff, -m_use));
+        if (e & 1) {
+          pk[e >> 1] = pack_bf16(pf[e - 1], pf[e]);
+          const bf16x2 pw = __builtin_bit_cast(bf16x2, pk[e >> 1]);
+          if (e & 2) ls1 = __builtin_amdgcn_fdot2_f32_bf16(pw, kOnes2, ls1, false);
+          else ls0 = __builtin_amdgcn_fdot2_f32_bf16(pw, kOnes2, ls0, false);
+          // kept in this chunk: group B's barrier below would otherwise let
+          // these sink below the MFMAs they run under
+          asm volatile("" ::"v"(pk[e >> 1]), "v"((e & 2) ? ls1 : ls0));
+        }
+      };
+      constexpr int XA = 8 / KS, XB = 8 / DT, MB = 16 / DT;
+      // A q.k fragment is read PDK MFMAs ahead of its MFMA, a V^T fragment
+      // PDV MFMAs (reading further ahead measured no faster).
+      {
+        bf16x8 kq[2 * KS];
+#pragma unroll
+        for (int m = 0; m < PDK; ++m) kq[m] = ld_k(kn, m >> 1, m & 1);
+#pragma unroll
+        for (int m = 0; m < 2 * KS; ++m) {
+          if (m + PDK < 2 * KS) kq[m + PDK] = ld_k(kn, (m + PDK) >> 1, (m + PDK) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+          s2[m & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[m], qreg[m >> 1], s2[m & 1], 0, 0, 0);
+#pragma unroll
+          for (int x = 0; x < XA; ++x) expo(m * XA + x);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      RPA_TL_PP_LAP(1);
+      if (grp != 0) __syncthreads();
+      RPA_TL_PP_LAP(2);
+      const int k0n = (blk + 1) * BK;
+      float m0 = kRedInit, m1 = kRedInit;
+      bf16x8 vq[4 * DT];
+#pragma unroll
+      for (int m = 0; m < PDV; ++m) vq[m] = ld_vt(vb, m / DT, m % DT);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 pb = __builtin_bit_cast(
+            bf16x8, make_uint4(pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]));
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int m = ks * DT + dt;
+          if (m + PDV < 4 * DT) vq[m + PDV] = ld_vt(vb, (m + PDV) / DT, (m + PDV) % DT);
+          __builtin_amdgcn_sched_barrier(0);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[m], pb, oacc[dt], 0, 0, 0);
+          if (ks < 2) {
+#pragma unroll
+            for (int x = 0; x < XB; ++x) expo(16 + m * XB + x);
+          } else {
+#pragma unroll
+            for (int x = 0; x < MB; ++x) {
+              const int e = (m - 2 * DT) * MB + x;
+              const float sv = logit(mask_next, k0n, s2[e >> 4][e & 15], e);
+              s2[e >> 4][e & 15] = sv;
+              if (x & 1) m1 = red(m1, sv);
+              else m0 = red(m0, sv);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      RPA_TL_PP_LAP(3);
+      l_run += ls0 + ls1;
+      const float mr = red(m0, m1);
+      mx = to_mx(red(mr, __shfl_xor(mr, 32)));
+      (void)MASK_NEXT;
+      RPA_TL_PP_LAP(4);
+      RPA_TL_PP_STEP();
+    };
+    // a wave with no query rows takes the same barriers and copies, no math
+    auto idle_step = [&](int blk) __attribute__((always_inline)) {
+      if (grp == 0) {
+        wait_vmem_all();
+        __syncthreads();
+        if (blk + 1 < blk_end) load_v(blk + 1);
+        if (blk + 3 < blk_end) load_k(blk + 3);
+        if (blk + 1 < blk_end) write_lds(blk + 1, kbuf(blk + 1), 0);
+        write_lds(blk, vbuf(blk), v_bytes);
+      } else {
+        __syncthreads();
+      }
+    };
+    auto run = [&](auto mask_next, int& blk, int end) __attribute__((always_inline)) {
+      for (; blk + 1 < end; blk += 2) {
+        step(mask_next, blk, sa, sb);
+        step(mask_next, blk + 1, sb, sa);
+      }
+      if (blk < end) {
+        step(mask_next, blk, sa, sb);
+        sa[0] = sb[0];
+        sa[1] = sb[1];
+        ++blk;
+      }
+    };
+    auto run_all = [&]() __attribute__((always_inline)) {
+      if (wave_live) {
+        int blk = blk_first;
+        run(std::true_type{}, blk, UA);
+        run(std::false_type{}, blk, UB);
+        run(std::true_type{}, blk, blk_end);
+      } else {
+        for (int blk = blk_first; blk < blk_end; ++blk) idle_step(blk);
+      }
+    };
+
+    // ---- prologue: K(b0), K(b0+1) in; then V(b0), K(b0+2) in flight; S(b0) ----
+    const int b0 = blk_first;
+    __syncthreads();  // the page table is in LDS
+    if (grp == 0) {
+      load_k(b0);
+      if (b0 + 1 < blk_end) load_k(b0 + 1);
+    }
+    wait_vmem_all();
+    __syncthreads();
+    if (grp == 0) {
+      write_lds(b0, kbuf(b0), 0);
+      load_v(b0);
+      if (b0 + 2 < blk_end) load_k(b0 + 2);
+    }
+    if (wave_live) {
+      const char* kb = kbuf(b0);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sa[hf][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sa[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_k(kb, ks, 0), qreg[ks], sa[0], 0, 0, 0);
+        sa[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_k(kb, ks, 1), qreg[ks], sa[1], 0, 0, 0);
+      }
+      float t = kRedInit;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const float sv = logit(std::true_type{}, b0 * BK, sa[e >> 4][e & 15], e);
+        sa[e >> 4][e & 15] = sv;
+        t = red(t, sv);
+      }
+      mx = to_mx(red(t, __shfl_xor(t, 32)));
+    }
+    run_all();
+
+    // ---- finalise (as prefill_kernel) ----
+    if (wave_live) {
+      float l_tot = l_run + __shfl_xor(l_run, 32);
+      float f = 1.f;
+      if (p.sink) {
+        const float sg = p.sink[h] * kLog2e;
+        const float mxs = fmaxf(m_run, sg);
+        f = __builtin_amdgcn_exp2f(m_run - mxs);
+        l_tot = l_tot * f + __builtin_amdgcn_exp2f(sg - mxs);
+      }
+      const float sc = f * p.v_scale / l_tot;
+      if (row_ok) {
+        uint16_t* op = static_cast<uint16_t*>(p.out) + ((long long)(q0 + row_q) * Hq + h) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int d = dt * 32 + j * 8 + kg * 4;
+            uint2 o;
+            o.x = f32_to_bf16(oacc[dt][4 * j + 0] * sc) |
+                  (f32_to_bf16(oacc[dt][4 * j + 1] * sc) << 16);
+            o.y = f32_to_bf16(oacc[dt][4 * j + 2] * sc) |
+                  (f32_to_bf16(oacc[dt][4 * j + 3] * sc) << 16);
+            *reinterpret_cast<uint2*>(op + d) = o;
+          }
+      }
+    }
+    wait_vmem_all();
+    __syncthreads();  // LDS is reused by the next unit
+    RPA_TL_PP_LAP(5);
+  }
+  RPA_TL_PP_END();
+}
+
 long long resident_grid(const void* kernel) {
   int per_cu = 0, dev = 0, cus = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, NT, 0) != hipSuccess ||
@@ -969,16 +1451,60 @@ hipError_t launch_d(const AttnParams& p, long long blocks, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D, bool CAP>
+hipError_t launch_pair_d(const AttnParams& p, long long blocks, hipStream_t s) {
+  static const long long resident = [] {
+    int per_cu = 0, dev = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&prefill_pair_kernel<D, CAP>), 2 * NT, 0) !=
+            hipSuccess ||
+        hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        per_cu * cus < 8)
+      return kPrefillGrid / 2;
+    return (long long)(per_cu * cus) / 8 * 8;
+  }();
+  if (blocks > resident) blocks = resident;
+  if (trace_active()) {
+    char nm[80];
+    std::snprintf(nm, sizeof nm, "prefill_pair_kernel<bf16,D%d%s>(tiles%s)", D, CAP ? ",cap" : "",
+                  p.fuse_update ? "+update" : "");
+    if (trace_launch(nm, (unsigned)blocks, 2 * NT, 0, s)) return hipSuccess;
+  }
+  prefill_pair_kernel<D, CAP><<<dim3((unsigned)blocks), 2 * NT, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+// The two-group kernel serves bf16 queries over a bf16 cache with an even
+// GQA group, when the prefill kernel does not also merge the rows' splits
+// and a sequence's block table fits in its LDS page table.
+bool pair_eligible(const AttnParams& p, bool bf16_cache, bool qf8) {
+  return bf16_cache && !qf8 && !p.fuse_merge && p.Hkv > 0 && (p.Hq / p.Hkv) % 2 == 0 &&
+         p.Dpad == p.D && p.pps <= kPairPages;
+}
+
 template <typename CT, bool QF8>
-hipError_t launch_t(const AttnParams& p, hipStream_t s) {
+hipError_t launch_t(const AttnParams& p0, hipStream_t s) {
+  AttnParams p = p0;
   const long long merge_blocks =
       p.fuse_merge ? ((long long)p.lay.max_merge_rows * p.Hkv + 3) / 4 : 0;
   const long long blocks = std::max((long long)p.lay.max_pf_items * p.Hq, merge_blocks);
   if (blocks <= 0) return hipSuccess;
   const bool cap = p.cap > 0.f;
+  // prefill_kernel first: when the planner runs it beside the rows (co_run)
+  // it must not queue behind the two-group kernel, which needs whole CUs and
+  // then exits at once
+  p.pf_pair = pair_eligible(p, sizeof(CT) == 2, QF8) ? 1 : 0;
+  hipError_t e;
   if (p.D == 64)
-    return cap ? launch_d<CT, 64, true, QF8>(p, blocks, s) : launch_d<CT, 64, false, QF8>(p, blocks, s);
-  return cap ? launch_d<CT, 128, true, QF8>(p, blocks, s) : launch_d<CT, 128, false, QF8>(p, blocks, s);
+    e = cap ? launch_d<CT, 64, true, QF8>(p, blocks, s) : launch_d<CT, 64, false, QF8>(p, blocks, s);
+  else
+    e = cap ? launch_d<CT, 128, true, QF8>(p, blocks, s) : launch_d<CT, 128, false, QF8>(p, blocks, s);
+  if (e != hipSuccess || !p.pf_pair) return e;
+  const long long pblocks = (long long)p.lay.max_pf_items * (p.Hq / 2);
+  if (p.D == 64)
+    return cap ? launch_pair_d<64, true>(p, pblocks, s) : launch_pair_d<64, false>(p, pblocks, s);
+  return cap ? launch_pair_d<128, true>(p, pblocks, s) : launch_pair_d<128, false>(p, pblocks, s);
 }
 
 }  // namespace
@@ -1009,8 +1535,16 @@ extern "C" int rpa_pf_timeline_read(unsigned long long* host, int n) {
   return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(rpa::g_pf_timeline),
                                   (size_t)n * sizeof(unsigned long long), 0, hipMemcpyDeviceToHost);
 }
+extern "C" int rpa_pp_timeline_read(unsigned long long* host, int n) {
+  if (n > rpa::kPfTimelineWaves * rpa::kPfWords) n = rpa::kPfTimelineWaves * rpa::kPfWords;
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(rpa::g_pp_timeline),
+                                  (size_t)n * sizeof(unsigned long long), 0, hipMemcpyDeviceToHost);
+}
 extern "C" int rpa_pf_timeline_clear(void) {
   static unsigned long long zero[rpa::kPfTimelineWaves * rpa::kPfWords];
+  const hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(rpa::g_pp_timeline), zero, sizeof(zero), 0,
+                                         hipMemcpyHostToDevice);
+  if (e != hipSuccess) return (int)e;
   return (int)hipMemcpyToSymbol(HIP_SYMBOL(rpa::g_pf_timeline), zero, sizeof(zero), 0,
                                 hipMemcpyHostToDevice);
 }

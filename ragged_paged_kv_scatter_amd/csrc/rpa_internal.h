@@ -190,6 +190,10 @@ struct AttnParams {
   uint32_t in_row_bytes;
   const void* new_k;
   const void* new_v;
+  // Set by launch_prefill when the two-group prefill kernel is launched too:
+  // it takes the batch unless the planner runs the prefill beside the rows
+  // (co_run), and prefill_kernel takes it only then.
+  int32_t pf_pair;
 };
 
 // Launchers (return hipSuccess or the launch error).

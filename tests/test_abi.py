@@ -277,7 +277,7 @@ def test_trace_format_lines(lib, kind):
     """rpa_trace_format runs rpa_forward's host path dry: the forward,
     workspace and stream lines, then one launch line per kernel in launch
     order (decode-only: plan, rows, prefill kernel merging the splits; with
-    prefill tiles: plan, rows, prefill on the side stream, merge; f32: plan,
+    prefill tiles: plan, rows, the prefill kernels on the side stream, merge; f32: plan,
     rows, merge), and the workspace size rpa_workspace_bytes reports."""
     import ragged_paged_kv_scatter_amd as rpa
     if kind == "f32":
@@ -292,7 +292,11 @@ def test_trace_format_lines(lib, kind):
             order = ["prep_kernel", "row_kernel", "prefill_kernel"]
         else:
             d.total_tokens, d.max_num_seqs = 2176, 132
-            order = ["prep_kernel", "row_kernel", "prefill_kernel", "merge_kernel"]
+            # bf16 over a bf16 cache, G = 4: the two-group prefill kernel is
+            # launched after prefill_kernel, and the planner's co_run flag
+            # decides on the device which of the two takes the tiles
+            order = ["prep_kernel", "row_kernel", "prefill_kernel", "prefill_pair_kernel",
+                     "merge_kernel"]
     o = good_opts()
     text = rpa.rpa_trace_format(d, o, with_update=True)
     lines = text.strip().split("\n")
@@ -317,7 +321,7 @@ def test_trace_format_lines(lib, kind):
     assert [l.split()[2].split("<")[0] for l in launches] == order
     for l in launches:
         f = _kv(l)
-        assert int(f["grid"]) >= 1 and int(f["block"]) in (256, 1024)
+        assert int(f["grid"]) >= 1 and int(f["block"]) in (256, 512, 1024)
     # without the update the planner's launch carries no scatter
     text2 = rpa.rpa_trace_format(d, o, with_update=False)
     assert "plan+scatter" not in text2 and "update=0" in text2 and "[rpa] update none" in text2
@@ -349,3 +353,32 @@ def test_noalloc_checks_before_touching_the_device(lib):
     st, need = ws_status(lib, big, o)
     assert st == 0 and need > _lib.NOALLOC_SCRATCH_BYTES
     assert lib.rpa_forward_noalloc(ctypes.byref(big), ctypes.byref(o), *args) == 5
+
+
+@pytest.mark.parametrize("case", ["bf16_even_group", "bf16_odd_group", "fp8_cache", "padded",
+                                  "long_table"])
+def test_two_group_prefill_kernel_selection(lib, case):
+    """Batches with prefill tiles launch the two-group prefill kernel beside
+    prefill_kernel only for bf16 queries over a bf16 cache with an even GQA
+    group, no lane padding and a block table of at most 8192 pages."""
+    import ragged_paged_kv_scatter_amd as rpa
+    kw = dict(q_dtype=_lib.RPA_BF16, kv_in_dtype=_lib.RPA_BF16, cache_dtype=_lib.RPA_BF16,
+              num_q_heads=8, num_kv_heads=2, head_dim=128, head_dim_padded=128,
+              pages_per_seq=64, num_pages=512, page_size=16, total_tokens=600, max_num_seqs=4)
+    expect = True
+    if case == "bf16_odd_group":
+        kw.update(num_q_heads=2)
+        expect = False
+    elif case == "fp8_cache":
+        kw.update(cache_dtype=_lib.RPA_FP8_E4M3)
+        expect = False
+    elif case == "padded":
+        kw.update(head_dim_padded=144)
+        expect = False
+    elif case == "long_table":
+        kw.update(pages_per_seq=8193, num_pages=40000)
+        expect = False
+    text = rpa.rpa_trace_format(good_desc(**kw), good_opts(), with_update=True)
+    names = [l.split()[2].split("<")[0] for l in text.strip().split("\n") if l.split()[1] == "launch"]
+    assert "prefill_kernel" in names
+    assert ("prefill_pair_kernel" in names) == expect, names

@@ -142,3 +142,27 @@ def test_pf_timeline_summary_by_hand():
     assert s["copy_wait_share"] == 0.1 and s["barrier_wait_share"] == 0.25
     assert s["clk_per_step"] == 125.0
     assert s["copy_wait_clk_per_step"] == 12.5 and s["barrier_wait_clk_per_step"] == 32.5
+
+
+def test_counter_summary_sums_a_launchs_dispatches(tmp_path, monkeypatch):
+    # two steps: each a prefill_kernel dispatch (exits at once, 1 KiB) and a
+    # prefill_pair_kernel dispatch (99 KiB), plus a calibration copy of 2 KiB
+    # read for 1 MiB copied; split over two instances per counter
+    rows = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
+    disp = [(1, "copy_kernel", 2.0), (2, "rpa::prefill_kernel<...>", 1.0),
+            (3, "rpa::prefill_pair_kernel<...>", 99.0), (4, "rpa::prefill_kernel<...>", 1.0),
+            (5, "rpa::prefill_pair_kernel<...>", 99.0), (6, "rpa::row_kernel<...>", 7.0)]
+    for name in ("FETCH_SIZE", "WRITE_SIZE"):
+        with open(tmp_path / f"{name}.csv", "w") as fh:
+            fh.write("\n".join(rows + [f"{i},{k},{name},{v / 2}\n{i},{k},{name},{v / 2}"
+                                       for i, k, v in disp]) + "\n")
+    monkeypatch.setattr(bench, "traffic_file", lambda w, k: str(tmp_path / "out.json"))
+    bench.summarize_counters("prefill_bf16", "prefill", str(tmp_path / "FETCH_SIZE.csv"),
+                             str(tmp_path / "WRITE_SIZE.csv"), 1 << 20)
+    import json
+    with open(tmp_path / "out.json") as fh:
+        out = json.load(fh)
+    # per launch: (1 + 99) KiB scaled by 1 MiB / 2 KiB
+    assert out["fetch"]["launches"] == 2 and out["fetch"]["dispatches"] == 4
+    assert out["fetch"]["bytes"] == 100 * 1024 * 512
+    assert out["traffic_bytes"] == 2 * 100 * 1024 * 512
