@@ -718,29 +718,35 @@ def probe_ceilings(dev, full=False):
     for per_cu in ((2, 1) if full else ()):
         xb = cus * per_cu
         xflops = xb * 4 * 4 * iters * 32 * 32 * 16 * 2
-        for exp_ in (1, 0):
-            for nv in (0, 1, 2, 4):
-                if nv == 0 and exp_ == 0:
-                    continue
-                ms = time_it(lambda: _probes.check(lib.rpa_probe_mix(
-                    ctypes.c_void_p(msink.data_ptr()), ctypes.c_void_p(clocks.data_ptr()), nv,
-                    exp_, iters, xb, stream), "mix probe"))
-                tag = f"mfma_w{4 * per_cu}_with_{nv}_{'fma_exp' if exp_ else 'fma_fma'}"
-                out[f"{tag}_tflops"] = xflops / (ms * 1e-3) / 1e12
-                c = clocks.view(-1, 2)[: xb * 4].double()
-                ok = c[:, 1] > 0
-                out[f"{tag}_clock_ghz"] = float((c[ok, 0] / c[ok, 1]).mean() * 0.1)
+        # accumulators in AGPRs (rpa_probe_mix) and in VGPRs, the attention
+        # kernels' form (rpa_probe_mix_vgpr_acc)
+        cases = [(fn, acc, exp_, nv)
+                 for fn, acc in ((lib.rpa_probe_mix, ""), (lib.rpa_probe_mix_vgpr_acc, "_vgpr_acc"))
+                 for exp_ in (1, 0) for nv in (0, 1, 2, 4) if nv or exp_]
+        for fn, acc, exp_, nv in cases:
+            ms = time_it(lambda: _probes.check(fn(
+                ctypes.c_void_p(msink.data_ptr()), ctypes.c_void_p(clocks.data_ptr()), nv, exp_,
+                iters, xb, stream), "mix probe"))
+            tag = f"mfma_w{4 * per_cu}_with_{nv}_{'fma_exp' if exp_ else 'fma_fma'}{acc}"
+            out[f"{tag}_tflops"] = xflops / (ms * 1e-3) / 1e12
+            c = clocks.view(-1, 2)[: xb * 4].double()
+            ok = c[:, 1] > 0
+            out[f"{tag}_clock_ghz"] = float((c[ok, 0] / c[ok, 1]).mean() * 0.1)
     # MFMA fed from LDS in the prefill kernel's patterns, 2 workgroups per CU
-    for name, mode in (_probes.LDS_MFMA_MODES.items() if full else ()):
-        liters = iters // 4
-        ms = time_it(lambda: _probes.check(lib.rpa_probe_lds_mfma(
-            ctypes.c_void_p(msink.data_ptr()), ctypes.c_void_p(clocks.data_ptr()), mode, liters,
-            mblocks, stream), "lds mfma probe"))
-        lflops = mblocks * 4 * 16 * liters * 32 * 32 * 16 * 2
-        out[f"mfma_{name}_tflops"] = lflops / (ms * 1e-3) / 1e12
-        c = clocks.view(-1, 2)[: mblocks * 4].double()
-        ok = c[:, 1] > 0
-        out[f"mfma_{name}_clock_ghz"] = float((c[ok, 0] / c[ok, 1]).mean() * 0.1)
+    # (2 waves per SIMD) and 1 (a wave alone on its SIMD)
+    for per_cu in ((2, 1) if full else ()):
+        lb = cus * per_cu
+        for name, mode in _probes.LDS_MFMA_MODES.items():
+            liters = iters // 4
+            ms = time_it(lambda: _probes.check(lib.rpa_probe_lds_mfma(
+                ctypes.c_void_p(msink.data_ptr()), ctypes.c_void_p(clocks.data_ptr()), mode,
+                liters, lb, stream), "lds mfma probe"))
+            lflops = lb * 4 * 16 * liters * 32 * 32 * 16 * 2
+            tag = f"mfma_{name}" + ("" if per_cu == 2 else "_w4")
+            out[f"{tag}_tflops"] = lflops / (ms * 1e-3) / 1e12
+            c = clocks.view(-1, 2)[: lb * 4].double()
+            ok = c[:, 1] > 0
+            out[f"{tag}_clock_ghz"] = float((c[ok, 0] / c[ok, 1]).mean() * 0.1)
     # VALU: 8 workgroups (32 waves) per CU, 8 chains per lane
     vblocks, viters = cus * 8, 4096
     vsink = torch.empty(vblocks * 256 * 8, dtype=torch.float32, device=dev)

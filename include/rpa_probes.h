@@ -78,6 +78,13 @@ int rpa_probe_dma(const void* src, size_t window_bytes, uint32_t* sink, int64_t*
 int rpa_probe_mix(float* sink, int64_t* clocks, int nv, int exp, int iters, int blocks,
                   void* stream);
 
+/* rpa_probe_mix built with the MFMA accumulators in VGPRs (the form the
+ * attention kernels' MFMAs take, since their VALU code reads the
+ * accumulators) rather than AGPRs, where the compiler puts them in
+ * rpa_probe_mix.  Same arguments and work. */
+int rpa_probe_mix_vgpr_acc(float* sink, int64_t* clocks, int nv, int exp, int iters, int blocks,
+                           void* stream);
+
 /* MFMA fed from LDS, in the prefill kernel's operand patterns: every wave of
  * `blocks` workgroups of 256 threads (32 KiB of LDS each) runs `iters` rounds
  * of 16 v_mfma_f32_32x32x16_bf16.  mode 0: A operand from one ds_read_b128

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "librpa_probes.so")
 EXPORTS = ("rpa_probe_read", "rpa_probe_copy", "rpa_probe_mfma", "rpa_probe_valu",
            "rpa_probe_lds", "rpa_probe_dma", "rpa_probe_lds_dma", "rpa_probe_mix",
-           "rpa_probe_lds_mfma")
+           "rpa_probe_lds_mfma", "rpa_probe_mix_vgpr_acc")
 VALU_OPS = {"exp": 0, "rcp": 1, "fma": 2}
 # LDS op -> bytes per instruction and wave
 LDS_OPS = {"ds_read_b128": (0, 1024), "ds_read_b64_tr_b16": (1, 512), "ds_write_b128": (2, 1024)}
@@ -36,6 +36,7 @@ def load():
     lib.rpa_probe_dma.argtypes = [P, SZ, P, P, I, I, P]
     lib.rpa_probe_lds_dma.argtypes = [P, SZ, P, P, I, ctypes.c_int64, I, P]
     lib.rpa_probe_mix.argtypes = [P, P, I, I, I, I, P]
+    lib.rpa_probe_mix_vgpr_acc.argtypes = [P, P, I, I, I, I, P]
     lib.rpa_probe_lds_mfma.argtypes = [P, P, I, I, I, P]
     for n in EXPORTS:
         getattr(lib, n).restype = ctypes.c_int

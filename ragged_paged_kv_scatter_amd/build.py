@@ -18,7 +18,9 @@ SOURCES = ["rpa_api.cpp", "scatter.hip", "plan.hip", "decode.hip", "prefill.hip"
            "validate.hip"]
 # measurement probes (include/rpa_probes.h), a library of their own
 PROBES_LIB = os.path.join(HERE, "librpa_probes.so")
-PROBES_SOURCES = ["probes.hip"]
+PROBES_SOURCES = ["probes.hip", "probes_vacc.hip"]
+# per-source extra flags: the VGPR-accumulator copy of the MFMA-beside-VALU probe
+EXTRA_FLAGS = {"probes_vacc.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 # measurement build of librpa.so with the row kernels' per-wave clock stamps
 # (RPA_WAVE_TIMELINE; read by bench.py --op timeline), built on request only
 TIMELINE_LIB = os.path.join(HERE, "librpa_timeline.so")
@@ -45,8 +47,8 @@ def _compile(sources, obj_dir, jobs, verbose, defines=()):
     for src in sources:
         obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmd = [hipcc(), *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src),
-               "-o", obj]
+        cmd = [hipcc(), *FLAGS, *EXTRA_FLAGS.get(src, []), *[f"-D{d}" for d in defines], "-c",
+               os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
         procs.append((src, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE,
