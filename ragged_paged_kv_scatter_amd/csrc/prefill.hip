@@ -547,10 +547,17 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
         regs[i] = a;
       }
     };
-    // The cache slot of key position tok (its K row; + v_bytes for V).
-    auto slot_row = [&](int tok) -> char* {
-      const int page = bt[tok >> sh];
+    // The cache slot of key position tok (its K row; + v_bytes for V).  The
+    // page id comes from the LDS table when the caller has checked that the
+    // table holds it (a global read would make the writer wait for every
+    // copy it has in flight).
+    auto slot_row = [&](int tok, bool in_pt) -> char* {
+      const int page = in_pt ? s_pt[(tok >> sh) - pt_base] : bt[tok >> sh];
       return cache_w + (uint64_t)(((uint32_t)page << sh) | (uint32_t)(tok & pmask)) * row_bytes;
+    };
+    // whether the LDS table holds the pages of key positions [lo, hi) (uniform)
+    auto pt_holds = [&](int lo, int hi) {
+      return (lo >> sh) >= pt_base && ((hi - 1) >> sh) < pt_base + kPT;
     };
     // Fused update, staged rows: the writer stores the codes of its own new
     // tokens (rows of block blk) as they were fetched, and zeroes pad lanes.
@@ -558,12 +565,13 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
       if (!writer) return;
       const int lo = max(blk * BK, own_lo), hi = min(blk * BK + BK, own_hi);
       if (lo >= hi) return;
+      const bool in_pt = pt_holds(lo, hi);
 #pragma unroll
       for (int i = 0; i < (VDIRECT ? 0 : PER); ++i) {
         const int cidx = tid + NT * i;
         const int tok = blk * BK + cidx / GCPR, cc = cidx % GCPR;
         if (tok >= lo && tok < hi) {
-          char* dst = slot_row(tok) + vofs;
+          char* dst = slot_row(tok, in_pt) + vofs;
           *reinterpret_cast<uint4*>(dst + cc * 16) = regs[i];
           if (cc == 0)
             for (int pc = GCPR; pc < (int)(p.Dpad * ESZ / 16); ++pc)
@@ -583,6 +591,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
       if (lo >= hi) return;
       const int wch = p.Dpad * ESZ / 16;               // chunks of a cache head row
       const int n = (hi - lo) * wch;
+      const bool in_pt = pt_holds(lo, hi);
       for (int i = tid; i < n; i += NT) {
         const int rr = i / wch, c = i - rr * wch;
         const int tok = lo + rr, r = tok - blk * BK;
@@ -591,7 +600,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
           const int pc = K_ ? kchunk(r, c) : swz_chunk<D>(r, c);
           v = *reinterpret_cast<const uint4*>(buf + r * RB_ + (pc << 4));
         }
-        *reinterpret_cast<uint4*>(slot_row(tok) + (K_ ? 0u : v_bytes) + c * 16) = v;
+        *reinterpret_cast<uint4*>(slot_row(tok, in_pt) + (K_ ? 0u : v_bytes) + c * 16) = v;
       }
     };
     auto stage_staged = [&](const uint4* regs, char* buf) {  // e4m3 -> bf16 into swizzled rows
@@ -1171,7 +1180,7 @@ __global__ __launch_bounds__(2 * NT, 1) void prefill_pair_kernel(AttnParams p) {
         const int tok = lo + r2, r = tok - blk * BK;
         uint4 v = make_uint4(0, 0, 0, 0);
         if (c < CPR) v = *reinterpret_cast<const uint4*>(buf + r * RB + (swz_chunk<D>(r, c) << 4));
-        const int page = bt[tok >> sh];
+        const int page = s_pt[(tok >> sh) - pt_base];  // own rows lie in the unit's range
         char* row = cache_w + (uint64_t)(((uint32_t)page << sh) | (uint32_t)(tok & pmask)) * row_bytes;
         *reinterpret_cast<uint4*>(row + vofs + c * 16) = v;
       }
