@@ -864,9 +864,10 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(AttnParams p) {
       RPA_TL_PF_AT(3);
       // Beside the row kernel the wave keeps its raised priority through the
       // barrier and copy part as well: the row waves on its SIMD are older,
-      // so at equal priority their loads win every VMEM issue slot and the
-      // copies of a step waited about 4500 clocks to issue (mixed bf16 batch
-      // 0.48 -> 0.46 ms per step).
+      // so at equal priority their loads win the VMEM issue slots, and the
+      // part of a step from its barrier to its first q.k MFMA, where the
+      // copies are issued, took about 4500 of 10800 clocks (mixed bf16
+      // batch: 0.48 -> 0.46 ms per step with the priority kept).
       if (!co_pf) __builtin_amdgcn_s_setprio(0);
       l_run += ls0 + ls1;
       const float mr = red(m0, m1);
