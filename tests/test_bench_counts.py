@@ -166,3 +166,19 @@ def test_counter_summary_sums_a_launchs_dispatches(tmp_path, monkeypatch):
     assert out["fetch"]["launches"] == 2 and out["fetch"]["dispatches"] == 4
     assert out["fetch"]["bytes"] == 100 * 1024 * 512
     assert out["traffic_bytes"] == 2 * 100 * 1024 * 512
+
+
+def test_committed_traffic_summaries_match_the_kernel_sources():
+    """Every committed HBM-traffic summary (profiles/traffic_*.json) was taken
+    from the kernel sources as they stand: the bench only reports traffic whose
+    source hash matches, and a stale summary would silently drop it."""
+    import glob
+    import json
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "traffic_*.json")))
+    assert paths
+    for path in paths:
+        with open(path) as fh:
+            t = json.load(fh)
+        assert t["kernel"] in bench.KERNEL_SOURCES, path
+        assert t["source_hash"] == bench.source_hash(t["kernel"]), path
+        assert t["traffic_bytes"] > 0 and t["fetch"]["launches"] > 0, path
